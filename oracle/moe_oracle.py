@@ -1,0 +1,393 @@
+"""Plain CPU oracle for one GPU's share of a Mixture-of-Experts layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call
+this module: only the tests, the package entry's smoke check and the CPU
+baseline leg of the benchmark use it.  It shares no code, table or constant
+with the HIP library and imports nothing from it.
+
+Every function is the plain definition of the step it computes, in float64
+unless a caller asks for float32 (used only to time a CPU baseline), written
+from these pages (cited by title and section):
+
+  [Moebius notes]  Zhongzhu Zhou, reading notes "Moebius：为 MoE 大模型推理服务
+                   实现无缝运行时并行策略切换" (zhongzhuzhou.org, 2026-06-28).
+  [MoE guide]      "MoE 推理优化全景指南" (charlestar.github.io, 2026-05-13).
+  [Moebius paper]  "Moebius: Serving Mixture-of-Expert Models with Seamless
+                   Runtime Parallelism Switch" (conceptio.app mirror).
+  [CS349D L8]      "Lecture 8 · 混合专家模型的推理" (CS349D notes, semidirectx.com).
+
+Readings taken where the pages are silent (each one is listed, with its reason,
+in the design notes of the repository):
+  * top-k order: key descending, equal keys -> lower expert id first;
+  * rows inside an expert segment: ascending token index (stable);
+  * stacked gate/up axis: rows [0, I) are the gate projection, [I, 2I) the up
+    projection; SwiGLU is SiLU(gate) * up with SiLU(z) = z / (1 + exp(-z));
+  * the tensor-parallel share slices the intermediate index of *both* halves
+    of the stacked axis by the same range, and the down projection's input
+    dimension by that range;
+  * the selection-only bias of the sigmoid gating is added to the logit;
+  * a shared expert is added with weight 1 after the routed sum.
+
+Parity status: every function below is pinned by the `-m "not gpu"` tests in
+tests/test_oracle_pins.py (worked examples printed on the pages, closed forms,
+invariants, brute force and library routines on tiny inputs).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GATE_TOPK_SOFTMAX = 0          # softmax over the k selected logits
+GATE_SOFTMAX_TOPK = 1          # softmax over all E, keep k, no renormalisation
+GATE_SOFTMAX_TOPK_RENORM = 2   # softmax over all E, keep k, divide by their sum
+GATE_SIGMOID_BIAS_RENORM = 3   # select on logit + bias, weights sigmoid / sum
+
+GATING_MODES = (GATE_TOPK_SOFTMAX, GATE_SOFTMAX_TOPK, GATE_SOFTMAX_TOPK_RENORM,
+                GATE_SIGMOID_BIAS_RENORM)
+
+
+def _as(a, dtype):
+    return np.asarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------------------
+# Router and gating
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_r, logit_bias=None, dtype=np.float64):
+    """Router scores s = W_r x for every token, plus an optional per-expert
+    additive bias.
+
+    [MoE guide] section "从 Dense FFN 到专家集合": the router produces expert
+    scores s = W_r x.  [CS349D L8] section 1.2: the gate is (x W_g), with the
+    noise term turned off at inference.
+
+    x: [T, H], w_r: [E, H]  ->  [T, E]
+    """
+    s = _as(x, dtype) @ _as(w_r, dtype).T
+    if logit_bias is not None:
+        s = s + _as(logit_bias, dtype)[None, :]
+    return s
+
+
+def select_topk(key, k):
+    """Indices of the k largest keys per row, ordered by key descending and,
+    among equal keys, by expert id ascending.
+
+    [CS349D L8] section 1.2: KeepTopK keeps the k largest gate values.  The
+    order among equal keys is not given by the pages; lower id first is used.
+
+    key: [T, E] (compared in its own precision)  ->  int64 [T, k]
+    """
+    key = np.asarray(key)
+    T, E = key.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    out = np.empty((T, k), dtype=np.int64)
+    ids = np.arange(E)
+    for t in range(T):
+        # lexsort sorts by the last key first: key descending, then id ascending
+        order = np.lexsort((ids, -key[t]))
+        out[t] = order[:k]
+    return out
+
+
+def _softmax(v):
+    m = np.max(v, axis=-1, keepdims=True)
+    e = np.exp(v - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _sigmoid(v):
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def gate_weights(logits, ids, mode):
+    """Gate weights of the selected experts, in float64.
+
+    [CS349D L8] section 1.2 lists the variants:
+      mode 0  top-k then softmax (Shazeer, Mixtral): G = Softmax(KeepTopK(H, k)),
+              the entries outside the top k are -inf, so the k weights sum to 1;
+      mode 1  softmax then top-k without renormalising (DeepSeek-V2): the k
+              weights are softmax probabilities over all E and sum to < 1;
+      mode 2  mode 1 followed by division by the sum of the k kept weights;
+      mode 3  sigmoid affinity, weights renormalised over the k selected; the
+              selection bias never enters the weights (DeepSeek-V3).
+
+    logits: [T, E], ids: [T, k]  ->  float64 [T, k]
+    """
+    s = _as(logits, np.float64)
+    sel = np.take_along_axis(s, ids, axis=1)
+    if mode == GATE_TOPK_SOFTMAX:
+        return _softmax(sel)
+    if mode in (GATE_SOFTMAX_TOPK, GATE_SOFTMAX_TOPK_RENORM):
+        p = np.take_along_axis(_softmax(s), ids, axis=1)
+        if mode == GATE_SOFTMAX_TOPK_RENORM:
+            p = p / np.sum(p, axis=1, keepdims=True)
+        return p
+    if mode == GATE_SIGMOID_BIAS_RENORM:
+        a = _sigmoid(sel)
+        return a / np.sum(a, axis=1, keepdims=True)
+    raise ValueError(f"unknown gating mode {mode}")
+
+
+def selection_key(logits, mode, sel_bias=None):
+    """The value the top-k selection compares.
+
+    Modes 0-2 compare the logits themselves: softmax keeps order, so selecting
+    before or after it picks the same experts ([CS349D L8] section 1.2).
+    Mode 3 compares logit + bias, the bias changing only which experts are
+    picked ([CS349D L8] section 1.2; [MoE guide] section "负载不均会拖慢整个集体
+    通信" on DeepSeek-V3's auxiliary-loss-free balancing).  The sum is taken in
+    the precision of the logits, so float32 logits give a float32 key.
+    """
+    s = np.asarray(logits)
+    if mode == GATE_SIGMOID_BIAS_RENORM and sel_bias is not None:
+        return s + np.asarray(sel_bias, dtype=s.dtype)[None, :]
+    return s
+
+
+def route(logits, k, mode, sel_bias=None):
+    """Top-k expert ids and their gate weights for each token.
+
+    logits: [T, E]  ->  (int64 ids [T, k], float64 weights [T, k])
+    """
+    key = selection_key(logits, mode, sel_bias)
+    ids = select_topk(key, k)
+    return ids, gate_weights(logits, ids, mode)
+
+
+# ---------------------------------------------------------------------------
+# Dispatch metadata: histogram, prefix sum, permutation
+# ---------------------------------------------------------------------------
+
+def expert_histogram(ids, e_begin, e_end):
+    """counts[e - e_begin] = number of (token, slot) pairs routed to expert e,
+    for the local experts e in [e_begin, e_end).
+
+    [MoE guide] section "Dispatch 并不是一次普通 all-to-all": histogram step.
+    """
+    counts = np.zeros(e_end - e_begin, dtype=np.int64)
+    for e in np.asarray(ids).reshape(-1):
+        if e_begin <= e < e_end:
+            counts[e - e_begin] += 1
+    return counts
+
+
+def exclusive_offsets(counts):
+    """offsets[0] = 0, offsets[i + 1] = offsets[i] + counts[i].
+
+    [MoE guide] section "Dispatch 并不是一次普通 all-to-all": the prefix sum gives
+    each expert's output offset.
+    """
+    off = np.zeros(len(counts) + 1, dtype=np.int64)
+    for i, c in enumerate(counts):
+        off[i + 1] = off[i] + c
+    return off
+
+
+def permute(ids, e_begin, e_end):
+    """Stable grouping of token copies by local expert.
+
+    [MoE guide] section "Dispatch 并不是一次普通 all-to-all": histogram, prefix
+    sum, then permute so that each expert's copies are contiguous; its example
+    keeps the original token order inside a segment ([t0, t2]).
+
+    Returns counts [E_loc], offsets [E_loc + 1], src_token [rows] (the token
+    each permuted row copies) and dst_row [T, k] (the row a (token, slot) pair
+    went to, -1 when its expert is not local).
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    counts = expert_histogram(ids, e_begin, e_end)
+    offsets = exclusive_offsets(counts)
+    cursor = offsets[:-1].copy()
+    src_token = np.empty(int(offsets[-1]), dtype=np.int64)
+    dst_row = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if e_begin <= e < e_end:
+                row = cursor[e - e_begin]
+                cursor[e - e_begin] += 1
+                dst_row[t, j] = row
+                src_token[row] = t
+    return counts, offsets, src_token, dst_row
+
+
+# ---------------------------------------------------------------------------
+# Experts
+# ---------------------------------------------------------------------------
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = np.asarray(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(x_rows, w13_e, w2_e, dtype=np.float64):
+    """One SwiGLU expert applied to a block of rows.
+
+    [Moebius notes] eq. (2) and [Moebius paper] section 3.1: an expert holds a
+    gate/up projection of shape (2I, H), the gate and up projections stacked
+    on the leading axis, and a down projection of shape (H, I).
+
+    x_rows: [m, H], w13_e: [2I, H], w2_e: [H, I]  ->  [m, H]
+    """
+    w13_e = _as(w13_e, dtype)
+    w2_e = _as(w2_e, dtype)
+    i_dim = w13_e.shape[0] // 2
+    u = _as(x_rows, dtype) @ w13_e.T
+    h = silu(u[:, :i_dim]) * u[:, i_dim:]
+    return h @ w2_e.T
+
+
+def grouped_ffn(x, src_token, offsets, w13, w2, dtype=np.float64):
+    """Expert outputs for every permuted row: expert i multiplies its own
+    contiguous block of m_i rows.
+
+    [MoE guide] section "Expert GEMM 为什么经常不够大": expert i computes
+    [m_i, hidden] @ W_i for its rows.
+
+    x: [T, H]; src_token: [rows]; offsets: [E_loc + 1];
+    w13: indexable by local expert -> [2I, H]; w2: -> [H, I]
+    ->  y_perm [rows, H]
+    """
+    x = np.asarray(x)
+    H = x.shape[1]
+    rows = int(offsets[-1])
+    y_perm = np.zeros((rows, H), dtype=dtype)
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            y_perm[r0:r1] = swiglu_expert(x[np.asarray(src_token[r0:r1])], w13[e], w2[e], dtype)
+    return y_perm
+
+
+def combine(y_perm, dst_row, w, y_shared=None, dtype=np.float64):
+    """Inverse permutation with the gate-weighted sum:
+    y[t] = sum_j w[t, j] * y_perm[dst_row[t, j]] over the local slots, summed
+    in slot order, plus the shared expert's output with weight 1.
+
+    [MoE guide] section "Dispatch 并不是一次普通 all-to-all": combine restores
+    the original token order and applies the routing weights.  [Moebius notes]
+    eq. (1).  [CS349D L8] section 1.2: a shared expert every token passes
+    through.
+    """
+    dst_row = np.asarray(dst_row)
+    w = _as(w, dtype)
+    T, k = dst_row.shape
+    H = y_perm.shape[1]
+    y = np.zeros((T, H), dtype=dtype)
+    for t in range(T):
+        for j in range(k):
+            r = dst_row[t, j]
+            if r >= 0:
+                y[t] += w[t, j] * y_perm[r]
+    if y_shared is not None:
+        y = y + _as(y_shared, dtype)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# The layer
+# ---------------------------------------------------------------------------
+
+def moe_layer(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
+              e_begin=0, e_end=None, w13_shared=None, w2_shared=None,
+              logits=None, dtype=np.float64):
+    """One GPU's share of the MoE layer forward through the permuted data path.
+
+    [MoE guide] section "一个 token 为什么要跨 GPU": router -> top-k ids and
+    weights -> count / prefix sum / permute -> experts grouped -> inverse
+    permutation + weighted sum.  [Moebius notes] eq. (1) is the result.
+
+    The share: local experts are [e_begin, e_end) (expert-parallel view,
+    [Moebius notes] eq. (4)); w13[i], w2[i] are those of expert e_begin + i.
+    For the tensor-parallel view pass the rank's slices ([Moebius notes]
+    eq. (3); see tp_shard) with the full expert range.
+
+    `logits` may be given (e.g. float32 logits from another implementation) to
+    route on exactly those values; otherwise they are computed here.
+
+    Returns (y [T, H], aux dict with logits, ids, w, counts, offsets,
+    src_token, dst_row).
+    """
+    x = np.asarray(x)
+    E = np.asarray(w_r).shape[0] if logits is None else np.asarray(logits).shape[1]
+    if e_end is None:
+        e_end = E
+    if logits is None:
+        logits = router_logits(x, w_r, logit_bias, dtype)
+    ids, w = route(logits, k, mode, sel_bias)
+    counts, offsets, src_token, dst_row = permute(ids, e_begin, e_end)
+    y_perm = grouped_ffn(x, src_token, offsets, w13, w2, dtype)
+    y_shared = None
+    if w13_shared is not None:
+        y_shared = swiglu_expert(x, w13_shared, w2_shared, dtype)
+    y = combine(y_perm, dst_row, w, y_shared, dtype)
+    aux = dict(logits=logits, ids=ids, w=w, counts=counts, offsets=offsets,
+               src_token=src_token, dst_row=dst_row)
+    return y, aux
+
+
+def moe_layer_dense(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
+                    w13_shared=None, w2_shared=None, dtype=np.float64):
+    """Brute-force evaluation of the layer with a dense gate vector.
+
+    [CS349D L8] section 1.2: y = sum_{i=1..E} G(x)_i E_i(x), G sparse with k
+    non-zeros.  Every expert is evaluated on every token and multiplied by its
+    dense gate entry (zero off the top k); no permutation is involved.  Only
+    for tiny inputs.
+    """
+    x = np.asarray(x)
+    logits = router_logits(x, w_r, logit_bias, dtype)
+    T, E = logits.shape
+    ids, w = route(logits, k, mode, sel_bias)
+    G = np.zeros((T, E), dtype=np.float64)
+    for t in range(T):
+        G[t, ids[t]] = w[t]
+    y = np.zeros((T, x.shape[1]), dtype=dtype)
+    for e in range(E):
+        y += G[:, e:e + 1] * swiglu_expert(x, w13[e], w2[e], dtype)
+    if w13_shared is not None:
+        y += swiglu_expert(x, w13_shared, w2_shared, dtype)
+    return y
+
+
+def tp_shard(w13, w2, rank, P):
+    """The tensor-parallel share of rank `rank` out of P.
+
+    [Moebius notes] eq. (3) and [Moebius paper] section 3.1: every rank holds
+    all E experts with W13 of shape (E, 2I/P, H) and W2 of shape (E, H, I/P).
+    Reading: the slice takes intermediate indices [rank*I/P, (rank+1)*I/P) of
+    the gate half and the same indices of the up half, so SwiGLU stays local;
+    W2 keeps the same input columns.
+
+    w13: [E, 2I, H], w2: [E, H, I]  ->  ([E, 2I/P, H], [E, H, I/P])
+    """
+    w13 = np.asarray(w13)
+    w2 = np.asarray(w2)
+    i_dim = w13.shape[1] // 2
+    if i_dim % P:
+        raise ValueError("I must be divisible by P")
+    s = i_dim // P
+    lo, hi = rank * s, (rank + 1) * s
+    w13_r = np.concatenate([w13[:, lo:hi, :], w13[:, i_dim + lo:i_dim + hi, :]], axis=1)
+    w2_r = w2[:, :, lo:hi]
+    return w13_r, w2_r
+
+
+def touched_experts_expected(E, k, n):
+    """Expected number of distinct experts a batch of n tokens touches under
+    uniform routing: E * (1 - (1 - k/E)^n).  [CS349D L8] section 2.1."""
+    return E * (1.0 - (1.0 - k / E) ** n)
+
+
+def imbalance_ratio(counts, n_assign=None, E=None):
+    """max_i n_i / (N_a / E).  [MoE guide] section "负载不均会拖慢整个集体通信"."""
+    counts = np.asarray(counts)
+    if n_assign is None:
+        n_assign = counts.sum()
+    if E is None:
+        E = len(counts)
+    return float(counts.max()) / (n_assign / E)
