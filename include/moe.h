@@ -1,0 +1,230 @@
+/*
+ * moe.h -- C ABI of a single-GPU Mixture-of-Experts layer forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one GPU's share of an MoE layer: router scores, top-k
+ * gating, per-expert histogram, prefix sum and permutation of token copies,
+ * grouped SwiGLU expert GEMMs, and the inverse permutation with the
+ * gate-weighted combine.  Passages cited below:
+ *
+ *   [Moebius notes]  Zhongzhu Zhou, reading notes "Moebius：为 MoE 大模型推理服务
+ *                    实现无缝运行时并行策略切换" (zhongzhuzhou.org).
+ *   [MoE guide]      "MoE 推理优化全景指南" (charlestar.github.io).
+ *   [Moebius paper]  "Moebius: Serving Mixture-of-Expert Models with Seamless
+ *                    Runtime Parallelism Switch".
+ *   [CS349D L8]      "Lecture 8 · 混合专家模型的推理" (CS349D notes).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named x, w_*, y*, logits, topk_*, counts, offsets, src_token,
+ *   dst_row, ws are DEVICE pointers; the caller owns every buffer.  The
+ *   library never allocates or frees memory and keeps no state between calls.
+ * - Every device pointer must be 16-byte aligned.  Matrices are row-major with
+ *   the contraction (K) dimension contiguous:
+ *     x[T][H], w_router[E][H], w13[e][2*I_loc][H], w2[e][H][I_loc].
+ *   In w13, rows [0, I_loc) are the gate projection and rows [I_loc, 2*I_loc)
+ *   the up projection ([Moebius paper] section 3.1 stacks the two; the order
+ *   is this library's convention).  The expert MLP is
+ *     y = W2 * (SiLU(W_gate x) * (W_up x)),  SiLU(z) = z / (1 + exp(-z)).
+ * - `stream` is a hipStream_t (NULL = the null stream).  Calls are enqueued
+ *   on it asynchronously; no call copies between host and device or
+ *   synchronises, so every call may be captured in a HIP graph.
+ * - Arguments are checked on the host before anything is enqueued; a failed
+ *   check returns an error and enqueues nothing.  A kernel launch failure
+ *   returns MOE_ERR_HIP.  T = 0 is a successful no-op (moe_permute still
+ *   writes zero counts and offsets).
+ * - Shape limits: 1 <= k <= 32, k <= E <= 1024, H and I_loc multiples of 32.
+ *   Other shapes return MOE_ERR_UNSUPPORTED.
+ * - Results are bitwise repeatable: no kernel uses atomics to combine
+ *   floating-point values or to order rows.
+ * - Inference is dropless: every (token, slot) pair routed to a local expert
+ *   is computed ([CS349D L8] section 1.4).
+ * - Non-finite inputs are outside the contract.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null / misaligned pointer, negative or inconsistent size */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but outside the shape / dtype / mode limits above */
+  MOE_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than the size query */
+  MOE_ERR_HIP = 4,           /* a HIP launch returned an error */
+  MOE_ERR_METADATA = 5       /* reserved: device-side metadata check failed */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,               /* float32 */
+  MOE_BF16 = 1               /* bfloat16; products accumulate in float32 */
+} moe_dtype;
+
+/* Gating variants, [CS349D L8] section 1.2. */
+typedef enum {
+  MOE_GATE_TOPK_SOFTMAX = 0,         /* softmax over the k selected logits (weights sum to 1)     */
+  MOE_GATE_SOFTMAX_TOPK = 1,         /* softmax over all E, keep k, no renormalisation (sum < 1)   */
+  MOE_GATE_SOFTMAX_TOPK_RENORM = 2,  /* softmax over all E, keep k, divide by their sum            */
+  MOE_GATE_SIGMOID_BIAS_RENORM = 3   /* select on logit + sel_bias, weight sigmoid(logit) / sum    */
+} moe_gating;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_str(int status);
+
+/*
+ * moe_route -- router scores and top-k gating.
+ *   [MoE guide] section "从 Dense FFN 到专家集合" (scores s = W_r x, top-k,
+ *   weighted sum); [CS349D L8] section 1.2 (gating variants, noise off at
+ *   inference).
+ *
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h] + logit_bias[e]   (float32)
+ *   If x == NULL and w_router == NULL, `logits` is an INPUT [T][E] and only
+ *   the gating runs on it (dt, H, logit_bias are then ignored).
+ *   Selection key: logits (modes 0-2) or logits + sel_bias, added in float32
+ *   (mode 3).  topk_ids[t][0..k) are the k largest keys ordered by key
+ *   descending, equal keys broken towards the lower expert id.
+ *   topk_w[t][j] is the gate weight of topk_ids[t][j] per `mode`.
+ *
+ *   x[T][H], w_router[E][H]: dtype `dt`.  logit_bias[E], sel_bias[E]: float32
+ *   or NULL (sel_bias is used by mode 3 only).  Outputs: logits[T][E] float32,
+ *   topk_ids[T][k] int32, topk_w[T][k] float32.
+ */
+int moe_route(const void* x, const void* w_router, int dt, int T, int H, int E, int k,
+              int mode, const float* logit_bias, const float* sel_bias,
+              float* logits, int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * moe_permute -- histogram, prefix sum and stable permutation of token copies.
+ *   [MoE guide] section "Dispatch 并不是一次普通 all-to-all" (histogram ->
+ *   prefix sum -> permute, e.g. ids [3,1,3,0,6] -> [t3][t1][t0,t2][t4]).
+ *
+ *   Local experts are [e_begin, e_end), E_loc = e_end - e_begin.
+ *   counts[i]   = number of (t, j) with topk_ids[t][j] == e_begin + i.
+ *   offsets[0] = 0, offsets[i+1] = offsets[i] + counts[i]  (E_loc + 1 values).
+ *   The row of (t, j) is offsets[i] + #{t' < t : e_begin + i in topk_ids[t']}:
+ *   rows of one expert keep ascending token order.  dst_row[t][j] is that row,
+ *   or -1 when the expert is not local; src_token[row] = t.
+ *   If x != NULL, x_perm[row][:] = x[src_token[row]][:] (dtype dt, H columns).
+ *
+ *   topk_ids[T][k] int32 with values in [0, E) and distinct within a token
+ *   (as moe_route produces).  Outputs: counts[E_loc], offsets[E_loc+1],
+ *   src_token[T*k] (first offsets[E_loc] entries written), dst_row[T][k]: int32
+ *   (topk_ids, src_token and dst_row may be NULL when T = 0).
+ *   ws: at least moe_permute_workspace_size(T, k, E_loc) bytes (may be NULL
+ *   when T <= 64: a single tile needs no workspace).
+ */
+size_t moe_permute_workspace_size(int T, int k, int E_loc);
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
+                const void* x, int H, int dt,
+                int32_t* counts, int32_t* offsets, int32_t* src_token, int32_t* dst_row,
+                void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn -- grouped SwiGLU expert MLPs over ragged row counts.
+ *   [MoE guide] section "Expert GEMM 为什么经常不够大" (expert i computes
+ *   [m_i, hidden] @ W_i in one schedule); [Moebius notes] eq. (2)-(4) and
+ *   [Moebius paper] section 3.1 (W13 (E_loc, 2I, H), W2 (E_loc, H, I); the
+ *   tensor-parallel share holds I/P of every expert).
+ *
+ *   For local expert i and every row r in [offsets[i], offsets[i+1]):
+ *     a = x_perm[r]            if x_perm != NULL
+ *       = x[src_token[r]]      otherwise (gather fused into the GEMM)
+ *     g = w13[i][0:I_loc] a,  u = w13[i][I_loc:2I_loc] a,  h = SiLU(g) * u
+ *     y_perm[r] = w2[i] h
+ *   h is rounded to dtype `dt` between the two GEMMs.  offsets live on the
+ *   device: no row count is read back to the host.
+ *
+ *   max_rows bounds offsets[E_loc] (grid sizing; T*k for a full layer).
+ *   x_perm[max_rows][H] or x[*][H] + src_token[max_rows]; w13, w2: dtype dt;
+ *   y_perm[max_rows][H] of dtype y_dt.  ws: at least
+ *   moe_grouped_ffn_workspace_size(...) bytes.
+ */
+size_t moe_grouped_ffn_workspace_size(int max_rows, int E_loc, int H, int I_loc, int dt);
+int moe_grouped_ffn(const void* x_perm, const void* x, const int32_t* src_token,
+                    const int32_t* offsets, int E_loc, int max_rows, int H, int I_loc,
+                    const void* w13, const void* w2, int dt,
+                    void* y_perm, int y_dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- inverse permutation with the gate-weighted sum.
+ *   [MoE guide] section "Dispatch 并不是一次普通 all-to-all" (combine restores
+ *   token order and applies the routing weights); [Moebius notes] eq. (1);
+ *   [CS349D L8] section 1.2 (a shared expert every token passes through).
+ *
+ *   y[t] = sum_{j < k, dst_row[t][j] >= 0} topk_w[t][j] * y_perm[dst_row[t][j]]
+ *          (+ y_shared[t] with weight 1 if y_shared != NULL),
+ *   accumulated in float32 in slot order and rounded once to dtype dt.
+ *   In the tensor-parallel view y is the rank's partial sum.
+ *
+ *   y_perm[*][H] dtype y_perm_dt; dst_row[T][k] int32; topk_w[T][k] float32;
+ *   y_shared[T][H] and y[T][H] dtype dt.
+ */
+int moe_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row, const float* topk_w,
+                int T, int k, int H, const void* y_shared, void* y, int dt, void* stream);
+
+/*
+ * moe_layer -- the whole share of the layer in one call:
+ *   route -> permute -> grouped SwiGLU GEMMs (gather fused) -> shared expert
+ *   -> combine, all enqueued on `stream` without host synchronisation.
+ *   [MoE guide] section "一个 token 为什么要跨 GPU" (the data path);
+ *   [Moebius notes] eq. (1).
+ *
+ *   Expert-parallel view: [e_begin, e_end) is the local range and w13/w2 hold
+ *   those experts ([Moebius notes] eq. (4)).  Tensor-parallel view: the full
+ *   range with I_loc = I/P slices ([Moebius notes] eq. (3)); the output is the
+ *   rank's partial sum.  The router always sees all E experts.
+ *   I_shared > 0 adds one always-on shared expert (w13_shared[2*I_shared][H],
+ *   w2_shared[H][I_shared]) with weight 1.
+ */
+typedef struct {
+  int H, E, k, I_loc, e_begin, e_end, I_shared;
+  int mode;                      /* moe_gating */
+  int dt;                        /* moe_dtype of x, y and every weight */
+  const void* w_router;          /* [E][H] */
+  const void* w13;               /* [E_loc][2*I_loc][H] */
+  const void* w2;                /* [E_loc][H][I_loc] */
+  const void* w13_shared;        /* [2*I_shared][H] or NULL */
+  const void* w2_shared;         /* [H][I_shared] or NULL */
+  const float* logit_bias;       /* [E] or NULL: added to the logits (selection and weights) */
+  const float* sel_bias;         /* [E] or NULL: mode 3 selection only */
+} moe_layer_desc;
+
+/* Optional copies of the intermediate results (every field may be NULL);
+ * buffers as in moe_route / moe_permute.  stage_events[i], when not NULL, is
+ * a hipEvent_t that moe_layer records on `stream` at stage boundary i:
+ *   0 before routing, 1 after the routing metadata (route + permute),
+ *   2 after the gate/up GEMM, 3 after the down GEMM, 4 after the shared
+ *   expert, 5 after the combine.
+ * (Per-stage timing: the time split between router, dispatch metadata,
+ * expert GEMMs and combine.) */
+#define MOE_STAGE_EVENTS 6
+typedef struct {
+  float* logits;                 /* [T][E] */
+  int32_t* topk_ids;             /* [T][k] */
+  float* topk_w;                 /* [T][k] */
+  int32_t* counts;               /* [E_loc] */
+  int32_t* offsets;              /* [E_loc + 1] */
+  int32_t* src_token;            /* [T*k] */
+  int32_t* dst_row;              /* [T][k] */
+  void* stage_events[MOE_STAGE_EVENTS];
+} moe_debug_out;
+
+/* Workspace bytes for moe_layer with up to T_max tokens (0 on invalid desc). */
+size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max);
+int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y,
+              void* ws, size_t ws_bytes, moe_debug_out* dbg, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

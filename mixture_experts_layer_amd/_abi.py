@@ -1,0 +1,71 @@
+"""ctypes declarations of the C ABI in include/moe.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+MOE_OK = 0
+MOE_F32 = 0
+MOE_BF16 = 1
+GATE_TOPK_SOFTMAX = 0
+GATE_SOFTMAX_TOPK = 1
+GATE_SOFTMAX_TOPK_RENORM = 2
+GATE_SIGMOID_BIAS_RENORM = 3
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+c_int, c_size_t, c_void_p, c_char_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
+
+
+class MoELayerDesc(ctypes.Structure):
+    _fields_ = [("H", c_int), ("E", c_int), ("k", c_int), ("I_loc", c_int), ("e_begin", c_int),
+                ("e_end", c_int), ("I_shared", c_int), ("mode", c_int), ("dt", c_int),
+                ("w_router", c_void_p), ("w13", c_void_p), ("w2", c_void_p),
+                ("w13_shared", c_void_p), ("w2_shared", c_void_p),
+                ("logit_bias", c_void_p), ("sel_bias", c_void_p)]
+
+
+class MoEDebugOut(ctypes.Structure):
+    _fields_ = [("logits", c_void_p), ("topk_ids", c_void_p), ("topk_w", c_void_p),
+                ("counts", c_void_p), ("offsets", c_void_p), ("src_token", c_void_p),
+                ("dst_row", c_void_p), ("stage_events", c_void_p * 6)]
+
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "moe_abi_version": (c_int, []),
+    "moe_status_str": (c_char_p, [c_int]),
+    "moe_route": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
+                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_permute_workspace_size": (c_size_t, [c_int, c_int, c_int]),
+    "moe_permute": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_int,
+                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                            c_void_p]),
+    "moe_grouped_ffn_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "moe_grouped_ffn": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_size_t,
+                                c_void_p]),
+    "moe_combine": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
+                            c_void_p, c_int, c_void_p]),
+    "moe_layer_workspace_size": (c_size_t, [ctypes.POINTER(MoELayerDesc), c_int]),
+    "moe_layer": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p, c_void_p,
+                          c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+
+def lib_path():
+    return os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, "lib", "libmoe_mi355x.so"))
+
+
+def load_library():
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"HIP library not built: {path} is missing "
+                          "(run `python -m mixture_experts_layer_amd.build`)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib

@@ -1,0 +1,390 @@
+// C ABI entry points: argument checks, workspace layout and kernel sequencing.
+// Declarations and the full contract are in include/moe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int elt_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+inline bool valid_dt(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Bump allocator over the caller's workspace (or a size count when base == 0).
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+int check_route_shape(int T, int E, int k, int mode) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (mode < 0 || mode > 3) return MOE_ERR_INVALID_ARG;
+  if (E > 1024 || k > KMAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_hidden(int H) {
+  if (H <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 32) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Expected rows per expert, used to pick the GEMM row tile.
+int mean_rows(int T, int k, int E) { return cdiv(T * k, E); }
+
+int max_tiles_for(int max_rows, int E_loc, int BM) {
+  if (max_rows <= 0) return 1;
+  const long long bound = ((long long)max_rows + (long long)E_loc * (BM - 1)) / BM;
+  return (int)(bound < max_rows ? bound : max_rows);
+}
+
+struct LayerWs {
+  float* logits;
+  int32_t *ids, *counts, *offsets, *src_token, *dst_row;
+  float* w;
+  int32_t *tile_counts, *tile_base, *rank, *n_tiles;
+  int4* tile_map;
+  void *h, *y_perm, *h_s, *y_s;
+  int BM, max_tiles, max_rows, n_tt;
+};
+
+int check_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (!valid_dt(d->dt)) return MOE_ERR_INVALID_ARG;
+  int st = check_hidden(d->H);
+  if (st) return st;
+  if (d->E < 1 || d->k < 1 || d->k > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->mode < 0 || d->mode > 3) return MOE_ERR_INVALID_ARG;
+  if (d->E > 1024 || d->k > KMAX) return MOE_ERR_UNSUPPORTED;
+  if (d->I_loc <= 0 || d->e_begin < 0 || d->e_end > d->E || d->e_begin >= d->e_end)
+    return MOE_ERR_INVALID_ARG;
+  if (d->I_loc % 32) return MOE_ERR_UNSUPPORTED;
+  if (d->I_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (d->I_shared % 32) return MOE_ERR_UNSUPPORTED;
+  if (!d->w_router || !d->w13 || !d->w2) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(d->w_router) || !aligned16(d->w13) || !aligned16(d->w2))
+    return MOE_ERR_INVALID_ARG;
+  if (d->I_shared > 0) {
+    if (!d->w13_shared || !d->w2_shared) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(d->w13_shared) || !aligned16(d->w2_shared)) return MOE_ERR_INVALID_ARG;
+  }
+  if ((d->logit_bias && !aligned16(d->logit_bias)) || (d->sel_bias && !aligned16(d->sel_bias)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w) {
+  const int E_loc = d->e_end - d->e_begin;
+  const int eb = elt_bytes(d->dt);
+  const int max_rows = T * (d->k < E_loc ? d->k : E_loc);
+  const int n_tt = cdiv(T, TOK_TILE);
+  const int BM = ffn_row_tile(d->dt, mean_rows(T, d->k, d->E));
+  const int max_tiles = max_tiles_for(max_rows, E_loc, BM);
+  Carver c(base);
+  LayerWs l;
+  l.logits = c.take<float>((size_t)T * d->E * 4);
+  l.ids = c.take<int32_t>((size_t)T * d->k * 4);
+  l.w = c.take<float>((size_t)T * d->k * 4);
+  l.tile_counts = c.take<int32_t>((size_t)n_tt * E_loc * 4);
+  l.tile_base = c.take<int32_t>((size_t)n_tt * E_loc * 4);
+  l.rank = c.take<int32_t>((size_t)T * d->k * 4);
+  l.counts = c.take<int32_t>((size_t)E_loc * 4);
+  l.offsets = c.take<int32_t>((size_t)(E_loc + 1) * 4);
+  l.src_token = c.take<int32_t>((size_t)T * d->k * 4);
+  l.dst_row = c.take<int32_t>((size_t)T * d->k * 4);
+  l.tile_map = c.take<int4>((size_t)max_tiles * sizeof(int4));
+  l.n_tiles = c.take<int32_t>(4);
+  l.h = c.take<char>((size_t)max_rows * d->I_loc * eb);
+  l.y_perm = c.take<char>((size_t)max_rows * d->H * eb);
+  l.h_s = l.y_s = nullptr;
+  if (d->I_shared > 0) {
+    l.h_s = c.take<char>((size_t)T * d->I_shared * eb);
+    l.y_s = c.take<char>((size_t)T * d->H * eb);
+  }
+  l.BM = BM;
+  l.max_tiles = max_tiles;
+  l.max_rows = max_rows;
+  l.n_tt = n_tt;
+  if (w) *w = l;
+  return c.used;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                      \
+  do {                                     \
+    hipError_t _e = (expr);                \
+    if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, dtype or mode";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    case MOE_ERR_METADATA: return "routing metadata check failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const void* x, const void* w_router, int dt, int T, int H, int E, int k, int mode,
+              const float* logit_bias, const float* sel_bias, float* logits, int32_t* topk_ids,
+              float* topk_w, void* stream) {
+  int st = check_route_shape(T, E, k, mode);
+  if (st) return st;
+  const bool given_logits = (x == nullptr && w_router == nullptr);
+  if (!given_logits) {
+    if (!x || !w_router || !valid_dt(dt)) return MOE_ERR_INVALID_ARG;
+    if ((st = check_hidden(H))) return st;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    if (logit_bias && !aligned16(logit_bias)) return MOE_ERR_INVALID_ARG;
+  }
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_ERR_INVALID_ARG;
+  if (sel_bias && !aligned16(sel_bias)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!given_logits) MOE_TRY(launch_router_logits(x, w_router, dt, T, H, E, logit_bias, logits, s));
+  GateTileArgs a{};
+  a.logits = logits;
+  a.sel_bias = sel_bias;
+  a.ids_out = topk_ids;
+  a.w_out = topk_w;
+  a.T = T; a.E = E; a.k = k; a.mode = mode;
+  a.do_gate = 1; a.do_permute = 0;
+  a.e_begin = 0; a.e_end = E;
+  return hip_status(launch_gate_tiles(a, cdiv(T, TOK_TILE), s));
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E_loc) {
+  if (T < 0 || k < 1 || E_loc < 1) return 0;
+  const int n_tt = cdiv(T, TOK_TILE);
+  return align_up((size_t)n_tt * E_loc * 4) * 2 + align_up((size_t)T * k * 4);
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
+                const void* x, int H, int dt, int32_t* counts, int32_t* offsets,
+                int32_t* src_token, int32_t* dst_row, void* x_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = check_route_shape(T, E, k, 0);
+  if (st) return st;
+  if (e_begin < 0 || e_end > E || e_begin >= e_end) return MOE_ERR_INVALID_ARG;
+  const int E_loc = e_end - e_begin;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !src_token || !dst_row)) return MOE_ERR_INVALID_ARG;
+  {
+    const void* ptrs[] = {topk_ids, counts, offsets, src_token, dst_row};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  }
+  if (x) {
+    if (!valid_dt(dt) || !x_perm) return MOE_ERR_INVALID_ARG;
+    if ((st = check_hidden(H))) return st;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  }
+  const size_t need = moe_permute_workspace_size(T, k, E_loc);
+  const bool single = T <= TOK_TILE;
+  if (!single && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n_tt = cdiv(T, TOK_TILE);
+  Carver c(ws);
+  int32_t* tile_counts = c.take<int32_t>((size_t)n_tt * E_loc * 4);
+  int32_t* tile_base = c.take<int32_t>((size_t)n_tt * E_loc * 4);
+  int32_t* rank = c.take<int32_t>((size_t)T * k * 4);
+
+  GateTileArgs a{};
+  a.ids_in = topk_ids;
+  a.T = T; a.E = E; a.k = k; a.mode = 0;
+  a.do_gate = 0; a.do_permute = 1;
+  a.e_begin = e_begin; a.e_end = e_end;
+  a.tile_counts = tile_counts; a.rank_out = rank;
+  a.single = single ? 1 : 0;
+  a.counts = counts; a.offsets = offsets; a.src_token = src_token; a.dst_row = dst_row;
+  a.BM = 16; a.tile_map = nullptr; a.n_tiles = nullptr;
+  MOE_TRY(launch_gate_tiles(a, n_tt, s));
+  if (!single) {
+    MOE_TRY(launch_permute_scan(tile_counts, n_tt, E_loc, tile_base, counts, offsets, 16, 0, 0,
+                                nullptr, nullptr, s));
+    MOE_TRY(launch_permute_scatter(topk_ids, rank, tile_base, offsets, T, k, e_begin, e_end,
+                                   dst_row, src_token, s));
+  }
+  if (x && T > 0)
+    MOE_TRY(launch_gather_rows(x, src_token, offsets, E_loc, T * (k < E_loc ? k : E_loc), H,
+                               elt_bytes(dt), x_perm, s));
+  return MOE_OK;
+}
+
+size_t moe_grouped_ffn_workspace_size(int max_rows, int E_loc, int H, int I_loc, int dt) {
+  if (max_rows < 0 || E_loc < 1 || H <= 0 || I_loc <= 0 || !valid_dt(dt)) return 0;
+  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc));
+  const int mt = max_tiles_for(max_rows, E_loc, BM);
+  return align_up((size_t)max_rows * I_loc * elt_bytes(dt)) + align_up((size_t)mt * sizeof(int4)) +
+         align_up(4);
+}
+
+int moe_grouped_ffn(const void* x_perm, const void* x, const int32_t* src_token,
+                    const int32_t* offsets, int E_loc, int max_rows, int H, int I_loc,
+                    const void* w13, const void* w2, int dt, void* y_perm, int y_dt, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!valid_dt(dt) || !valid_dt(y_dt) || E_loc < 1 || max_rows < 0 || I_loc <= 0)
+    return MOE_ERR_INVALID_ARG;
+  int st = check_hidden(H);
+  if (st) return st;
+  if (I_loc % 32 || E_loc > 1024) return MOE_ERR_UNSUPPORTED;
+  if (dt == MOE_F32 && y_dt != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (!offsets || !w13 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!x_perm && (!x || !src_token)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_perm, x, src_token, offsets, w13, w2, y_perm, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  if (max_rows == 0) return MOE_OK;
+  const size_t need = moe_grouped_ffn_workspace_size(max_rows, E_loc, H, I_loc, dt);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc));
+  const int mt = max_tiles_for(max_rows, E_loc, BM);
+  Carver c(ws);
+  void* h = c.take<char>((size_t)max_rows * I_loc * elt_bytes(dt));
+  int4* tile_map = c.take<int4>((size_t)mt * sizeof(int4));
+  int32_t* n_tiles = c.take<int32_t>(4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(launch_tile_map_from_offsets(offsets, E_loc, BM, max_rows, mt, tile_map, n_tiles, s));
+  FfnArgs a{};
+  a.x = x_perm ? x_perm : x;
+  a.src_token = x_perm ? nullptr : src_token;
+  a.tile_map = tile_map; a.n_tiles = n_tiles; a.M_dense = 0; a.max_tiles = mt;
+  a.H = H; a.I_loc = I_loc; a.w13 = w13; a.w2 = w2; a.h = h; a.y = y_perm;
+  a.dt = dt; a.y_dt = y_dt;
+  return hip_status(launch_grouped_ffn(a, BM, s));
+}
+
+int moe_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row, const float* topk_w,
+                int T, int k, int H, const void* y_shared, void* y, int dt, void* stream) {
+  if (!valid_dt(dt) || !valid_dt(y_perm_dt) || T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  int st = check_hidden(H);
+  if (st) return st;
+  if (k > KMAX) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !dst_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {y_perm, dst_row, topk_w, y, y_shared};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(y_perm, y_perm_dt, dst_row, topk_w, T, k, H, y_shared, y, dt,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max) {
+  if (check_desc(d) != MOE_OK || T_max < 0) return 0;
+  return layer_layout(d, T_max, nullptr, nullptr);
+}
+
+int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, size_t ws_bytes,
+              moe_debug_out* dbg, void* stream) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  const size_t need = layer_layout(d, T, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  LayerWs l;
+  layer_layout(d, T, ws, &l);
+  if (dbg) {
+    const void* ptrs[] = {dbg->logits, dbg->topk_ids, dbg->topk_w, dbg->counts,
+                          dbg->offsets, dbg->src_token, dbg->dst_row};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+    if (dbg->logits) l.logits = dbg->logits;
+    if (dbg->topk_ids) l.ids = dbg->topk_ids;
+    if (dbg->topk_w) l.w = dbg->topk_w;
+    if (dbg->counts) l.counts = dbg->counts;
+    if (dbg->offsets) l.offsets = dbg->offsets;
+    if (dbg->src_token) l.src_token = dbg->src_token;
+    if (dbg->dst_row) l.dst_row = dbg->dst_row;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E_loc = d->e_end - d->e_begin;
+  auto mark = [&](int i) -> hipError_t {
+    if (dbg && dbg->stage_events[i])
+      return hipEventRecord(static_cast<hipEvent_t>(dbg->stage_events[i]), s);
+    return hipSuccess;
+  };
+
+  MOE_TRY(mark(0));
+  // a1: router logits
+  MOE_TRY(launch_router_logits(x, d->w_router, d->dt, T, d->H, d->E, d->logit_bias, l.logits, s));
+  // a2-a5: gating, histogram, prefix sum, permutation, GEMM tile map
+  const bool single = T <= TOK_TILE;
+  GateTileArgs a{};
+  a.logits = l.logits; a.sel_bias = d->sel_bias;
+  a.ids_out = l.ids; a.w_out = l.w;
+  a.T = T; a.E = d->E; a.k = d->k; a.mode = d->mode;
+  a.do_gate = 1; a.do_permute = 1;
+  a.e_begin = d->e_begin; a.e_end = d->e_end;
+  a.tile_counts = l.tile_counts; a.rank_out = l.rank;
+  a.single = single ? 1 : 0;
+  a.counts = l.counts; a.offsets = l.offsets; a.src_token = l.src_token; a.dst_row = l.dst_row;
+  a.BM = l.BM; a.tile_map = l.tile_map; a.n_tiles = l.n_tiles;
+  a.max_rows = l.max_rows; a.max_tiles = l.max_tiles;
+  MOE_TRY(launch_gate_tiles(a, l.n_tt, s));
+  if (!single) {
+    MOE_TRY(launch_permute_scan(l.tile_counts, l.n_tt, E_loc, l.tile_base, l.counts, l.offsets,
+                                l.BM, l.max_rows, l.max_tiles, l.tile_map, l.n_tiles, s));
+    MOE_TRY(launch_permute_scatter(l.ids, l.rank, l.tile_base, l.offsets, T, d->k, d->e_begin,
+                                   d->e_end, l.dst_row, l.src_token, s));
+  }
+  MOE_TRY(mark(1));
+  // a6-a7: grouped SwiGLU GEMMs, gather fused into the first
+  FfnArgs f{};
+  f.x = x; f.src_token = l.src_token; f.tile_map = l.tile_map; f.n_tiles = l.n_tiles;
+  f.M_dense = 0; f.max_tiles = l.max_tiles;
+  f.H = d->H; f.I_loc = d->I_loc; f.w13 = d->w13; f.w2 = d->w2;
+  f.h = l.h; f.y = l.y_perm; f.dt = d->dt; f.y_dt = d->dt;
+  MOE_TRY(launch_ffn_gate_up(f, l.BM, s));
+  MOE_TRY(mark(2));
+  MOE_TRY(launch_ffn_down(f, l.BM, s));
+  MOE_TRY(mark(3));
+  // a8: shared expert over every token
+  if (d->I_shared > 0) {
+    const int BMs = ffn_row_tile(d->dt, T);
+    FfnArgs g{};
+    g.x = x; g.src_token = nullptr; g.tile_map = nullptr; g.n_tiles = nullptr;
+    g.M_dense = T; g.max_tiles = cdiv(T, BMs);
+    g.H = d->H; g.I_loc = d->I_shared; g.w13 = d->w13_shared; g.w2 = d->w2_shared;
+    g.h = l.h_s; g.y = l.y_s; g.dt = d->dt; g.y_dt = d->dt;
+    MOE_TRY(launch_grouped_ffn(g, BMs, s));
+  }
+  MOE_TRY(mark(4));
+  // a9: inverse permutation + weighted sum (+ shared expert)
+  MOE_TRY(launch_combine(l.y_perm, d->dt, l.dst_row, l.w, T, d->k, d->H,
+                         d->I_shared > 0 ? l.y_s : nullptr, y, d->dt, s));
+  MOE_TRY(mark(5));
+  return MOE_OK;
+}
+
+}  // extern "C"

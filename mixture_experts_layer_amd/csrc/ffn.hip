@@ -1,0 +1,318 @@
+// Grouped SwiGLU expert GEMMs over ragged per-expert row counts, gfx950.
+//
+// "MoE 推理优化全景指南", section Expert GEMM 为什么经常不够大: experts with
+// different row counts m_i run in one schedule, expert i computing
+// [m_i, hidden] @ W_i.  Expert layout per the Moebius paper, section 3.1:
+// W13 (E_loc, 2I, H) with gate and up stacked, W2 (E_loc, H, I).
+//
+// Row counts live on the device.  The grid is sized for the worst case and
+// every block reads its (expert, row range) from a tile map built by the
+// routing kernels; blocks past the map's length exit at once.  Nothing is
+// read back to the host.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+struct DirectArgs {
+  const bf16_t* X;          // activation rows, K contiguous
+  const int32_t* src_token; // null: row r reads X row r; else X row src_token[r]
+  const int4* tile_map;     // null: dense rows [0, M_dense) of expert 0
+  const int32_t* n_tiles;
+  int M_dense;
+  const bf16_t* W;          // [E_loc][rows][K]
+  long long w_stride;       // elements between experts
+  int K;                    // contraction length (multiple of 32)
+  int N_out;                // output columns (multiple of 16 * NT)
+  int up_off;               // SwiGLU: row offset of the up half in W
+  void* Y;                  // [rows][N_out]
+};
+
+// ---------------------------------------------------------------------------
+// Direct-load bf16 MFMA kernel.  A block owns BM = 16*MT rows of one expert
+// and 16*NT output columns; its NW waves split the K dimension and each
+// streams its weight rows straight from HBM into MFMA fragments (every weight
+// element is used by all BM rows at once, so staging it through LDS would buy
+// no reuse).  Partial sums meet in LDS in a fixed order.
+//
+// v_mfma_f32_16x16x32_bf16 with A = weight fragment (row n = lane % 16) and
+// B = activation fragment (column m = lane % 16), both taking 8 consecutive
+// K elements at offset 8 * (lane / 16); the accumulator lane l holds
+// C[n = 4*(l/16) + i][m = l % 16].
+//
+// SWIGLU: W rows [n] (gate) and [up_off + n] (up) are multiplied together and
+// the epilogue writes SiLU(gate) * up.
+// ---------------------------------------------------------------------------
+template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
+  constexpr int NS = SWIGLU ? 2 : 1;
+  constexpr int BM = 16 * MT;
+  constexpr int BN = 16 * NT;
+  constexpr int NACC = MT * NT * NS;
+  constexpr int PITCH = 65;
+  constexpr int U = 4;
+  __shared__ float red[NW * NACC * 4 * PITCH];
+
+  const int n_ntiles = a.N_out / BN;
+  const int tile = blockIdx.x / n_ntiles;
+  const int ntile = blockIdx.x - tile * n_ntiles;
+  int e, r0, r1;
+  if (a.tile_map) {
+    if (tile >= a.n_tiles[0]) return;
+    const int4 tm = a.tile_map[tile];
+    e = tm.x; r0 = tm.y; r1 = tm.z;
+  } else {
+    e = 0; r0 = tile * BM; r1 = min(r0 + BM, a.M_dense);
+    if (r0 >= a.M_dense) return;
+  }
+  const int n0 = ntile * BN;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int kg = 8 * (lane >> 4);
+
+  const bf16_t* xp[MT];
+  bool xv[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = r0 + 16 * mt + (lane & 15);
+    xv[mt] = row < r1;
+    const int src = xv[mt] ? (a.src_token ? a.src_token[row] : row) : 0;
+    xp[mt] = a.X + (size_t)src * a.K + kg;
+  }
+  const bf16_t* We = a.W + (size_t)e * a.w_stride;
+  const bf16_t* wg[NT];
+  const bf16_t* wu[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + 16 * nt + (lane & 15);
+    wg[nt] = We + (size_t)n * a.K + kg;
+    wu[nt] = We + (size_t)(a.up_off + n) * a.K + kg;
+  }
+
+  f32x4_t acc[MT][NT][NS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc[mt][nt][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's contiguous share of the K steps (32 elements each)
+  const int S = a.K / 32;
+  const int s_begin = (S * wid) / NW;
+  const int s_end = (S * (wid + 1)) / NW;
+
+  int s = s_begin;
+  for (; s + U <= s_end; s += U) {
+    uint4 xa[U][MT], wa[U][NT], wb[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ko = (s + u) * 32;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        wa[u][nt] = *reinterpret_cast<const uint4*>(wg[nt] + ko);
+        if (SWIGLU) wb[u][nt] = *reinterpret_cast<const uint4*>(wu[nt] + ko);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        xa[u][mt] = xv[mt] ? *reinterpret_cast<const uint4*>(xp[mt] + ko) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[mt][nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(wa[u][nt]), as_bf16x8(xa[u][mt]), acc[mt][nt][0], 0, 0, 0);
+          if (SWIGLU)
+            acc[mt][nt][NS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(wb[u][nt]), as_bf16x8(xa[u][mt]), acc[mt][nt][NS - 1], 0, 0, 0);
+        }
+  }
+  for (; s < s_end; ++s) {
+    const int ko = s * 32;
+    uint4 xa[MT], wa[NT], wb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      wa[nt] = *reinterpret_cast<const uint4*>(wg[nt] + ko);
+      if (SWIGLU) wb[nt] = *reinterpret_cast<const uint4*>(wu[nt] + ko);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      xa[mt] = xv[mt] ? *reinterpret_cast<const uint4*>(xp[mt] + ko) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[mt][nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(wa[nt]), as_bf16x8(xa[mt]), acc[mt][nt][0], 0, 0, 0);
+        if (SWIGLU)
+          acc[mt][nt][NS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(wb[nt]), as_bf16x8(xa[mt]), acc[mt][nt][NS - 1], 0, 0, 0);
+      }
+  }
+
+  // partial sums -> LDS: red[w][((mt*NT + nt)*NS + which)*4 + i][lane]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int w = 0; w < NS; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[(wid * NACC + (mt * NT + nt) * NS + w) * 4 * PITCH + i * PITCH + lane] =
+              acc[mt][nt][w][i];
+  __syncthreads();
+
+  // reduce over waves in wave order and write BM x BN outputs, n fastest
+  for (int o = threadIdx.x; o < BM * BN; o += NW * 64) {
+    const int m = o / BN, n = o - m * BN;
+    const int row = r0 + m;
+    if (row >= r1) continue;
+    const int mt = m >> 4, ml = m & 15, nt = n >> 4, nl = n & 15;
+    const int i = nl & 3, src_lane = ml + 16 * (nl >> 2);
+    const int base = ((mt * NT + nt) * NS) * 4 * PITCH + i * PITCH + src_lane;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      g += red[w * NACC * 4 * PITCH + base];
+      if (SWIGLU) u += red[w * NACC * 4 * PITCH + base + 4 * PITCH];
+    }
+    const float out = SWIGLU ? silu(g) * u : g;
+    const size_t yi = (size_t)row * a.N_out + n0 + n;
+    if (OUT_BF16) reinterpret_cast<bf16_t*>(a.Y)[yi] = f32_to_bf16(out);
+    else reinterpret_cast<float*>(a.Y)[yi] = out;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 layer: one thread per output element of a 16 x 16 tile, plain FMA
+// dot products over K (the fp32 configuration is small).
+// ---------------------------------------------------------------------------
+struct F32Args {
+  const float* X;
+  const int32_t* src_token;
+  const int4* tile_map;
+  const int32_t* n_tiles;
+  int M_dense;
+  const float* W;
+  long long w_stride;
+  int K, N_out, up_off;
+  float* Y;
+};
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void ffn_f32_kernel(F32Args a) {
+  const int n_ntiles = a.N_out / 16;
+  const int tile = blockIdx.x / n_ntiles;
+  const int ntile = blockIdx.x - tile * n_ntiles;
+  int e, r0, r1;
+  if (a.tile_map) {
+    if (tile >= a.n_tiles[0]) return;
+    const int4 tm = a.tile_map[tile];
+    e = tm.x; r0 = tm.y; r1 = tm.z;
+  } else {
+    e = 0; r0 = tile * 16; r1 = min(r0 + 16, a.M_dense);
+    if (r0 >= a.M_dense) return;
+  }
+  const int row = r0 + (threadIdx.x >> 4);
+  const int n = ntile * 16 + (threadIdx.x & 15);
+  if (row >= r1) return;
+  const int src = a.src_token ? a.src_token[row] : row;
+  const float4* xr = reinterpret_cast<const float4*>(a.X + (size_t)src * a.K);
+  const float* We = a.W + (size_t)e * a.w_stride;
+  const float4* wg = reinterpret_cast<const float4*>(We + (size_t)n * a.K);
+  const float4* wu = reinterpret_cast<const float4*>(We + (size_t)(a.up_off + n) * a.K);
+  float g = 0.f, u = 0.f;
+  for (int q = 0; q < a.K / 4; ++q) {
+    const float4 xv = xr[q];
+    const float4 gv = wg[q];
+    g = fmaf(xv.x, gv.x, g); g = fmaf(xv.y, gv.y, g); g = fmaf(xv.z, gv.z, g); g = fmaf(xv.w, gv.w, g);
+    if (SWIGLU) {
+      const float4 uv = wu[q];
+      u = fmaf(xv.x, uv.x, u); u = fmaf(xv.y, uv.y, u); u = fmaf(xv.z, uv.z, u); u = fmaf(xv.w, uv.w, u);
+    }
+  }
+  a.Y[(size_t)row * a.N_out + n] = SWIGLU ? silu(g) * u : g;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+int ffn_row_tile(int dt, int mean_rows) {
+  if (dt == 0) return 16;
+  if (mean_rows <= 16) return 16;
+  if (mean_rows <= 32) return 32;
+  return 64;
+}
+
+static int pick_nw(int steps, int max_nw) {
+  int nw = 1;
+  while (nw * 2 <= max_nw && steps / (nw * 2) >= 6) nw *= 2;
+  return nw;
+}
+
+template <int MT, int NW, bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_direct_t(const DirectArgs& a, int max_tiles, hipStream_t st) {
+  const int grid = max_tiles * (a.N_out / 16);
+  ffn_direct_kernel<MT, 1, NW, SWIGLU, OUT_BF16><<<grid, NW * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int MT, int MAX_NW, bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_direct_nw(const DirectArgs& a, int nw, int max_tiles, hipStream_t st) {
+  switch (nw) {
+    case 1: return launch_direct_t<MT, 1, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    case 2: return launch_direct_t<MT, 2, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    case 4: return launch_direct_t<MT, 4, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    default:
+      if constexpr (MAX_NW >= 16) {
+        if (nw >= 16) return launch_direct_t<MT, 16, SWIGLU, OUT_BF16>(a, max_tiles, st);
+      }
+      return launch_direct_t<MT, 8, SWIGLU, OUT_BF16>(a, max_tiles, st);
+  }
+}
+
+template <bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, hipStream_t st) {
+  const int steps = a.K / 32;
+  if (BM == 16) return launch_direct_nw<1, 16, SWIGLU, OUT_BF16>(a, pick_nw(steps, 16), max_tiles, st);
+  if (BM == 32) return launch_direct_nw<2, 16, SWIGLU, OUT_BF16>(a, pick_nw(steps, 16), max_tiles, st);
+  return launch_direct_nw<4, 8, SWIGLU, OUT_BF16>(a, pick_nw(steps, 8), max_tiles, st);
+}
+
+hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {
+  if (a.max_tiles <= 0) return hipSuccess;
+  if (a.dt == 0) {
+    F32Args g1{(const float*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
+               (const float*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, (float*)a.h};
+    ffn_f32_kernel<true><<<a.max_tiles * (a.I_loc / 16), 256, 0, st>>>(g1);
+    return hipGetLastError();
+  }
+  DirectArgs g1{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
+                (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h};
+  return launch_direct<true, true>(g1, BM, a.max_tiles, st);
+}
+
+hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st) {
+  if (a.max_tiles <= 0) return hipSuccess;
+  if (a.dt == 0) {
+    F32Args g2{(const float*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
+               (const float*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, (float*)a.y};
+    ffn_f32_kernel<false><<<a.max_tiles * (a.H / 16), 256, 0, st>>>(g2);
+    return hipGetLastError();
+  }
+  DirectArgs g2{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
+                (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y};
+  if (a.y_dt == 0) return launch_direct<false, false>(g2, BM, a.max_tiles, st);
+  return launch_direct<false, true>(g2, BM, a.max_tiles, st);
+}
+
+hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st) {
+  hipError_t err = launch_ffn_gate_up(a, BM, st);
+  if (err != hipSuccess) return err;
+  return launch_ffn_down(a, BM, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,118 @@
+// Device helpers for the gfx950 kernels: bf16 conversion, 16-byte vector
+// loads, MFMA fragment types, and block-wide scans used by the routing
+// metadata kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_kernels.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Expand 8 packed bf16 (one 16-byte load) into floats.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of n ints held in LDS (n <= 4 * blockDim.x).
+// `data` is replaced by its exclusive prefix sums; returns the total.
+// `tmp` needs blockDim.x + 1 ints.  All threads of the block must call it.
+// ---------------------------------------------------------------------------
+__device__ inline int block_exclusive_scan(int* data, int n, int* tmp) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int b = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) local += data[b + i];
+  tmp[tid] = local;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread sums.
+  for (int off = 1; off < nt; off <<= 1) {
+    int v = (tid >= off) ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += v;
+    __syncthreads();
+  }
+  int run = tmp[tid] - local;
+  const int total = tmp[nt - 1];
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) {
+      const int v = data[b + i];
+      data[b + i] = run;
+      run += v;
+    }
+  __syncthreads();
+  return total;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM tile map: for every local expert, ceil(count / BM) row tiles of at most
+// BM rows.  Entry = {expert, row_begin, row_end, 0}; n_tiles[0] = number of
+// entries.  cnt[] holds counts and off[] exclusive offsets (both in LDS).
+// An expert whose rows fall outside [0, max_rows) gets no tiles, and at most
+// max_tiles entries are written, so a GEMM driven by the map never indexes
+// outside its buffers even if the offsets were inconsistent.
+// scratch: E_loc ints of LDS, tmp: blockDim.x + 1 ints of LDS.
+// ---------------------------------------------------------------------------
+__device__ inline int tiles_of(int c, int o, int BM, int max_rows) {
+  if (c <= 0 || o < 0 || o + c > max_rows) return 0;
+  return (c + BM - 1) / BM;
+}
+
+__device__ inline void block_build_tile_map(const int* cnt, const int* off, int E_loc, int BM,
+                                            int max_rows, int max_tiles, int* scratch, int* tmp,
+                                            int4* tile_map, int* n_tiles) {
+  for (int e = threadIdx.x; e < E_loc; e += blockDim.x)
+    scratch[e] = tiles_of(cnt[e], off[e], BM, max_rows);
+  __syncthreads();
+  const int total = block_exclusive_scan(scratch, E_loc, tmp);
+  for (int e = threadIdx.x; e < E_loc; e += blockDim.x) {
+    const int nt = tiles_of(cnt[e], off[e], BM, max_rows);
+    const int r_end = off[e] + cnt[e];
+    for (int q = 0; q < nt; ++q) {
+      const int slot = scratch[e] + q;
+      if (slot >= max_tiles) break;
+      const int r0 = off[e] + q * BM;
+      tile_map[slot] = make_int4(e, r0, min(r0 + BM, r_end), 0);
+    }
+  }
+  if (threadIdx.x == 0) n_tiles[0] = min(total, max_tiles);
+}
+
+}  // namespace moe

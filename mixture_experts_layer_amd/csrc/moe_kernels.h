@@ -1,0 +1,79 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int TOK_TILE = 64;   // tokens per routing-metadata tile
+constexpr int KMAX = 32;       // largest supported top-k
+
+struct GateTileArgs {
+  // gating
+  const float* logits;      // [T][E]
+  const float* sel_bias;    // [E] or null (mode 3)
+  const int32_t* ids_in;    // [T][k] when do_gate == 0
+  int32_t* ids_out;         // [T][k]
+  float* w_out;             // [T][k]
+  int T, E, k, mode;
+  int do_gate, do_permute;
+  int e_begin, e_end;
+  // multi-tile outputs
+  int32_t* tile_counts;     // [n_tiles_tok][E_loc]
+  int32_t* rank_out;        // [T][k]
+  // single-tile outputs
+  int single;
+  int32_t* counts;          // [E_loc]
+  int32_t* offsets;         // [E_loc + 1]
+  int32_t* src_token;       // [T*k]
+  int32_t* dst_row;         // [T][k]
+  int BM;                   // GEMM row tile for the tile map
+  int max_rows, max_tiles;  // bounds of the GEMM buffers the map drives
+  int4* tile_map;           // [max_tiles] or null
+  int32_t* n_tiles;         // [1]
+};
+
+hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,
+                                const float* bias, float* logits, hipStream_t st);
+hipError_t launch_gate_tiles(const GateTileArgs& a, int n_tiles_tok, hipStream_t st);
+
+// Multi-tile permutation: per-expert scan over tiles, then scatter.
+hipError_t launch_permute_scan(const int32_t* tile_counts, int n_tiles_tok, int E_loc,
+                               int32_t* tile_base, int32_t* counts, int32_t* offsets, int BM,
+                               int max_rows, int max_tiles, int4* tile_map, int32_t* n_tiles,
+                               hipStream_t st);
+hipError_t launch_permute_scatter(const int32_t* ids, const int32_t* rank, const int32_t* tile_base,
+                                  const int32_t* offsets, int T, int k, int e_begin, int e_end,
+                                  int32_t* dst_row, int32_t* src_token, hipStream_t st);
+hipError_t launch_gather_rows(const void* x, const int32_t* src_token, const int32_t* offsets,
+                              int E_loc, int max_rows, int H, int elt_bytes, void* x_perm,
+                              hipStream_t st);
+hipError_t launch_tile_map_from_offsets(const int32_t* offsets, int E_loc, int BM, int max_rows,
+                                        int max_tiles, int4* tile_map, int32_t* n_tiles,
+                                        hipStream_t st);
+
+// Grouped expert GEMMs.
+struct FfnArgs {
+  const void* x;            // activations: x_perm rows, or token rows gathered via src_token
+  const int32_t* src_token; // null: row r reads x row r
+  const int4* tile_map;     // null: dense rows [0, M) of expert 0 in BM tiles
+  const int32_t* n_tiles;
+  int M_dense;              // rows when tile_map is null
+  int max_tiles;
+  int H, I_loc;
+  const void* w13;          // [E_loc][2*I_loc][H]
+  const void* w2;           // [E_loc][H][I_loc]
+  void* h;                  // [rows][I_loc], dtype dt
+  void* y;                  // [rows][H], dtype y_dt
+  int dt, y_dt;
+};
+int ffn_row_tile(int dt, int mean_rows);
+hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st);
+hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st);
+hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st);
+
+hipError_t launch_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row,
+                          const float* w, int T, int k, int H, const void* y_shared, void* y,
+                          int dt, hipStream_t st);
+
+}  // namespace moe

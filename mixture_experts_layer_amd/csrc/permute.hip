@@ -1,0 +1,149 @@
+// Prefix sums and the stable scatter of token copies for gfx950.
+//
+// "MoE 推理优化全景指南", section Dispatch 并不是一次普通 all-to-all:
+// histogram -> prefix sum -> permute, each expert's copies contiguous and in
+// token order.  The per-tile histograms and in-tile ranks come from the gating
+// kernel; here one block turns them into offsets and per-tile bases, and a
+// wide kernel writes dst_row / src_token.  No atomics anywhere, so the
+// permutation is the same on every run.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+// One block: for every local expert, an exclusive scan of its counts over the
+// token tiles (tile_base), its total (counts), then the exclusive scan over
+// experts (offsets) and the GEMM tile map.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __restrict__ tile_counts,
+                                                            int n_tt, int E_loc,
+                                                            int32_t* __restrict__ tile_base,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets, int BM,
+                                                            int max_rows, int max_tiles,
+                                                            int4* __restrict__ tile_map,
+                                                            int32_t* __restrict__ n_tiles) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1025];
+  __shared__ int s_scr[1024];
+  __shared__ int s_tmp[1025];
+  // Threads of one expert walk the tiles in order; 4 tiles per load batch.
+  for (int el = threadIdx.x; el < E_loc; el += blockDim.x) {
+    int run = 0;
+    int tt = 0;
+    for (; tt + 4 <= n_tt; tt += 4) {
+      const int c0 = tile_counts[(size_t)(tt + 0) * E_loc + el];
+      const int c1 = tile_counts[(size_t)(tt + 1) * E_loc + el];
+      const int c2 = tile_counts[(size_t)(tt + 2) * E_loc + el];
+      const int c3 = tile_counts[(size_t)(tt + 3) * E_loc + el];
+      tile_base[(size_t)(tt + 0) * E_loc + el] = run; run += c0;
+      tile_base[(size_t)(tt + 1) * E_loc + el] = run; run += c1;
+      tile_base[(size_t)(tt + 2) * E_loc + el] = run; run += c2;
+      tile_base[(size_t)(tt + 3) * E_loc + el] = run; run += c3;
+    }
+    for (; tt < n_tt; ++tt) {
+      const int c = tile_counts[(size_t)tt * E_loc + el];
+      tile_base[(size_t)tt * E_loc + el] = run;
+      run += c;
+    }
+    s_cnt[el] = run;
+    s_off[el] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
+  if (threadIdx.x == 0) s_off[E_loc] = total;
+  __syncthreads();
+  for (int el = threadIdx.x; el < E_loc; el += blockDim.x) counts[el] = s_cnt[el];
+  for (int el = threadIdx.x; el <= E_loc; el += blockDim.x) offsets[el] = s_off[el];
+  if (tile_map)
+    block_build_tile_map(s_cnt, s_off, E_loc, BM, max_rows, max_tiles, s_scr, s_tmp, tile_map,
+                         n_tiles);
+}
+
+// One thread per (token, slot): row = offsets[e] + tile_base[tile][e] + rank.
+__global__ __launch_bounds__(256) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ offsets, int T, int k,
+    int e_begin, int e_end, int32_t* __restrict__ dst_row, int32_t* __restrict__ src_token) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= T * k) return;
+  const int t = p / k;
+  const int e = ids[p];
+  int row = -1;
+  if (e >= e_begin && e < e_end) {
+    const int el = e - e_begin;
+    const int E_loc = e_end - e_begin;
+    row = offsets[el] + tile_base[(size_t)(t / TOK_TILE) * E_loc + el] + rank[p];
+    src_token[row] = t;
+  }
+  dst_row[p] = row;
+}
+
+// x_perm[row] = x[src_token[row]] for rows < offsets[E_loc]; 16-byte copies.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ src_token,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int E_loc, int row_vecs,
+                                                          uint4* __restrict__ x_perm) {
+  const int row = blockIdx.x;
+  if (row >= offsets[E_loc]) return;
+  const int t = src_token[row];
+  for (int c = threadIdx.x; c < row_vecs; c += blockDim.x)
+    x_perm[(size_t)row * row_vecs + c] = x[(size_t)t * row_vecs + c];
+}
+
+// Tile map for a standalone grouped-FFN call, from device offsets.
+__global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets,
+                                                       int E_loc, int BM, int max_rows,
+                                                       int max_tiles,
+                                                       int4* __restrict__ tile_map,
+                                                       int32_t* __restrict__ n_tiles) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1025];
+  __shared__ int s_scr[1024];
+  __shared__ int s_tmp[257];
+  for (int e = threadIdx.x; e <= E_loc; e += blockDim.x) s_off[e] = offsets[e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E_loc; e += blockDim.x) s_cnt[e] = s_off[e + 1] - s_off[e];
+  __syncthreads();
+  block_build_tile_map(s_cnt, s_off, E_loc, BM, max_rows, max_tiles, s_scr, s_tmp, tile_map,
+                       n_tiles);
+}
+
+hipError_t launch_permute_scan(const int32_t* tile_counts, int n_tt, int E_loc,
+                               int32_t* tile_base, int32_t* counts, int32_t* offsets, int BM,
+                               int max_rows, int max_tiles, int4* tile_map, int32_t* n_tiles,
+                               hipStream_t st) {
+  const int threads = E_loc > 512 ? 1024 : (E_loc > 256 ? 512 : 256);
+  permute_scan_kernel<<<1, threads, 0, st>>>(tile_counts, n_tt, E_loc, tile_base, counts, offsets,
+                                             BM, max_rows, max_tiles, tile_map, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scatter(const int32_t* ids, const int32_t* rank, const int32_t* tile_base,
+                                  const int32_t* offsets, int T, int k, int e_begin, int e_end,
+                                  int32_t* dst_row, int32_t* src_token, hipStream_t st) {
+  const int n = T * k;
+  if (n <= 0) return hipSuccess;
+  permute_scatter_kernel<<<(n + 255) / 256, 256, 0, st>>>(ids, rank, tile_base, offsets, T, k,
+                                                          e_begin, e_end, dst_row, src_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* src_token, const int32_t* offsets,
+                              int E_loc, int max_rows, int H, int elt_bytes, void* x_perm,
+                              hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  const int row_vecs = H * elt_bytes / 16;
+  gather_rows_kernel<<<max_rows, 256, 0, st>>>((const uint4*)x, src_token, offsets, E_loc,
+                                               row_vecs, (uint4*)x_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_map_from_offsets(const int32_t* offsets, int E_loc, int BM, int max_rows,
+                                        int max_tiles, int4* tile_map, int32_t* n_tiles,
+                                        hipStream_t st) {
+  tile_map_kernel<<<1, 256, 0, st>>>(offsets, E_loc, BM, max_rows, max_tiles, tile_map, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

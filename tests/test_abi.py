@@ -1,0 +1,135 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, and rejects bad arguments before touching a GPU.  No call
+here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_amd as M
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 10
+    out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(moe_\w+)", out))
+    assert set(names) <= exported
+    assert set(names) == set(M.EXPORTED_SYMBOLS)
+    lib = M.get_lib()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings():
+    assert M.moe_abi_version() == 1
+    for s in range(6):
+        assert M.moe_status_str(s)
+    assert M.moe_status_str(99) == "unknown status"
+
+
+def test_workspace_queries():
+    assert M.moe_permute_workspace_size(8192, 8, 128) > 8192 * 8 * 4
+    assert M.moe_permute_workspace_size(-1, 8, 128) == 0
+    assert M.moe_grouped_ffn_workspace_size(65536, 128, 4096, 1536, 1) >= 65536 * 1536 * 2
+    d = M.MoELayerDesc(H=4096, E=128, k=8, I_loc=1536, e_begin=0, e_end=128, I_shared=0, mode=2,
+                       dt=1, w_router=256, w13=512, w2=768)
+    n = M.moe_layer_workspace_size(d, 8192)
+    assert n >= 8192 * 8 * (1536 + 4096) * 2
+    assert M.moe_layer_workspace_size(d, 16) < n
+    d.k = 200
+    assert M.moe_layer_workspace_size(d, 16) == 0
+
+
+class _FakePtr:
+    """Stands in for a device tensor: argument checks read only the address."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+P = _FakePtr(1 << 20)
+MIS = _FakePtr((1 << 20) + 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9, E=8), 1),            # k > E
+    (dict(k=0), 1),
+    (dict(T=-1), 1),
+    (dict(mode=7), 1),
+    (dict(E=2000, k=2), 2),         # beyond the supported E
+    (dict(k=40, E=64), 2),          # beyond the supported k
+    (dict(H=100), 2),               # H not a multiple of 32
+    (dict(H=0), 1),
+])
+def test_route_rejects(kw, status):
+    a = dict(T=4, H=256, E=8, k=2, mode=0)
+    a.update(kw)
+    with pytest.raises(M.MoEError) as e:
+        M.moe_route(P, P, 1, a["T"], a["H"], a["E"], a["k"], a["mode"], None, None, P, P, P,
+                    stream=0)
+    assert e.value.status == status
+
+
+def test_route_rejects_misaligned_and_null():
+    with pytest.raises(M.MoEError) as e:
+        M.moe_route(MIS, P, 1, 4, 256, 8, 2, 0, None, None, P, P, P, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:
+        M.moe_route(P, P, 1, 4, 256, 8, 2, 0, None, None, None, P, P, stream=0)
+    assert e.value.status == 1
+
+
+def test_permute_rejects():
+    with pytest.raises(M.MoEError) as e:   # bad expert range
+        M.moe_permute(P, 4, 2, 8, 5, 3, None, 0, 0, P, P, P, P, None, P, 1 << 20, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:   # multi-tile batch without workspace
+        M.moe_permute(P, 1000, 2, 8, 0, 8, None, 0, 0, P, P, P, P, None, None, 0, stream=0)
+    assert e.value.status == 3
+
+
+def test_grouped_ffn_and_combine_reject():
+    with pytest.raises(M.MoEError) as e:   # I_loc not a multiple of 32
+        M.moe_grouped_ffn(P, None, None, P, 8, 16, 256, 100, P, P, 1, P, 1, P, 1 << 20, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(M.MoEError) as e:   # no workspace
+        M.moe_grouped_ffn(P, None, None, P, 8, 16, 256, 128, P, P, 1, P, 1, None, 0, stream=0)
+    assert e.value.status == 3
+    with pytest.raises(M.MoEError) as e:   # fp32 layer cannot emit bf16 rows
+        M.moe_grouped_ffn(P, None, None, P, 8, 16, 256, 128, P, P, 0, P, 1, P, 1 << 20, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(M.MoEError) as e:
+        M.moe_combine(P, 1, P, P, 4, 2, 256, None, MIS, 1, stream=0)
+    assert e.value.status == 1
+
+
+def test_layer_rejects_bad_descriptors():
+    base = dict(H=256, E=8, k=2, I_loc=128, e_begin=0, e_end=8, I_shared=0, mode=0, dt=1,
+                w_router=1 << 20, w13=1 << 21, w2=1 << 22)
+    for change, status in ((dict(e_end=9), 1), (dict(e_begin=8), 1), (dict(I_loc=100), 2),
+                           (dict(dt=5), 1), (dict(w13=(1 << 21) + 8), 1), (dict(I_shared=64), 1)):
+        d = M.MoELayerDesc(**{**base, **change})
+        with pytest.raises(M.MoEError) as e:
+            M.moe_layer(d, 4, P, P, P, 1 << 30, stream=0)
+        assert e.value.status == status, change
+    d = M.MoELayerDesc(**base)
+    with pytest.raises(M.MoEError) as e:
+        M.moe_layer(d, 4, P, P, P, 10, stream=0)
+    assert e.value.status == 3
+    M.moe_layer(d, 0, P, P, P, 0, stream=0)   # T = 0 is a no-op
