@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""MoE layer forward benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--T T]
+
+A step is one pass of the whole layer (router, gating, histogram, prefix sum,
+permutation, grouped SwiGLU GEMMs, shared expert if any, combine) over one
+batch of T seeded synthetic tokens, through the fused C entry point
+moe_layer.  Inputs are resident in HBM before the timed region.  Steps
+rotate over `copies` byte-identical copies of the layer's weights at
+distinct addresses, so the 256 MB Infinity Cache cannot serve the weights
+of one step from the previous one.
+
+Printed: one JSON line with tokens/s (value), the roofline of the dominant
+kernel (timed live with HIP events that moe_layer records on its stream at
+stage boundaries), the whole-layer roofline fraction, a per-stage time split,
+a graph-replayed sweep over the workload's other token counts, and the CPU
+oracle timed on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s and % roofline (HBM GB/s at decode, MFMA at prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X fp32 (vector/matrix) for the fp32 layer
+WORKLOAD_NAMES = {
+    "toy_f32": "toy_moe_layer_f32",
+    "mixtral_8x7b": "mixtral_8x7b_moe_layer",
+    "qwen3_ep_all128": "qwen3_235b_a22b_moe_layer_ep_all128",
+    "qwen3_tp8_rank0": "qwen3_235b_a22b_moe_layer_tp8_rank0",
+    "deepseek_v3": "deepseek_v3_moe_layer_shared1",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_ep_all128", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--T", type=int, default=None, help="tokens per step (default: largest of the workload)")
+    ap.add_argument("--copies", type=int, default=None, help="weight copies to rotate over")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
+    ap.add_argument("--sweep-workloads", default="qwen3_ep_all128,qwen3_tp8_rank0",
+                    help="workloads whose token counts are swept (comma list)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens in the CPU oracle sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (bytes / FLOPs the method itself must move or compute)
+# ---------------------------------------------------------------------------
+
+def layer_work(cfg, T, counts, I_loc, elt):
+    rows = int(sum(counts))
+    touched = int(sum(1 for c in counts if c > 0))
+    H, E = cfg.H, cfg.E
+    w_bytes = elt * (E * H + touched * 3 * I_loc * H + 3 * cfg.I_shared * H)
+    b_alg = w_bytes + 2 * elt * T * H
+    f_alg = 2 * T * E * H + 6 * rows * I_loc * H + 6 * T * cfg.I_shared * H
+    g1_flops = 4 * rows * I_loc * H
+    g1_bytes = elt * (touched * 2 * I_loc * H + T * H + rows * I_loc)
+    return dict(rows=rows, touched=touched, b_alg=b_alg, f_alg=f_alg, g1_flops=g1_flops,
+                g1_bytes=g1_bytes)
+
+
+def roofs(cfg):
+    if cfg.dtype == "f32":
+        return HBM_PEAK_GBS, MFMA_F32_PEAK_TFLOPS
+    return HBM_PEAK_GBS, MFMA_BF16_PEAK_TFLOPS
+
+
+# ---------------------------------------------------------------------------
+# GPU setup
+# ---------------------------------------------------------------------------
+
+class Bench:
+    def __init__(self, name, T_max, copies):
+        import torch
+        import mixture_experts_layer_amd as M
+        import workloads as W
+        self.torch, self.M, self.W = torch, M, W
+        self.cfg = cfg = W.CONFIGS[name]
+        L = W.make_layer(cfg, device="cuda", seed=0, T_max=T_max)
+        w13, w2 = W.share_weights(L.w13, L.w2, cfg.tp_P, cfg.tp_rank)
+        L.w13 = L.w2 = None
+        torch.cuda.empty_cache()
+        self.L = L
+        self.elt = 4 if cfg.dtype == "f32" else 2
+        self.I_loc = w13.shape[1] // 2
+        per_copy = (w13.numel() + w2.numel() + L.w_r.numel()) * self.elt
+        if copies is None:
+            copies = max(2, min(16, math.ceil(2.0e9 / per_copy)))
+        self.copies = copies
+        self.layers = []
+        for c in range(copies):
+            a, b, r = (w13, w2, L.w_r) if c == 0 else (w13.clone(), w2.clone(), L.w_r.clone())
+            d = M.layer_desc(cfg.H, cfg.E, cfg.k, self.I_loc, cfg.mode, M.dtype_code(L.x), r, a, b,
+                             I_shared=cfg.I_shared, w13_shared=L.w13_shared,
+                             w2_shared=L.w2_shared, logit_bias=L.logit_bias, sel_bias=L.sel_bias)
+            self.layers.append((d, a, b, r))
+        self.ws_bytes = M.moe_layer_workspace_size(self.layers[0][0], T_max)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.y_full = torch.empty((T_max, cfg.H), dtype=L.x.dtype, device="cuda")
+        self.set_T(T_max)
+        torch.cuda.synchronize()
+
+    def set_T(self, T):
+        self.T = T
+        self.x = self.L.x[:T]
+        self.y = self.y_full[:T]
+
+    def counts(self):
+        torch, M = self.torch, self.M
+        E_loc = self.cfg.E_loc
+        counts = torch.empty((E_loc,), dtype=torch.int32, device="cuda")
+        dbg = M.debug_out(counts=counts)
+        M.moe_layer(self.layers[0][0], self.T, self.x, self.y, self.ws, self.ws_bytes, dbg)
+        torch.cuda.synchronize()
+        return counts.cpu().tolist()
+
+    def step(self, i, dbg=None):
+        d = self.layers[i % self.copies][0]
+        self.M.moe_layer(d, self.T, self.x, self.y, self.ws, self.ws_bytes, dbg)
+
+    def timed_eager(self, steps, warmup):
+        """Exactly `steps` eager layer calls; every call records the six stage
+        events on the library's stream."""
+        torch, M = self.torch, self.M
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        for row in evs:
+            for e in row:
+                e.record()          # materialise the underlying hipEvent_t
+        dbgs = [M.debug_out(stage_events=[e.cuda_event for e in row]) for row in evs]
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, dbgs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / steps
+        names = ["route_permute", "gemm_gate_up", "gemm_down", "shared_expert", "combine"]
+        split = {n: sum(r[j].elapsed_time(r[j + 1]) for r in evs) / steps for j, n in enumerate(names)}
+        return ms, split
+
+    def timed_graph(self, steps, warmup):
+        """Layer time from replays of a HIP graph holding one layer call per
+        weight copy (launch overhead amortised, as graph-replayed decode)."""
+        torch = self.torch
+        for i in range(max(warmup, 2)):
+            self.step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(self.copies):
+                self.step(c)
+        reps = max(1, math.ceil(steps / self.copies))
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / (reps * self.copies)
+
+
+def roofline_entry(cfg, work, t_g1_ms):
+    hbm, mfma = roofs(cfg)
+    ai = work["g1_flops"] / max(work["g1_bytes"], 1)
+    ridge = mfma * 1e12 / (hbm * 1e9)
+    if ai >= ridge:
+        ach = work["g1_flops"] / (t_g1_ms * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=round(ach, 2), peak=mfma, unit="TFLOP/s",
+                    frac=round(ach / mfma, 4), traffic=None)
+    ach = work["g1_bytes"] / (t_g1_ms * 1e-3) / 1e9
+    return dict(bound="hbm", achieved=round(ach, 1), peak=hbm, unit="GB/s",
+                frac=round(ach / hbm, 4), traffic=None)
+
+
+def layer_roof_frac(cfg, work, ms):
+    hbm, mfma = roofs(cfg)
+    t_roof = max(work["b_alg"] / (hbm * 1e9), work["f_alg"] / (mfma * 1e12))
+    bound = "hbm" if work["b_alg"] / (hbm * 1e9) >= work["f_alg"] / (mfma * 1e12) else "mfma"
+    return bound, t_roof * 1e3, t_roof / (ms * 1e-3)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(bench, n_sample):
+    import numpy as np
+    import torch
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    L, cfg = bench.L, bench.cfg
+    W = bench.W
+    T = bench.T
+    n = min(n_sample, T)
+    idx = W.sample_rows(T, n, seed=1).numpy()
+    f = lambda t: None if t is None else t.float().cpu().numpy()
+    x = f(L.x[:T])[idx]
+    w_r = f(L.w_r)
+    lb = f(L.logit_bias)
+    sb = f(L.sel_bias)
+    # host copies of the weights stay in their storage dtype; the oracle's
+    # per-expert widening to float32 is inside the timed region
+    w13_h = bench.layers[0][1].cpu()
+    w2_h = bench.layers[0][2].cpu()
+
+    class V:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return self.t[e].float().numpy()
+
+    kw = {}
+    if cfg.I_shared:
+        kw = dict(w13_shared=f(L.w13_shared), w2_shared=f(L.w2_shared))
+    t0 = time.perf_counter()
+    O.moe_layer(x, w_r, V(w13_h), V(w2_h), cfg.k, cfg.mode, logit_bias=lb, sel_bias=sb,
+                dtype=np.float32, **kw)
+    dt = time.perf_counter() - t0
+    return dict(value=round(n / dt, 2), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{n} of the {T} tokens (seeded subset), float32 numpy oracle, "
+                       f"per-expert bf16->fp32 widening inside the timed region; {dt:.1f} s")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; this build runs the single-GPU share of the layer only.", flush=True)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.workload]
+    T = args.T or cfg.T_max
+
+    bench = Bench(args.workload, T, args.copies)
+    counts = bench.counts()
+    work = layer_work(cfg, T, counts, bench.I_loc, bench.elt)
+    ms, split = bench.timed_eager(args.steps, args.warmup)
+    roof = roofline_entry(cfg, work, split["gemm_gate_up"])
+    roof["kernel"] = "ffn_direct_kernel (gate/up GEMM + SwiGLU)"
+    roof["avg_launch_ms"] = round(split["gemm_gate_up"], 4)
+    l_bound, t_roof_ms, l_frac = layer_roof_frac(cfg, work, ms)
+    ms_graph = bench.timed_graph(args.steps, args.warmup)
+
+    sweep = []
+    if not args.no_sweep:
+        for name in [s for s in args.sweep_workloads.split(",") if s]:
+            c2 = W.CONFIGS[name]
+            Ts = [T2 for T2 in c2.T_list if not (name == args.workload and T2 == T)]
+            if not Ts:
+                continue
+            b2 = bench if name == args.workload else Bench(name, max(Ts), None)
+            for T2 in Ts:
+                b2.set_T(T2)
+                w2k = layer_work(c2, T2, b2.counts(), b2.I_loc, b2.elt)
+                ms2 = b2.timed_graph(max(args.steps, 20), args.warmup)
+                bd, tr, fr = layer_roof_frac(c2, w2k, ms2)
+                sweep.append(dict(workload=WORKLOAD_NAMES[name], T=T2, ms=round(ms2, 4),
+                                  tokens_per_s=round(T2 / (ms2 * 1e-3), 1), bound=bd,
+                                  roofline_ms=round(tr, 4), frac=round(fr, 4),
+                                  touched_experts=w2k["touched"]))
+                print(f"# sweep {name} T={T2}: {ms2:.4f} ms, {fr:.3f} of roofline ({bd})",
+                      file=sys.stderr, flush=True)
+            if b2 is not bench:
+                del b2
+                torch.cuda.empty_cache()
+            bench.set_T(T)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(bench, args.cpu_sample)
+
+    imb = max(counts) / (sum(counts) / len(counts)) if sum(counts) else 0.0
+    line = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "T": T, "H": cfg.H,
+                   "I_loc": bench.I_loc, "E": cfg.E, "k": cfg.k, "gating_mode": cfg.mode,
+                   "I_shared": cfg.I_shared, "weight_copies": bench.copies,
+                   "parallelism": "single-gpu share"},
+        "roofline": roof,
+        "layer_roofline": {"bound": l_bound, "t_roof_ms": round(t_roof_ms, 4),
+                           "frac": round(l_frac, 4), "b_alg_bytes": work["b_alg"],
+                           "f_alg_flops": work["f_alg"]},
+        "ms_per_step_graph": round(ms_graph, 4),
+        "stage_ms": {k2: round(v, 4) for k2, v in split.items()},
+        "routing": {"rows": work["rows"], "touched_experts": work["touched"],
+                    "imbalance_ratio": round(imb, 3)},
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
