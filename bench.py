@@ -266,7 +266,7 @@ def main():
     work = layer_work(cfg, T, counts, bench.I_loc, bench.elt)
     ms, split = bench.timed_eager(args.steps, args.warmup)
     roof = roofline_entry(cfg, work, split["gemm_gate_up"])
-    roof["kernel"] = "ffn_direct_kernel (gate/up GEMM + SwiGLU)"
+    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (moe_layer stage events 1 -> 2)"
     roof["avg_launch_ms"] = round(split["gemm_gate_up"], 4)
     l_bound, t_roof_ms, l_frac = layer_roof_frac(cfg, work, ms)
     ms_graph = bench.timed_graph(args.steps, args.warmup)

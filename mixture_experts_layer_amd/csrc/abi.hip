@@ -94,7 +94,7 @@ size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w) {
   const int eb = elt_bytes(d->dt);
   const int max_rows = T * (d->k < E_loc ? d->k : E_loc);
   const int n_tt = cdiv(T, TOK_TILE);
-  const int BM = ffn_row_tile(d->dt, mean_rows(T, d->k, d->E));
+  const int BM = ffn_row_tile(d->dt, mean_rows(T, d->k, d->E), d->H, d->I_loc);
   const int max_tiles = max_tiles_for(max_rows, E_loc, BM);
   Carver c(base);
   LayerWs l;
@@ -241,7 +241,7 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e
 
 size_t moe_grouped_ffn_workspace_size(int max_rows, int E_loc, int H, int I_loc, int dt) {
   if (max_rows < 0 || E_loc < 1 || H <= 0 || I_loc <= 0 || !valid_dt(dt)) return 0;
-  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc));
+  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc), H, I_loc);
   const int mt = max_tiles_for(max_rows, E_loc, BM);
   return align_up((size_t)max_rows * I_loc * elt_bytes(dt)) + align_up((size_t)mt * sizeof(int4)) +
          align_up(4);
@@ -265,7 +265,7 @@ int moe_grouped_ffn(const void* x_perm, const void* x, const int32_t* src_token,
   if (max_rows == 0) return MOE_OK;
   const size_t need = moe_grouped_ffn_workspace_size(max_rows, E_loc, H, I_loc, dt);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc));
+  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc), H, I_loc);
   const int mt = max_tiles_for(max_rows, E_loc, BM);
   Carver c(ws);
   void* h = c.take<char>((size_t)max_rows * I_loc * elt_bytes(dt));
@@ -277,6 +277,7 @@ int moe_grouped_ffn(const void* x_perm, const void* x, const int32_t* src_token,
   a.x = x_perm ? x_perm : x;
   a.src_token = x_perm ? nullptr : src_token;
   a.tile_map = tile_map; a.n_tiles = n_tiles; a.M_dense = 0; a.max_tiles = mt;
+  a.mean_rows = cdiv(max_rows, E_loc);
   a.H = H; a.I_loc = I_loc; a.w13 = w13; a.w2 = w2; a.h = h; a.y = y_perm;
   a.dt = dt; a.y_dt = y_dt;
   return hip_status(launch_grouped_ffn(a, BM, s));
@@ -362,7 +363,7 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
   // a6-a7: grouped SwiGLU GEMMs, gather fused into the first
   FfnArgs f{};
   f.x = x; f.src_token = l.src_token; f.tile_map = l.tile_map; f.n_tiles = l.n_tiles;
-  f.M_dense = 0; f.max_tiles = l.max_tiles;
+  f.M_dense = 0; f.max_tiles = l.max_tiles; f.mean_rows = mean_rows(T, d->k, d->E);
   f.H = d->H; f.I_loc = d->I_loc; f.w13 = d->w13; f.w2 = d->w2;
   f.h = l.h; f.y = l.y_perm; f.dt = d->dt; f.y_dt = d->dt;
   MOE_TRY(launch_ffn_gate_up(f, l.BM, s));
@@ -371,10 +372,10 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
   MOE_TRY(mark(3));
   // a8: shared expert over every token
   if (d->I_shared > 0) {
-    const int BMs = ffn_row_tile(d->dt, T);
+    const int BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared);
     FfnArgs g{};
     g.x = x; g.src_token = nullptr; g.tile_map = nullptr; g.n_tiles = nullptr;
-    g.M_dense = T; g.max_tiles = cdiv(T, BMs);
+    g.M_dense = T; g.max_tiles = cdiv(T, BMs); g.mean_rows = T;
     g.H = d->H; g.I_loc = d->I_shared; g.w13 = d->w13_shared; g.w2 = d->w2_shared;
     g.h = l.h_s; g.y = l.y_s; g.dt = d->dt; g.y_dt = d->dt;
     MOE_TRY(launch_grouped_ffn(g, BMs, s));

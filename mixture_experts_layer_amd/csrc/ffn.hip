@@ -60,7 +60,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
   if (a.tile_map) {
     if (tile >= a.n_tiles[0]) return;
     const int4 tm = a.tile_map[tile];
-    e = tm.x; r0 = tm.y; r1 = tm.z;
+    e = tm.x; r0 = tm.y + (tile - tm.w) * BM; r1 = min(r0 + BM, tm.z);
   } else {
     e = 0; r0 = tile * BM; r1 = min(r0 + BM, a.M_dense);
     if (r0 >= a.M_dense) return;
@@ -187,6 +187,233 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// LDS-tiled bf16 MFMA kernel for prefill-sized row counts.
+//
+// Block tile: TM = 128 rows x TN = 256 weight rows, K in chunks of 64,
+// 4 waves in a 2 x 2 grid, each wave 64 rows x 128 weight rows of
+// v_mfma_f32_32x32x16_bf16 (A = weight fragment, B = activation fragment;
+// accumulator lane l holds row m = l % 32 and weight rows
+// 8*q + 4*(l/32) + r, register 4*q + r).
+//
+// Operands reach LDS through global_load_lds_dwordx4: each lane copies 16
+// bytes from any global address (so the token gather of the gate/up GEMM
+// happens inside the load) to LDS slot base + 16 * lane.  A wave
+// instruction fills 8 rows of 128 bytes.  Rows are XOR-swizzled in 16-byte
+// chunks (chunk c of row r sits at c ^ ((r >> 1) & 7)) so the 32 lanes
+// reading one column chunk hit distinct banks.  Three stages: while stage s
+// is multiplied, stages s+1 and s+2 are in flight.
+//
+// SWIGLU: the 256 weight rows are 128 gate rows [n0, n0+128) followed by
+// the matching 128 up rows; each wave holds gate and up accumulators for
+// the same (row, column) and writes SiLU(gate) * up.
+//
+// Block order: blocks of one expert are numbered M-tile-fastest inside
+// groups of G N-tiles, so the M-tiles sharing a weight tile run together;
+// consecutive numbers are mapped to one XCD (workgroups are dealt to the 8
+// XCDs round-robin) so that they share that XCD's L2.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+struct TileArgs {
+  const bf16_t* X;
+  const int32_t* src_token;
+  const int4* tile_map;     // {expert, first row, end row, first tile of expert}
+  const int32_t* n_tiles;
+  int M_dense;
+  const bf16_t* W;
+  long long w_stride;
+  int K;
+  int N_out;                // output columns: I_loc (SWIGLU) or H
+  int up_off;
+  void* Y;
+  int group;                // N-tiles per group
+};
+
+constexpr int TL_M = 128, TL_N = 256, TL_K = 64, TL_STAGES = 3;
+constexpr int TL_XBYTES = TL_M * TL_K * 2;                 // 16 KB
+constexpr int TL_WBYTES = TL_N * TL_K * 2;                 // 32 KB
+constexpr int TL_STAGE_BYTES = TL_XBYTES + TL_WBYTES;      // 48 KB
+
+__device__ __forceinline__ int tl_swz(int r) { return (r >> 1) & 7; }
+
+template <bool SWIGLU, bool OUT_BF16>
+__global__ __launch_bounds__(256) void ffn_tile_kernel(TileArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n_cols_tile = SWIGLU ? TL_N / 2 : TL_N;
+  const int NTn = a.N_out / n_cols_tile;
+
+  // ---- which (expert, M-tile, N-tile) this block computes
+  int e = 0, off = 0, end = a.M_dense, ms = 0, n_active;
+  if (a.tile_map) n_active = a.n_tiles[0] * NTn;
+  else n_active = ((a.M_dense + TL_M - 1) / TL_M) * NTn;
+  int b = blockIdx.x;
+  if (b >= n_active) return;
+  {
+    const int per = n_active >> 3;                 // XCD-contiguous numbering
+    if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  }
+  const int mi = b / NTn;
+  if (a.tile_map) {
+    const int4 tm = a.tile_map[mi];
+    e = tm.x; off = tm.y; end = tm.z; ms = tm.w;
+  }
+  const int te = (end - off + TL_M - 1) / TL_M;
+  const int li = b - ms * NTn;
+  const int G = a.group;
+  const int g = li / (te * G);
+  const int rem = li - g * te * G;
+  const int Gc = min(G, NTn - g * G);
+  const int m_t = rem / Gc;
+  const int n_t = g * G + (rem - m_t * Gc);
+  const int r0 = off + m_t * TL_M;
+  const int r1 = min(r0 + TL_M, end);
+  const int n0 = n_t * n_cols_tile;
+
+  // ---- per-lane global source pointers for the 12 load instructions
+  const int prow = lane >> 3;        // row inside an 8-row group
+  const int pchunk = lane & 7;       // LDS chunk slot written by this lane
+  const bf16_t* xsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rt = (wid + 4 * j) * 8 + prow;          // tile row 0..127
+    int row = r0 + rt;
+    if (row >= r1) row = r0;                          // padding rows read a valid row
+    const int src = a.src_token ? a.src_token[row] : row;
+    const int c = pchunk ^ tl_swz(rt);
+    xsrc[j] = a.X + (size_t)src * a.K + c * 8;
+  }
+  const bf16_t* We = a.W + (size_t)e * a.w_stride;
+  const bf16_t* wsrc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rt = (wid + 4 * j) * 8 + prow;          // tile row 0..255
+    int wrow;
+    if (SWIGLU) wrow = rt < 128 ? n0 + rt : a.up_off + n0 + (rt - 128);
+    else wrow = n0 + rt;
+    const int c = pchunk ^ tl_swz(rt);
+    wsrc[j] = We + (size_t)wrow * a.K + c * 8;
+  }
+
+  auto issue = [&](int ks, int buf) {
+    unsigned char* sx = smem + buf * TL_STAGE_BYTES;
+    unsigned char* sw = sx + TL_XBYTES;
+    const int ko = ks * TL_K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[j] + ko),
+                                       (lds_void_t*)(sx + (wid + 4 * j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[j] + ko),
+                                       (lds_void_t*)(sw + (wid + 4 * j) * 1024), 16, 0, 0);
+  };
+
+  const int wm = wid >> 1, wn = wid & 1;
+  const int lrow = lane & 31;
+  const int lsw = tl_swz(lrow);
+  const int khalf = lane >> 5;
+  // weight-row bases of the wave's 4 N subtiles inside the 256-row tile
+  int nbase[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    if (SWIGLU) nbase[ni] = (ni < 2 ? 0 : 128) + wn * 64 + (ni & 1) * 32;
+    else nbase[ni] = wn * 128 + ni * 32;
+  }
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int nk = a.K / TL_K;
+  auto load_frags = [&](const unsigned char* sx, const unsigned char* sw, int kk, bf16x8_t* xf,
+                        bf16x8_t* wf) {
+    const int cpos = ((kk * 2 + khalf) ^ lsw) * 16;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+      xf[mi] = *reinterpret_cast<const bf16x8_t*>(sx + (wm * 64 + mi * 32 + lrow) * 128 + cpos);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      wf[ni] = *reinterpret_cast<const bf16x8_t*>(sw + (nbase[ni] + lrow) * 128 + cpos);
+  };
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int ks = 0; ks < nk; ++ks) {
+    // Stage ks has landed for this wave once at most the 12 loads of stage
+    // ks+1 are outstanding; the barrier makes that true for every wave.  The
+    // fragments of the previous stage were all consumed by its MFMAs, so no
+    // LDS read of the buffer refilled below is still in flight.  (A
+    // __syncthreads() here would also drain stage ks+1 from the queue.)
+    if (ks + 1 < nk) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (ks + 2 < nk) issue(ks + 2, (ks + 2) % TL_STAGES);
+    const unsigned char* sx = smem + (ks % TL_STAGES) * TL_STAGE_BYTES;
+    const unsigned char* sw = sx + TL_XBYTES;
+    bf16x8_t xf[2][2], wf[2][4];
+    load_frags(sx, sw, 0, xf[0], wf[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < 4) load_frags(sx, sw, kk + 1, xf[cur ^ 1], wf[cur ^ 1]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][ni], xf[cur][mi],
+                                                                acc[mi][ni], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int row = r0 + wm * 64 + mi * 32 + lrow;
+    if (row >= r1) continue;
+    if (SWIGLU) {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int col0 = n0 + wn * 64 + ni * 32 + 4 * khalf;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = acc[mi][ni][4 * q + r], uv = acc[mi][ni + 2][4 * q + r];
+            h[r] = silu(gv) * uv;
+          }
+          uint2 o = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.Y) + (size_t)row * a.N_out +
+                                    col0 + 8 * q) = o;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int col0 = n0 + wn * 128 + ni * 32 + 4 * khalf;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const size_t yi = (size_t)row * a.N_out + col0 + 8 * q;
+          if (OUT_BF16) {
+            uint2 o = make_uint2(pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]),
+                                 pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]));
+            *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.Y) + yi) = o;
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + yi) =
+                make_float4(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                            acc[mi][ni][4 * q + 3]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // float32 layer: one thread per output element of a 16 x 16 tile, plain FMA
 // dot products over K (the fp32 configuration is small).
 // ---------------------------------------------------------------------------
@@ -211,7 +438,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(F32Args a) {
   if (a.tile_map) {
     if (tile >= a.n_tiles[0]) return;
     const int4 tm = a.tile_map[tile];
-    e = tm.x; r0 = tm.y; r1 = tm.z;
+    e = tm.x; r0 = tm.y + (tile - tm.w) * 16; r1 = min(r0 + 16, tm.z);
   } else {
     e = 0; r0 = tile * 16; r1 = min(r0 + 16, a.M_dense);
     if (r0 >= a.M_dense) return;
@@ -240,11 +467,42 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(F32Args a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-int ffn_row_tile(int dt, int mean_rows) {
+bool ffn_tile_ok(int H, int I_loc) {
+  return H % TL_K == 0 && H % TL_N == 0 && I_loc % TL_K == 0 && I_loc % (TL_N / 2) == 0;
+}
+
+int ffn_row_tile(int dt, int mean_rows, int H, int I_loc) {
   if (dt == 0) return 16;
+  if (mean_rows >= 64 && ffn_tile_ok(H, I_loc)) return TL_M;
   if (mean_rows <= 16) return 16;
   if (mean_rows <= 32) return 32;
   return 64;
+}
+
+template <bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_tile(const TileArgs& a, int max_tiles, hipStream_t st) {
+  static bool attr_set = false;
+  const int lds = TL_STAGES * TL_STAGE_BYTES;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&ffn_tile_kernel<SWIGLU, OUT_BF16>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  const int ntn = a.N_out / (SWIGLU ? TL_N / 2 : TL_N);
+  ffn_tile_kernel<SWIGLU, OUT_BF16><<<max_tiles * ntn, 256, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+// N-tiles per group: enough M-tiles x N-tiles of one expert to fill the 32
+// CUs of an XCD while they share that expert's weight tiles.
+static int tile_group(int mean_rows, int ntn) {
+  const int te = (mean_rows + TL_M - 1) / TL_M;
+  int g = 32 / (te > 0 ? te : 1);
+  if (g < 1) g = 1;
+  if (g > ntn) g = ntn;
+  return g;
 }
 
 static int pick_nw(int steps, int max_nw) {
@@ -290,6 +548,12 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {
     ffn_f32_kernel<true><<<a.max_tiles * (a.I_loc / 16), 256, 0, st>>>(g1);
     return hipGetLastError();
   }
+  if (BM == TL_M) {
+    TileArgs t{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
+               (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h,
+               tile_group(a.mean_rows, a.I_loc / (TL_N / 2))};
+    return launch_tile<true, true>(t, a.max_tiles, st);
+  }
   DirectArgs g1{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
                 (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h};
   return launch_direct<true, true>(g1, BM, a.max_tiles, st);
@@ -302,6 +566,13 @@ hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st) {
                (const float*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, (float*)a.y};
     ffn_f32_kernel<false><<<a.max_tiles * (a.H / 16), 256, 0, st>>>(g2);
     return hipGetLastError();
+  }
+  if (BM == TL_M) {
+    TileArgs t{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
+               (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y,
+               tile_group(a.mean_rows, a.H / TL_N)};
+    if (a.y_dt == 0) return launch_tile<false, false>(t, a.max_tiles, st);
+    return launch_tile<false, true>(t, a.max_tiles, st);
   }
   DirectArgs g2{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
                 (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y};

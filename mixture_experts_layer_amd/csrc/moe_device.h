@@ -83,8 +83,9 @@ __device__ inline int block_exclusive_scan(int* data, int n, int* tmp) {
 
 // ---------------------------------------------------------------------------
 // GEMM tile map: for every local expert, ceil(count / BM) row tiles of at most
-// BM rows.  Entry = {expert, row_begin, row_end, 0}; n_tiles[0] = number of
-// entries.  cnt[] holds counts and off[] exclusive offsets (both in LDS).
+// BM rows.  Every entry of expert e is {e, first row of e, end row of e,
+// index of e's first entry}; tile q of e covers rows [first + q*BM,
+// min(first + (q+1)*BM, end)).  n_tiles[0] = number of entries.  cnt[] holds counts and off[] exclusive offsets (both in LDS).
 // An expert whose rows fall outside [0, max_rows) gets no tiles, and at most
 // max_tiles entries are written, so a GEMM driven by the map never indexes
 // outside its buffers even if the offsets were inconsistent.
@@ -104,12 +105,11 @@ __device__ inline void block_build_tile_map(const int* cnt, const int* off, int 
   const int total = block_exclusive_scan(scratch, E_loc, tmp);
   for (int e = threadIdx.x; e < E_loc; e += blockDim.x) {
     const int nt = tiles_of(cnt[e], off[e], BM, max_rows);
-    const int r_end = off[e] + cnt[e];
+    const int4 entry = make_int4(e, off[e], off[e] + cnt[e], scratch[e]);
     for (int q = 0; q < nt; ++q) {
       const int slot = scratch[e] + q;
       if (slot >= max_tiles) break;
-      const int r0 = off[e] + q * BM;
-      tile_map[slot] = make_int4(e, r0, min(r0 + BM, r_end), 0);
+      tile_map[slot] = entry;
     }
   }
   if (threadIdx.x == 0) n_tiles[0] = min(total, max_tiles);

@@ -60,6 +60,7 @@ struct FfnArgs {
   const int32_t* n_tiles;
   int M_dense;              // rows when tile_map is null
   int max_tiles;
+  int mean_rows;            // expected rows per expert (block-order heuristics)
   int H, I_loc;
   const void* w13;          // [E_loc][2*I_loc][H]
   const void* w2;           // [E_loc][H][I_loc]
@@ -67,7 +68,7 @@ struct FfnArgs {
   void* y;                  // [rows][H], dtype y_dt
   int dt, y_dt;
 };
-int ffn_row_tile(int dt, int mean_rows);
+int ffn_row_tile(int dt, int mean_rows, int H, int I_loc);
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st);
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st);

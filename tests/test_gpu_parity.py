@@ -173,7 +173,7 @@ def test_permute_empty_batch():
 # ---------------------------------------------------------------- grouped FFN + combine
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("T,E,k", [(3, 8, 2), (40, 16, 4), (300, 16, 2), (700, 8, 2)])
+@pytest.mark.parametrize("T,E,k", [(3, 8, 2), (40, 16, 4), (300, 16, 2), (700, 8, 2), (1500, 4, 2)])
 def test_grouped_ffn_and_combine(dt, T, E, k):
     H, I = 256, 128
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -244,6 +244,30 @@ def test_layer_small(name, H, I, E, T):
         L.w2_shared = (torch.randn((H, I), device=DEV) * s).to(torch.bfloat16)
     gl = GpuLayer(L)
     check_layer(gl, gl.run(T), T)
+
+
+# shapes that take the LDS-tiled prefill kernel (>= 64 rows per expert,
+# I_loc a multiple of 128, H a multiple of 256), with ragged expert tails
+TILE = [
+    ("mixtral_8x7b", 256, 256, 8, 300),
+    ("mixtral_8x7b", 512, 384, 8, 1000),
+    ("qwen3_ep_all128", 256, 128, 16, 1111),
+    ("deepseek_v3", 512, 256, 32, 700),
+]
+
+
+@pytest.mark.parametrize("name,H,I,E,T", TILE)
+def test_layer_tile_path(name, H, I, E, T):
+    cfg = W.CONFIGS[name]
+    L = W.make_layer(cfg, device=DEV, seed=5, T_max=T, H=H, I=I, E=E)
+    if cfg.I_shared:
+        s = 1.0 / H ** 0.5
+        L.w13_shared = (torch.randn((2 * I, H), device=DEV) * s).to(torch.bfloat16)
+        L.w2_shared = (torch.randn((H, I), device=DEV) * s).to(torch.bfloat16)
+    gl = GpuLayer(L)
+    check_layer(gl, gl.run(T), T)
+    gl2 = GpuLayer(L, e_begin=E // 4, e_end=E // 2)
+    check_layer(gl2, gl2.run(T), T)
 
 
 @pytest.mark.parametrize("T", [1, 9, 64, 200])
