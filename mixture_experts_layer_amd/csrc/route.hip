@@ -76,75 +76,190 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const Tin* __restrict_
 
 // ---------------------------------------------------------------------------
 // Router logits on bf16 MFMA: one block (4 waves) per 64 tokens and all E
-// experts (E <= 256).  W_r is staged through LDS in K chunks of 64 and shared
-// by the 4 waves; each wave owns 16 tokens.  v_mfma_f32_16x16x32_bf16 with
-// A = x fragment (row = token), B = W_r fragment (column = expert); the
-// accumulator lane l holds token 4*(l/16)+i, expert l%16.
+// experts (E = 32 * EW, E <= 256).  Token rows and W_r rows reach LDS in K
+// chunks of 64 through global_load_lds_dwordx4, three chunks in flight, rows
+// XOR-swizzled in 16-byte chunks against bank conflicts.  Each wave owns 16
+// tokens: v_mfma_f32_16x16x32_bf16 with A = W_r fragment (row = expert),
+// B = token fragment; accumulator lane l holds token l % 16 and experts
+// 4*(l/16) + i, stored as one 16-byte vector.
 // ---------------------------------------------------------------------------
-constexpr int RT_KC = 64;          // K chunk
-constexpr int RT_LD = RT_KC + 8;   // LDS row pitch (bf16), padded against bank conflicts
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
 
+constexpr int RT_TOK = 64, RT_K = 64, RT_STAGES = 3;
+
+__device__ __forceinline__ int rt_swz(int r) { return (r >> 1) & 7; }
+
+template <int EW>
 __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wr, int T,
-                                                          int H, int E,
-                                                          const float* __restrict__ bias,
+                                                          int H, const float* __restrict__ bias,
                                                           float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) bf16_t sw[256 * RT_LD];
+  constexpr int E = 32 * EW;
+  constexpr int XB = RT_TOK * 128;          // token chunk bytes
+  constexpr int WB = E * 128;               // W_r chunk bytes
+  constexpr int SB = XB + WB;
+  constexpr int NL = 2 + EW;                // loads per wave per stage
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int Ep = (E + 15) & ~15;
-  const int nb = Ep >> 4;
-  const int t0 = blockIdx.x * 64 + wid * 16;
-  const int my_tok = t0 + (lane & 15);
-  const bool tok_ok = my_tok < T;
-  const int kg = (lane >> 4) * 8;
+  const int t0 = blockIdx.x * RT_TOK;
+  const int prow = lane >> 3, pch = lane & 7;
 
-  f32x4_t acc[16];
+  const bf16_t* xsrc[2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 2; ++j) {
+    const int rt = (wid + 4 * j) * 8 + prow;
+    const int t = min(t0 + rt, T - 1);
+    xsrc[j] = x + (size_t)t * H + (pch ^ rt_swz(rt)) * 8;
+  }
+  const bf16_t* wsrc[EW];
+#pragma unroll
+  for (int j = 0; j < EW; ++j) {
+    const int rt = (wid + 4 * j) * 8 + prow;
+    wsrc[j] = wr + (size_t)rt * H + (pch ^ rt_swz(rt)) * 8;
+  }
+  auto issue = [&](int ks, int buf) {
+    unsigned char* sx = smem + buf * SB;
+    unsigned char* sw = sx + XB;
+    const int ko = ks * RT_K;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[j] + ko),
+                                       (lds_void_t*)(sx + (wid + 4 * j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < EW; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[j] + ko),
+                                       (lds_void_t*)(sw + (wid + 4 * j) * 1024), 16, 0, 0);
+  };
 
-  for (int k0 = 0; k0 < H; k0 += RT_KC) {
-    __syncthreads();
-    // stage W_r[0:Ep, k0:k0+64): Ep rows x 8 chunks of 16 bytes
-    for (int c = threadIdx.x; c < Ep * 8; c += 256) {
-      const int r = c >> 3, q = (c & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < E) v = *reinterpret_cast<const uint4*>(wr + (size_t)r * H + k0 + q);
-      *reinterpret_cast<uint4*>(sw + r * RT_LD + q) = v;
-    }
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-    if (tok_ok) {
-      const bf16_t* xp = x + (size_t)my_tok * H + k0 + kg;
-      a0 = *reinterpret_cast<const uint4*>(xp);
-      a1 = *reinterpret_cast<const uint4*>(xp + 32);
-    }
-    __syncthreads();
+  f32x4_t acc[E / 16];
 #pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      if (n < nb) {
-        const bf16_t* bp = sw + (n * 16 + (lane & 15)) * RT_LD + kg;
-        const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(bp + 32);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(b0), acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(b1), acc[n], 0, 0, 0);
+  for (int i = 0; i < E / 16; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int lrow = lane & 15, kq = lane >> 4;
+  const int nk = H / RT_K;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int ks = 0; ks < nk; ++ks) {
+    // stage ks landed once at most the NL loads of stage ks+1 are pending;
+    // the previous stage's fragments were consumed by its MFMAs
+    if (ks + 1 < nk) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(NL) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (ks + 2 < nk) issue(ks + 2, (ks + 2) % RT_STAGES);
+    const unsigned char* sx = smem + (ks % RT_STAGES) * SB;
+    const unsigned char* sw = sx + XB;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + kq;
+      const int xr = wid * 16 + lrow;
+      const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(sx + xr * 128 + ((c ^ rt_swz(xr)) * 16));
+#pragma unroll
+      for (int nb = 0; nb < E / 16; ++nb) {
+        const int wrow = nb * 16 + lrow;
+        const bf16x8_t wf =
+            *reinterpret_cast<const bf16x8_t*>(sw + wrow * 128 + ((c ^ rt_swz(wrow)) * 16));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf, acc[nb], 0, 0, 0);
       }
     }
   }
+  const int t = t0 + wid * 16 + lrow;
+  if (t < T) {
 #pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    if (n < nb) {
-      const int e = n * 16 + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = blockIdx.x * 64 + wid * 16 + (lane >> 4) * 4 + i;
-        if (t < T && e < E) logits[(size_t)t * E + e] = acc[n][i] + (bias ? bias[e] : 0.f);
+    for (int nb = 0; nb < E / 16; ++nb) {
+      const int e = nb * 16 + 4 * kq;
+      float4 v = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+      if (bias) {
+        v.x += bias[e]; v.y += bias[e + 1]; v.z += bias[e + 2]; v.w += bias[e + 3];
       }
+      *reinterpret_cast<float4*>(logits + (size_t)t * E + e) = v;
     }
   }
 }
 
+template <int EW>
+static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, int H,
+                                     const float* bias, float* logits, hipStream_t st) {
+  static bool attr_set = false;
+  const int lds = RT_STAGES * (RT_TOK * 128 + 32 * EW * 128);
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_mfma_kernel<EW>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  router_mfma_kernel<EW><<<(T + RT_TOK - 1) / RT_TOK, 256, lds, st>>>(x, wr, T, H, bias, logits);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
-// Gating + routing metadata for one tile of TOK_TILE tokens (4 waves, one
-// token per wave at a time).
+// Wave-wide reductions: DPP inside each 16-lane row (pairs at distance 1, 2,
+// then the half-row and row mirrors), then the four row results via
+// readlane.  Every lane ends with the result; the combination order is fixed,
+// so float sums are the same on every run.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+// (key, id) arg-max: larger key wins, equal keys go to the smaller id.
+__device__ __forceinline__ bool better(float ok, int oi, float k, int i) {
+  return ok > k || (ok == k && oi < i);
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& k, int& i) {
+  const float ok = dpp_f<CTRL>(k);
+  const int oi = dpp_i<CTRL>(i);
+  if (better(ok, oi, k, i)) { k = ok; i = oi; }
+}
+__device__ __forceinline__ void wave_argmax(float& k, int& i) {
+  argmax_step<DPP_XOR1>(k, i);
+  argmax_step<DPP_XOR2>(k, i);
+  argmax_step<DPP_HALF_MIRROR>(k, i);
+  argmax_step<DPP_MIRROR>(k, i);
+  float bk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    const float ok = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k), r));
+    const int oi = __builtin_amdgcn_readlane(i, r);
+    if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+  }
+  k = bk;
+  i = bi;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<DPP_XOR1>(v);
+  v += dpp_f<DPP_XOR2>(v);
+  v += dpp_f<DPP_HALF_MIRROR>(v);
+  v += dpp_f<DPP_MIRROR>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// ---------------------------------------------------------------------------
+// Gating + routing metadata for one tile of TOK_TILE tokens (NW waves; a
+// wave takes tokens wid, wid + NW, ...; the next token's logits are loaded
+// while the current one is processed).
 //
 // Selection: k rounds of a wave-wide arg-max over (key descending, id
 // ascending); the key is the logit, or logit + sel_bias in float32 for the
@@ -162,61 +277,59 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 // scan and scatter kernels.
 // do_gate == 0: ids come from ids_in (permutation only, no gating).
 // ---------------------------------------------------------------------------
-template <int EPL>
-__global__ __launch_bounds__(256) void gate_tile_kernel(GateTileArgs a) {
-  __shared__ int s_ids[TOK_TILE * KMAX];
+template <int EPL, int NW>
+__global__ __launch_bounds__(NW * 64) void gate_tile_kernel(GateTileArgs a) {
+  __shared__ __attribute__((aligned(16))) int s_ids[TOK_TILE * KMAX];
   __shared__ int s_rank[TOK_TILE * KMAX];
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1025];
   __shared__ int s_scr[1024];
-  __shared__ int s_tmp[257];
+  __shared__ int s_tmp[NW * 64 + 1];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int t0 = tile * TOK_TILE;
   const int ntok = max(0, min(TOK_TILE, a.T - t0));
   const int k = a.k, E = a.E;
+  const bool sig = a.mode == 3;
 
   if (a.do_gate) {
-    for (int tt = wid; tt < ntok; tt += 4) {
-      const int t = t0 + tt;
-      float key[EPL], s[EPL];
-      bool avail[EPL];
+    float s_next[EPL];
+    auto load = [&](int tt, float* s) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        avail[i] = e < E;
-        s[i] = avail[i] ? a.logits[(size_t)t * E + e] : 0.f;
-        key[i] = s[i];
-        if (a.mode == 3 && a.sel_bias && avail[i]) key[i] = s[i] + a.sel_bias[e];
+        s[i] = (tt < ntok && e < E) ? a.logits[(size_t)(t0 + tt) * E + e] : 0.f;
       }
+    };
+    load(wid, s_next);
+    for (int tt = wid; tt < ntok; tt += NW) {
+      const int t = t0 + tt;
+      float s[EPL], key[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) s[i] = s_next[i];
+      load(tt + NW, s_next);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? s[i] : -INFINITY;
+        if (sig && a.sel_bias && e < E) key[i] = s[i] + a.sel_bias[e];
+      }
+      bool avail[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) avail[i] = lane + 64 * i < E;
       int sel_id = -1;       // lane j < k keeps the j-th choice
       float sel_s = 0.f;
       for (int r = 0; r < k; ++r) {
-        // local best among available entries
-        float bk = 0.f;
+        float bk = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
           const int e = lane + 64 * i;
-          if (avail[i] && (bi == 0x7fffffff || key[i] > bk)) {
-            bk = key[i];
-            bi = e;
-          }
+          if (avail[i] && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
         }
-        // wave arg-max: larger key wins, equal keys -> smaller id
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float ok = __shfl_xor(bk, o);
-          const int oi = __shfl_xor(bi, o);
-          const bool take = (oi != 0x7fffffff) &&
-                            (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi));
-          if (take) {
-            bk = ok;
-            bi = oi;
-          }
-        }
-        // owner lane retires the winner and reports its logit
+        wave_argmax(bk, bi);
+        // the owner lane retires the winner; every lane learns its logit
         float win_s = 0.f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
@@ -224,8 +337,8 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(GateTileArgs a) {
             avail[i] = false;
             win_s = s[i];
           }
-        const int owner = bi & 63;
-        win_s = __shfl(win_s, owner);
+        win_s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, win_s),
+                                                                    bi & 63));
         if (lane == r) {
           sel_id = bi;
           sel_s = win_s;
@@ -233,39 +346,25 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(GateTileArgs a) {
       }
       // gate weights of the k choices (lanes 0..k-1)
       const bool mine = lane < k;
-      float wv = 0.f;
+      float wv;
       if (a.mode == 0) {
-        float m = mine ? sel_s : -INFINITY;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-        float ev = mine ? expf(sel_s - m) : 0.f;
-        float z = ev;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
-        wv = ev / z;
+        const float m = wave_max(mine ? sel_s : -INFINITY);
+        const float ev = mine ? expf(sel_s - m) : 0.f;
+        wv = ev / wave_sum(ev);
       } else if (a.mode == 1 || a.mode == 2) {
-        // softmax over all E: the maximum logit is the first choice
-        const float m = __shfl(sel_s, 0);
+        // softmax over all E; the largest logit is the first choice
+        const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sel_s), 0));
         float z = 0.f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
           if (lane + 64 * i < E) z += expf(s[i] - m);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+        z = wave_sum(z);
         float p = mine ? expf(sel_s - m) / z : 0.f;
-        if (a.mode == 2) {
-          float ps = p;
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) ps += __shfl_xor(ps, o);
-          p = p / ps;
-        }
+        if (a.mode == 2) p = p / wave_sum(p);
         wv = p;
       } else {
-        float sg = mine ? 1.0f / (1.0f + expf(-sel_s)) : 0.f;
-        float ss = sg;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        wv = sg / ss;
+        const float sg = mine ? 1.0f / (1.0f + expf(-sel_s)) : 0.f;
+        wv = sg / wave_sum(sg);
       }
       if (mine) {
         a.ids_out[(size_t)t * k + lane] = sel_id;
@@ -274,27 +373,36 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(GateTileArgs a) {
       }
     }
   } else {
-    for (int i = threadIdx.x; i < ntok * k; i += 256) s_ids[i] = a.ids_in[(size_t)t0 * k + i];
+    for (int i = threadIdx.x; i < ntok * k; i += NW * 64) s_ids[i] = a.ids_in[(size_t)t0 * k + i];
   }
   if (!a.do_permute) return;
+  const int npair = ntok * k;
+  // pad the id list to a multiple of 16 with an id no expert has
+  for (int p = npair + threadIdx.x; p < ((npair + 15) & ~15); p += NW * 64) s_ids[p] = -1;
   __syncthreads();
 
-  // atomic-free histogram and in-tile ranks
+  // atomic-free histogram and in-tile ranks, 16 ids per LDS pass
   const int E_loc = a.e_end - a.e_begin;
-  const int npair = ntok * k;
-  for (int el = threadIdx.x; el < E_loc; el += 256) {
+  for (int el = threadIdx.x; el < E_loc; el += NW * 64) {
     const int e = a.e_begin + el;
     int c = 0;
-    for (int p = 0; p < npair; ++p)
-      if (s_ids[p] == e) s_rank[p] = c++;
+    for (int p = 0; p < npair; p += 16) {
+      const int4* q = reinterpret_cast<const int4*>(s_ids + p);
+      const int4 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
+      const int ids16[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                             v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (ids16[j] == e) s_rank[p + j] = c++;
+    }
     s_cnt[el] = c;
   }
   __syncthreads();
 
   if (!a.single) {
-    for (int el = threadIdx.x; el < E_loc; el += 256)
+    for (int el = threadIdx.x; el < E_loc; el += NW * 64)
       a.tile_counts[(size_t)tile * E_loc + el] = s_cnt[el];
-    for (int p = threadIdx.x; p < npair; p += 256) {
+    for (int p = threadIdx.x; p < npair; p += NW * 64) {
       const int e = s_ids[p];
       const bool local = e >= a.e_begin && e < a.e_end;
       a.rank_out[(size_t)t0 * k + p] = local ? s_rank[p] : -1;
@@ -303,14 +411,14 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(GateTileArgs a) {
   }
 
   // single tile: finish the permutation here
-  for (int el = threadIdx.x; el < E_loc; el += 256) s_off[el] = s_cnt[el];
+  for (int el = threadIdx.x; el < E_loc; el += NW * 64) s_off[el] = s_cnt[el];
   __syncthreads();
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
   if (threadIdx.x == 0) s_off[E_loc] = total;
   __syncthreads();
-  for (int el = threadIdx.x; el < E_loc; el += 256) a.counts[el] = s_cnt[el];
-  for (int el = threadIdx.x; el <= E_loc; el += 256) a.offsets[el] = s_off[el];
-  for (int p = threadIdx.x; p < npair; p += 256) {
+  for (int el = threadIdx.x; el < E_loc; el += NW * 64) a.counts[el] = s_cnt[el];
+  for (int el = threadIdx.x; el <= E_loc; el += NW * 64) a.offsets[el] = s_off[el];
+  for (int p = threadIdx.x; p < npair; p += NW * 64) {
     const int e = s_ids[p];
     int row = -1;
     if (e >= a.e_begin && e < a.e_end) {
@@ -330,29 +438,43 @@ __global__ __launch_bounds__(256) void gate_tile_kernel(GateTileArgs a) {
 hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,
                                 const float* bias, float* logits, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (dt == 0) {
+  const bool mfma_shape = dt == 1 && T > 32 && H % RT_K == 0 &&
+                          (E == 32 || E == 64 || E == 128 || E == 256);
+  if (!mfma_shape) {
     dim3 grid(E, (T + 7) / 8);
-    router_gemv_kernel<float, 8><<<grid, 256, 0, st>>>((const float*)x, (const float*)wr, T, H,
-                                                       E, bias, logits);
-  } else if (T <= 32 || E > 256 || H % RT_KC) {
-    dim3 grid(E, (T + 7) / 8);
-    router_gemv_kernel<bf16_t, 8><<<grid, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)wr, T,
-                                                        H, E, bias, logits);
-  } else {
-    router_mfma_kernel<<<(T + 63) / 64, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)wr, T, H, E,
-                                                      bias, logits);
+    if (dt == 0)
+      router_gemv_kernel<float, 8><<<grid, 256, 0, st>>>((const float*)x, (const float*)wr, T, H,
+                                                         E, bias, logits);
+    else
+      router_gemv_kernel<bf16_t, 8><<<grid, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)wr, T,
+                                                          H, E, bias, logits);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  const bf16_t* xb = (const bf16_t*)x;
+  const bf16_t* wb = (const bf16_t*)wr;
+  switch (E) {
+    case 32: return launch_router_mfma<1>(xb, wb, T, H, bias, logits, st);
+    case 64: return launch_router_mfma<2>(xb, wb, T, H, bias, logits, st);
+    case 128: return launch_router_mfma<4>(xb, wb, T, H, bias, logits, st);
+    default: return launch_router_mfma<8>(xb, wb, T, H, bias, logits, st);
+  }
+}
+
+template <int NW>
+static void launch_gate_nw(const GateTileArgs& a, int grid, hipStream_t st) {
+  const int epl = (a.E + 63) / 64;
+  if (epl <= 1) gate_tile_kernel<1, NW><<<grid, NW * 64, 0, st>>>(a);
+  else if (epl <= 2) gate_tile_kernel<2, NW><<<grid, NW * 64, 0, st>>>(a);
+  else if (epl <= 4) gate_tile_kernel<4, NW><<<grid, NW * 64, 0, st>>>(a);
+  else if (epl <= 8) gate_tile_kernel<8, NW><<<grid, NW * 64, 0, st>>>(a);
+  else gate_tile_kernel<16, NW><<<grid, NW * 64, 0, st>>>(a);
 }
 
 hipError_t launch_gate_tiles(const GateTileArgs& a, int n_tiles_tok, hipStream_t st) {
-  const int epl = (a.E + 63) / 64;
   const int grid = n_tiles_tok > 0 ? n_tiles_tok : 1;
-  if (epl <= 1) gate_tile_kernel<1><<<grid, 256, 0, st>>>(a);
-  else if (epl <= 2) gate_tile_kernel<2><<<grid, 256, 0, st>>>(a);
-  else if (epl <= 4) gate_tile_kernel<4><<<grid, 256, 0, st>>>(a);
-  else if (epl <= 8) gate_tile_kernel<8><<<grid, 256, 0, st>>>(a);
-  else gate_tile_kernel<16><<<grid, 256, 0, st>>>(a);
+  // one tile (decode-sized batch): 16 waves share its 64 tokens
+  if (grid == 1) launch_gate_nw<16>(a, grid, st);
+  else launch_gate_nw<4>(a, grid, st);
   return hipGetLastError();
 }
 
