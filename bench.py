@@ -55,7 +55,10 @@ def parse():
     ap.add_argument("--sweep-workloads", default="qwen3_ep_all128,qwen3_tp8_rank0",
                     help="workloads whose token counts are swept (comma list)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens in the CPU oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the CPU oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
+                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -247,6 +250,47 @@ def cpu_baseline(bench, n_sample):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, from the committed counter summary
+# ---------------------------------------------------------------------------
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "qwen3_ep_all128_T8192_gemm_gate_up_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "mixture_experts_layer_amd", "csrc", "ffn.hip")
+
+
+def kernel_source_sha256():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic(workload, T):
+    """Bytes per launch of the gate/up GEMM measured with FETCH_SIZE and
+    WRITE_SIZE (scaled by the copy-kernel calibration), if the summary was
+    taken on this workload and on the kernel source as it is now."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            line = next(l for l in f if l.startswith("traffic_json: "))
+        rec = json.loads(line[len("traffic_json: "):])
+    except (OSError, StopIteration, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("T") != T:
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe():
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe": "torch.neg float32", "read_bytes": 1 << 30,
+                      "write_bytes": 1 << 30, "dispatches": 3}), flush=True)
+
 
 def main():
     args = parse()
@@ -258,6 +302,9 @@ def main():
     import torch
     import workloads as W
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe()
+        return
     cfg = W.CONFIGS[args.workload]
     T = args.T or cfg.T_max
 
@@ -267,6 +314,8 @@ def main():
     ms, split = bench.timed_eager(args.steps, args.warmup)
     roof = roofline_entry(cfg, work, split["gemm_gate_up"])
     roof["kernel"] = "grouped gate/up GEMM + SwiGLU (moe_layer stage events 1 -> 2)"
+    roof["traffic"] = committed_traffic(WORKLOAD_NAMES[args.workload], T)
+    roof["algorithmic_bytes"] = work["g1_bytes"]
     roof["avg_launch_ms"] = round(split["gemm_gate_up"], 4)
     l_bound, t_roof_ms, l_frac = layer_roof_frac(cfg, work, ms)
     ms_graph = bench.timed_graph(args.steps, args.warmup)

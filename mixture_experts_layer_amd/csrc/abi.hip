@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_kernels.h"
 
 using namespace moe;

@@ -189,23 +189,23 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
 // ---------------------------------------------------------------------------
 // LDS-tiled bf16 MFMA kernel for prefill-sized row counts.
 //
-// Block tile: TM = 128 rows x TN = 256 weight rows, K in chunks of 64,
-// 4 waves in a 2 x 2 grid, each wave 64 rows x 128 weight rows of
-// v_mfma_f32_32x32x16_bf16 (A = weight fragment, B = activation fragment;
-// accumulator lane l holds row m = l % 32 and weight rows
-// 8*q + 4*(l/32) + r, register 4*q + r).
+// Block tile: TM rows x TN weight rows, K in chunks of TK, WM x WN waves,
+// each wave (TM/WM) rows x (TN/WN) weight rows of v_mfma_f32_32x32x16_bf16
+// (A = weight fragment, B = activation fragment; accumulator lane l holds
+// row m = l % 32 and weight rows 8*q + 4*(l/32) + r, register 4*q + r).
 //
 // Operands reach LDS through global_load_lds_dwordx4: each lane copies 16
 // bytes from any global address (so the token gather of the gate/up GEMM
-// happens inside the load) to LDS slot base + 16 * lane.  A wave
-// instruction fills 8 rows of 128 bytes.  Rows are XOR-swizzled in 16-byte
-// chunks (chunk c of row r sits at c ^ ((r >> 1) & 7)) so the 32 lanes
-// reading one column chunk hit distinct banks.  Three stages: while stage s
-// is multiplied, stages s+1 and s+2 are in flight.
+// happens inside the load) to LDS slot base + 16 * lane; one wave
+// instruction fills 1 KB.  Rows are XOR-swizzled in 16-byte chunks (chunk c
+// of row r sits at c ^ ((r / R) % C), R rows per 256 bytes, C chunks per
+// row) so that 16 lanes reading one column chunk of 16 rows hit 16 distinct
+// 4-bank groups.  STAGES buffers: while stage s is multiplied, the next
+// STAGES-1 are in flight.
 //
-// SWIGLU: the 256 weight rows are 128 gate rows [n0, n0+128) followed by
-// the matching 128 up rows; each wave holds gate and up accumulators for
-// the same (row, column) and writes SiLU(gate) * up.
+// SWIGLU: the TN weight rows are TN/2 gate rows [n0, n0 + TN/2) followed by
+// the matching up rows; each wave holds gate and up accumulators for the
+// same (row, column) and writes SiLU(gate) * up.
 //
 // Block order: blocks of one expert are numbered M-tile-fastest inside
 // groups of G N-tiles, so the M-tiles sharing a weight tile run together;
@@ -230,24 +230,49 @@ struct TileArgs {
   int group;                // N-tiles per group
 };
 
-constexpr int TL_M = 128, TL_N = 256, TL_K = 64, TL_STAGES = 3;
-constexpr int TL_XBYTES = TL_M * TL_K * 2;                 // 16 KB
-constexpr int TL_WBYTES = TL_N * TL_K * 2;                 // 32 KB
-constexpr int TL_STAGE_BYTES = TL_XBYTES + TL_WBYTES;      // 48 KB
+template <int TM_, int TN_, int TK_, int STAGES_, int WM_, int WN_, int MINB_>
+struct TileCfg {
+  static constexpr int TM = TM_, TN = TN_, TK = TK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr int MINB = MINB_;
+  static constexpr int NWAVE = WM * WN, NTHR = NWAVE * 64;
+  static constexpr int RB = TK * 2;                 // bytes per LDS row
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;              // rows per load instruction
+  static constexpr int RP256 = 256 / RB;            // rows per 256 bytes
+  static constexpr int XBYTES = TM * RB, WBYTES = TN * RB, SBYTES = XBYTES + WBYTES;
+  static constexpr int XLOADS = TM / RPI / NWAVE;   // load instructions per wave per stage
+  static constexpr int WLOADS = TN / RPI / NWAVE;
+  static constexpr int NLOADS = XLOADS + WLOADS;
+  static constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
+  static constexpr int MFM = WTM / 32, MFN = WTN / 32;
+  static constexpr int LDS = STAGES * SBYTES;
+  static_assert(TM % (RPI * NWAVE) == 0 && TN % (RPI * NWAVE) == 0, "load split");
+  static_assert(WTM % 32 == 0 && WTN % 64 == 0, "wave tile");
+  static_assert(TK % 16 == 0, "k step");
+};
 
-__device__ __forceinline__ int tl_swz(int r) { return (r >> 1) & 7; }
+template <class C>
+__device__ __forceinline__ int tile_swz(int r) { return (r / C::RP256) % C::CPR; }
 
-template <bool SWIGLU, bool OUT_BF16>
-__global__ __launch_bounds__(256) void ffn_tile_kernel(TileArgs a) {
+// Wait until at most N vector-memory loads of this wave are outstanding and
+// all its LDS reads have returned, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_stage_barrier() {
+  static_assert(N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+template <class C, bool SWIGLU, bool OUT_BF16>
+__global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int n_cols_tile = SWIGLU ? TL_N / 2 : TL_N;
+  const int n_cols_tile = SWIGLU ? C::TN / 2 : C::TN;
   const int NTn = a.N_out / n_cols_tile;
 
   // ---- which (expert, M-tile, N-tile) this block computes
   int e = 0, off = 0, end = a.M_dense, ms = 0, n_active;
   if (a.tile_map) n_active = a.n_tiles[0] * NTn;
-  else n_active = ((a.M_dense + TL_M - 1) / TL_M) * NTn;
+  else n_active = ((a.M_dense + C::TM - 1) / C::TM) * NTn;
   int b = blockIdx.x;
   if (b >= n_active) return;
   {
@@ -259,7 +284,7 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(TileArgs a) {
     const int4 tm = a.tile_map[mi];
     e = tm.x; off = tm.y; end = tm.z; ms = tm.w;
   }
-  const int te = (end - off + TL_M - 1) / TL_M;
+  const int te = (end - off + C::TM - 1) / C::TM;
   const int li = b - ms * NTn;
   const int G = a.group;
   const int g = li / (te * G);
@@ -267,103 +292,128 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(TileArgs a) {
   const int Gc = min(G, NTn - g * G);
   const int m_t = rem / Gc;
   const int n_t = g * G + (rem - m_t * Gc);
-  const int r0 = off + m_t * TL_M;
-  const int r1 = min(r0 + TL_M, end);
+  const int r0 = off + m_t * C::TM;
+  const int r1 = min(r0 + C::TM, end);
   const int n0 = n_t * n_cols_tile;
 
-  // ---- per-lane global source pointers for the 12 load instructions
-  const int prow = lane >> 3;        // row inside an 8-row group
-  const int pchunk = lane & 7;       // LDS chunk slot written by this lane
-  const bf16_t* xsrc[4];
+  // ---- per-lane global source pointers for the load instructions
+  const int prow = lane / C::CPR;    // row inside a load instruction's row group
+  const int pchunk = lane % C::CPR;  // LDS chunk slot written by this lane
+  const bf16_t* xsrc[C::XLOADS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rt = (wid + 4 * j) * 8 + prow;          // tile row 0..127
+  for (int j = 0; j < C::XLOADS; ++j) {
+    const int rt = (wid + C::NWAVE * j) * C::RPI + prow;
     int row = r0 + rt;
     if (row >= r1) row = r0;                          // padding rows read a valid row
     const int src = a.src_token ? a.src_token[row] : row;
-    const int c = pchunk ^ tl_swz(rt);
-    xsrc[j] = a.X + (size_t)src * a.K + c * 8;
+    xsrc[j] = a.X + (size_t)src * a.K + (pchunk ^ tile_swz<C>(rt)) * 8;
   }
   const bf16_t* We = a.W + (size_t)e * a.w_stride;
-  const bf16_t* wsrc[8];
+  const bf16_t* wsrc[C::WLOADS];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int rt = (wid + 4 * j) * 8 + prow;          // tile row 0..255
+  for (int j = 0; j < C::WLOADS; ++j) {
+    const int rt = (wid + C::NWAVE * j) * C::RPI + prow;
     int wrow;
-    if (SWIGLU) wrow = rt < 128 ? n0 + rt : a.up_off + n0 + (rt - 128);
+    if (SWIGLU) wrow = rt < C::TN / 2 ? n0 + rt : a.up_off + n0 + (rt - C::TN / 2);
     else wrow = n0 + rt;
-    const int c = pchunk ^ tl_swz(rt);
-    wsrc[j] = We + (size_t)wrow * a.K + c * 8;
+    wsrc[j] = We + (size_t)wrow * a.K + (pchunk ^ tile_swz<C>(rt)) * 8;
   }
 
   auto issue = [&](int ks, int buf) {
-    unsigned char* sx = smem + buf * TL_STAGE_BYTES;
-    unsigned char* sw = sx + TL_XBYTES;
-    const int ko = ks * TL_K;
+    unsigned char* sx = smem + buf * C::SBYTES;
+    unsigned char* sw = sx + C::XBYTES;
+    const int ko = ks * C::TK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C::XLOADS; ++j)
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[j] + ko),
-                                       (lds_void_t*)(sx + (wid + 4 * j) * 1024), 16, 0, 0);
+                                       (lds_void_t*)(sx + (wid + C::NWAVE * j) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < C::WLOADS; ++j)
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[j] + ko),
-                                       (lds_void_t*)(sw + (wid + 4 * j) * 1024), 16, 0, 0);
+                                       (lds_void_t*)(sw + (wid + C::NWAVE * j) * 1024), 16, 0, 0);
   };
 
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / C::WN, wn = wid % C::WN;
   const int lrow = lane & 31;
-  const int lsw = tl_swz(lrow);
   const int khalf = lane >> 5;
-  // weight-row bases of the wave's 4 N subtiles inside the 256-row tile
-  int nbase[4];
+  // weight-row bases of the wave's N subtiles inside the TN-row tile
+  int nbase[C::MFN];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    if (SWIGLU) nbase[ni] = (ni < 2 ? 0 : 128) + wn * 64 + (ni & 1) * 32;
-    else nbase[ni] = wn * 128 + ni * 32;
+  for (int ni = 0; ni < C::MFN; ++ni) {
+    if (SWIGLU) {
+      constexpr int HALF = C::MFN / 2;
+      nbase[ni] = (ni < HALF ? 0 : C::TN / 2) + wn * (C::WTN / 2) + (ni % HALF) * 32;
+    } else {
+      nbase[ni] = wn * C::WTN + ni * 32;
+    }
+  }
+  int xoff[C::MFM], woff[C::MFN];    // row offsets; the swizzle term is per row
+  int xsw[C::MFM], wsw[C::MFN];
+#pragma unroll
+  for (int mi = 0; mi < C::MFM; ++mi) {
+    const int r = wm * C::WTM + mi * 32 + lrow;
+    xoff[mi] = r * C::RB;
+    xsw[mi] = tile_swz<C>(r);
+  }
+#pragma unroll
+  for (int ni = 0; ni < C::MFN; ++ni) {
+    const int r = nbase[ni] + lrow;
+    woff[ni] = r * C::RB;
+    wsw[ni] = tile_swz<C>(r);
   }
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[C::MFM][C::MFN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::MFM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C::MFN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  const int nk = a.K / TL_K;
+  constexpr int KK = C::TK / 16;     // MFMA K steps per stage
+  const int nk = a.K / C::TK;
   auto load_frags = [&](const unsigned char* sx, const unsigned char* sw, int kk, bf16x8_t* xf,
                         bf16x8_t* wf) {
-    const int cpos = ((kk * 2 + khalf) ^ lsw) * 16;
+    const int c = kk * 2 + khalf;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-      xf[mi] = *reinterpret_cast<const bf16x8_t*>(sx + (wm * 64 + mi * 32 + lrow) * 128 + cpos);
+    for (int mi = 0; mi < C::MFM; ++mi)
+      xf[mi] = *reinterpret_cast<const bf16x8_t*>(sx + xoff[mi] + ((c ^ xsw[mi]) * 16));
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      wf[ni] = *reinterpret_cast<const bf16x8_t*>(sw + (nbase[ni] + lrow) * 128 + cpos);
+    for (int ni = 0; ni < C::MFN; ++ni)
+      wf[ni] = *reinterpret_cast<const bf16x8_t*>(sw + woff[ni] + ((c ^ wsw[ni]) * 16));
   };
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
+#pragma unroll
+  for (int s0 = 0; s0 < C::STAGES - 1; ++s0)
+    if (s0 < nk) issue(s0, s0);
   for (int ks = 0; ks < nk; ++ks) {
-    // Stage ks has landed for this wave once at most the 12 loads of stage
-    // ks+1 are outstanding; the barrier makes that true for every wave.  The
-    // fragments of the previous stage were all consumed by its MFMAs, so no
-    // LDS read of the buffer refilled below is still in flight.  (A
-    // __syncthreads() here would also drain stage ks+1 from the queue.)
-    if (ks + 1 < nk) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (ks + 2 < nk) issue(ks + 2, (ks + 2) % TL_STAGES);
-    const unsigned char* sx = smem + (ks % TL_STAGES) * TL_STAGE_BYTES;
-    const unsigned char* sw = sx + TL_XBYTES;
-    bf16x8_t xf[2][2], wf[2][4];
+    // Stage ks has landed for this wave once at most the loads of the
+    // STAGES-2 younger stages are outstanding; the barrier makes that true
+    // for every wave.  The fragments of the previous stage were consumed by
+    // its MFMAs, so no LDS read of the buffer refilled below is in flight.
+    // (A __syncthreads() here would also drain the younger stages.)
+    const int younger = min(nk - 1 - ks, C::STAGES - 2);
+    switch (younger) {
+      case 0: wait_stage_barrier<0>(); break;
+      case 1: wait_stage_barrier<C::NLOADS>(); break;
+      case 2: wait_stage_barrier<(C::STAGES > 3 ? 2 : 1) * C::NLOADS>(); break;
+      case 3: wait_stage_barrier<(C::STAGES > 4 ? 3 : 1) * C::NLOADS>(); break;
+      default: wait_stage_barrier<(C::STAGES > 5 ? 4 : 1) * C::NLOADS>(); break;
+    }
+    if (ks + C::STAGES - 1 < nk) issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES);
+    const unsigned char* sx = smem + (ks % C::STAGES) * C::SBYTES;
+    const unsigned char* sw = sx + C::XBYTES;
+    bf16x8_t xf[2][C::MFM], wf[2][C::MFN];
     load_frags(sx, sw, 0, xf[0], wf[0]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
-      if (kk + 1 < 4) load_frags(sx, sw, kk + 1, xf[cur ^ 1], wf[cur ^ 1]);
+      if (kk + 1 < KK) load_frags(sx, sw, kk + 1, xf[cur ^ 1], wf[cur ^ 1]);
+      // keep the next step's LDS reads ahead of this step's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < C::MFM; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < C::MFN; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][ni], xf[cur][mi],
                                                                 acc[mi][ni], 0, 0, 0);
     }
@@ -371,21 +421,20 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(TileArgs a) {
 
   // ---- epilogue
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int row = r0 + wm * 64 + mi * 32 + lrow;
+  for (int mi = 0; mi < C::MFM; ++mi) {
+    const int row = r0 + wm * C::WTM + mi * 32 + lrow;
     if (row >= r1) continue;
     if (SWIGLU) {
+      constexpr int HALF = C::MFN / 2;
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int col0 = n0 + wn * 64 + ni * 32 + 4 * khalf;
+      for (int ni = 0; ni < HALF; ++ni) {
+        const int col0 = n0 + wn * (C::WTN / 2) + ni * 32 + 4 * khalf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gv = acc[mi][ni][4 * q + r], uv = acc[mi][ni + 2][4 * q + r];
-            h[r] = silu(gv) * uv;
-          }
+          for (int r = 0; r < 4; ++r)
+            h[r] = silu(acc[mi][ni][4 * q + r]) * acc[mi][ni + HALF][4 * q + r];
           uint2 o = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
           *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.Y) + (size_t)row * a.N_out +
                                     col0 + 8 * q) = o;
@@ -393,8 +442,8 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(TileArgs a) {
       }
     } else {
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int col0 = n0 + wn * 128 + ni * 32 + 4 * khalf;
+      for (int ni = 0; ni < C::MFN; ++ni) {
+        const int col0 = n0 + wn * C::WTN + ni * 32 + 4 * khalf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const size_t yi = (size_t)row * a.N_out + col0 + 8 * q;
@@ -412,6 +461,16 @@ __global__ __launch_bounds__(256) void ffn_tile_kernel(TileArgs a) {
     }
   }
 }
+
+// Tile shapes for prefill-sized expert GEMMs (8 waves: two per SIMD, so one
+// wave's waits on LDS or on the stage barrier overlap the other's MFMAs).
+// Experts with >= 384 expected rows take 256-row tiles; smaller ones take
+// 128-row tiles, which waste less on each expert's partial last tile.
+using TileBig = TileCfg<256, 256, 64, 2, 2, 4, 1>;
+using TileMed = TileCfg<128, 256, 64, 3, 2, 4, 1>;
+constexpr int BIG_TILE_MIN_ROWS = 384;
+static_assert(TileBig::TN == TileMed::TN && TileBig::TK == TileMed::TK, "shared shape limits");
+constexpr int TL_N = TileMed::TN, TL_K = TileMed::TK;
 
 // ---------------------------------------------------------------------------
 // float32 layer: one thread per output element of a 16 x 16 tile, plain FMA
@@ -473,36 +532,46 @@ bool ffn_tile_ok(int H, int I_loc) {
 
 int ffn_row_tile(int dt, int mean_rows, int H, int I_loc) {
   if (dt == 0) return 16;
-  if (mean_rows >= 64 && ffn_tile_ok(H, I_loc)) return TL_M;
+  if (mean_rows >= 64 && ffn_tile_ok(H, I_loc))
+    return mean_rows >= BIG_TILE_MIN_ROWS ? TileBig::TM : TileMed::TM;
   if (mean_rows <= 16) return 16;
   if (mean_rows <= 32) return 32;
   return 64;
 }
 
-template <bool SWIGLU, bool OUT_BF16>
-static hipError_t launch_tile(const TileArgs& a, int max_tiles, hipStream_t st) {
+static bool is_tile_bm(int BM) { return BM == TileBig::TM || BM == TileMed::TM; }
+
+template <class C, bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, hipStream_t st) {
   static bool attr_set = false;
-  const int lds = TL_STAGES * TL_STAGE_BYTES;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ffn_tile_kernel<SWIGLU, OUT_BF16>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  const int ntn = a.N_out / (SWIGLU ? TL_N / 2 : TL_N);
-  ffn_tile_kernel<SWIGLU, OUT_BF16><<<max_tiles * ntn, 256, lds, st>>>(a);
+  const int ntn = a.N_out / (SWIGLU ? C::TN / 2 : C::TN);
+  ffn_tile_kernel<C, SWIGLU, OUT_BF16><<<max_tiles * ntn, C::NTHR, C::LDS, st>>>(a);
   return hipGetLastError();
 }
 
 // N-tiles per group: enough M-tiles x N-tiles of one expert to fill the 32
 // CUs of an XCD while they share that expert's weight tiles.
-static int tile_group(int mean_rows, int ntn) {
-  const int te = (mean_rows + TL_M - 1) / TL_M;
+static int tile_group(int mean_rows, int tm, int ntn) {
+  const int te = (mean_rows + tm - 1) / tm;
   int g = 32 / (te > 0 ? te : 1);
   if (g < 1) g = 1;
   if (g > ntn) g = ntn;
   return g;
+}
+
+template <bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_tile(TileArgs a, int BM, int mean_rows, int max_tiles, hipStream_t st) {
+  const int ntn = a.N_out / (SWIGLU ? TL_N / 2 : TL_N);
+  a.group = tile_group(mean_rows, BM, ntn);
+  if (BM == TileBig::TM) return launch_tile_cfg<TileBig, SWIGLU, OUT_BF16>(a, max_tiles, st);
+  return launch_tile_cfg<TileMed, SWIGLU, OUT_BF16>(a, max_tiles, st);
 }
 
 static int pick_nw(int steps, int max_nw) {
@@ -548,11 +617,10 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {
     ffn_f32_kernel<true><<<a.max_tiles * (a.I_loc / 16), 256, 0, st>>>(g1);
     return hipGetLastError();
   }
-  if (BM == TL_M) {
+  if (is_tile_bm(BM)) {
     TileArgs t{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
-               (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h,
-               tile_group(a.mean_rows, a.I_loc / (TL_N / 2))};
-    return launch_tile<true, true>(t, a.max_tiles, st);
+               (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h, 1};
+    return launch_tile<true, true>(t, BM, a.mean_rows, a.max_tiles, st);
   }
   DirectArgs g1{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
                 (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h};
@@ -567,12 +635,11 @@ hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st) {
     ffn_f32_kernel<false><<<a.max_tiles * (a.H / 16), 256, 0, st>>>(g2);
     return hipGetLastError();
   }
-  if (BM == TL_M) {
+  if (is_tile_bm(BM)) {
     TileArgs t{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
-               (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y,
-               tile_group(a.mean_rows, a.H / TL_N)};
-    if (a.y_dt == 0) return launch_tile<false, false>(t, a.max_tiles, st);
-    return launch_tile<false, true>(t, a.max_tiles, st);
+               (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y, 1};
+    if (a.y_dt == 0) return launch_tile<false, false>(t, BM, a.mean_rows, a.max_tiles, st);
+    return launch_tile<false, true>(t, BM, a.mean_rows, a.max_tiles, st);
   }
   DirectArgs g2{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
                 (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y};
