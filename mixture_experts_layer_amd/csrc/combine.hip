@@ -26,24 +26,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int r = dst_row[(size_t)t * k + j];
-    if (r < 0) continue;
-    const float wj = w[(size_t)t * k + j];
-    float v[8];
-    if (IN_BF16) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(
-          reinterpret_cast<const bf16_t*>(y_perm) + (size_t)r * H + c0);
-      unpack_bf16x8(raw, v);
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(
-          reinterpret_cast<const float*>(y_perm) + (size_t)r * H + c0);
-      const float4 lo = p[0], hi = p[1];
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  // up to 8 permuted rows per batch: their loads are all in flight before the
+  // first multiply-add; the sum still runs in slot order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int rows[8];
+    float wj[8];
+    uint4 raw[8][IN_BF16 ? 1 : 2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      rows[u] = j < k ? dst_row[(size_t)t * k + j] : -1;
+      wj[u] = j < k ? w[(size_t)t * k + j] : 0.f;
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    for (int u = 0; u < 8; ++u) {
+      if (rows[u] < 0) continue;
+      if (IN_BF16) {
+        raw[u][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(y_perm) +
+                                                     (size_t)rows[u] * H + c0);
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(y_perm) +
+                                                        (size_t)rows[u] * H + c0);
+        raw[u][0] = p[0];
+        raw[u][IN_BF16 ? 0 : 1] = p[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (rows[u] < 0) continue;
+      float v[8];
+      if (IN_BF16) {
+        unpack_bf16x8(raw[u][0], v);
+      } else {
+        const uint4 lo = raw[u][0], hi = raw[u][IN_BF16 ? 0 : 1];
+        v[0] = __uint_as_float(lo.x); v[1] = __uint_as_float(lo.y);
+        v[2] = __uint_as_float(lo.z); v[3] = __uint_as_float(lo.w);
+        v[4] = __uint_as_float(hi.x); v[5] = __uint_as_float(hi.y);
+        v[6] = __uint_as_float(hi.z); v[7] = __uint_as_float(hi.w);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj[u], v[q], acc[q]);
+    }
   }
   if (y_shared) {
     float v[8];

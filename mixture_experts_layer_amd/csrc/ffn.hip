@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
   constexpr int BN = 16 * NT;
   constexpr int NACC = MT * NT * NS;
   constexpr int PITCH = 65;
-  constexpr int U = 4;
+  constexpr int U = MT == 1 ? 8 : (MT == 2 ? 6 : 4);   // K steps per load batch
   __shared__ float red[NW * NACC * 4 * PITCH];
 
   const int n_ntiles = a.N_out / BN;
@@ -96,17 +96,19 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) acc[mt][nt][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // this wave's contiguous share of the K steps (32 elements each)
+  // this wave's contiguous share of the K steps (32 elements each), taken
+  // U steps per batch: every load of a batch is issued before its first
+  // MFMA.  Steps past the share re-read the share's last step (a valid
+  // address) and multiply zeros, so a batch never waits step by step.
   const int S = a.K / 32;
   const int s_begin = (S * wid) / NW;
   const int s_end = (S * (wid + 1)) / NW;
 
-  int s = s_begin;
-  for (; s + U <= s_end; s += U) {
+  for (int s = s_begin; s < s_end; s += U) {
     uint4 xa[U][MT], wa[U][NT], wb[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ko = (s + u) * 32;
+      const int ko = min(s + u, s_end - 1) * 32;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         wa[u][nt] = *reinterpret_cast<const uint4*>(wg[nt] + ko);
@@ -117,7 +119,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
         xa[u][mt] = xv[mt] ? *reinterpret_cast<const uint4*>(xp[mt] + ko) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (s + u >= s_end) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xa[u][mt] = make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -128,28 +134,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
             acc[mt][nt][NS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 as_bf16x8(wb[u][nt]), as_bf16x8(xa[u][mt]), acc[mt][nt][NS - 1], 0, 0, 0);
         }
-  }
-  for (; s < s_end; ++s) {
-    const int ko = s * 32;
-    uint4 xa[MT], wa[NT], wb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      wa[nt] = *reinterpret_cast<const uint4*>(wg[nt] + ko);
-      if (SWIGLU) wb[nt] = *reinterpret_cast<const uint4*>(wu[nt] + ko);
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      xa[mt] = xv[mt] ? *reinterpret_cast<const uint4*>(xp[mt] + ko) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[mt][nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(wa[nt]), as_bf16x8(xa[mt]), acc[mt][nt][0], 0, 0, 0);
-        if (SWIGLU)
-          acc[mt][nt][NS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(wb[nt]), as_bf16x8(xa[mt]), acc[mt][nt][NS - 1], 0, 0, 0);
-      }
   }
 
   // partial sums -> LDS: red[w][((mt*NT + nt)*NS + which)*4 + i][lane]
@@ -556,15 +541,10 @@ static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, hipStream_t 
   return hipGetLastError();
 }
 
-// N-tiles per group: enough M-tiles x N-tiles of one expert to fill the 32
-// CUs of an XCD while they share that expert's weight tiles.
-static int tile_group(int mean_rows, int tm, int ntn) {
-  const int te = (mean_rows + tm - 1) / tm;
-  int g = 32 / (te > 0 ? te : 1);
-  if (g < 1) g = 1;
-  if (g > ntn) g = ntn;
-  return g;
-}
+// N-tiles per group.  One N-tile per group (all M-tiles of an expert that
+// share a weight tile numbered consecutively, on one XCD) fetched the least
+// from beyond L2 and ran fastest among groups of 1, 2, 4 and all N-tiles.
+static int tile_group(int /*mean_rows*/, int /*tm*/, int /*ntn*/) { return 1; }
 
 template <bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_tile(TileArgs a, int BM, int mean_rows, int max_tiles, hipStream_t st) {
@@ -574,9 +554,11 @@ static hipError_t launch_tile(TileArgs a, int BM, int mean_rows, int max_tiles, 
   return launch_tile_cfg<TileMed, SWIGLU, OUT_BF16>(a, max_tiles, st);
 }
 
-static int pick_nw(int steps, int max_nw) {
+// Waves per block: enough that each wave's K share is one load batch where
+// the block size allows it, and never shares of fewer than 4 steps.
+static int pick_nw(int steps, int max_nw, int batch) {
   int nw = 1;
-  while (nw * 2 <= max_nw && steps / (nw * 2) >= 6) nw *= 2;
+  while (nw * 2 <= max_nw && (steps + nw - 1) / nw > batch && steps / (nw * 2) >= 4) nw *= 2;
   return nw;
 }
 
@@ -604,9 +586,9 @@ static hipError_t launch_direct_nw(const DirectArgs& a, int nw, int max_tiles, h
 template <bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, hipStream_t st) {
   const int steps = a.K / 32;
-  if (BM == 16) return launch_direct_nw<1, 16, SWIGLU, OUT_BF16>(a, pick_nw(steps, 16), max_tiles, st);
-  if (BM == 32) return launch_direct_nw<2, 16, SWIGLU, OUT_BF16>(a, pick_nw(steps, 16), max_tiles, st);
-  return launch_direct_nw<4, 8, SWIGLU, OUT_BF16>(a, pick_nw(steps, 8), max_tiles, st);
+  if (BM == 16) return launch_direct_nw<1, 16, SWIGLU, OUT_BF16>(a, pick_nw(steps, 16, 8), max_tiles, st);
+  if (BM == 32) return launch_direct_nw<2, 8, SWIGLU, OUT_BF16>(a, pick_nw(steps, 8, 6), max_tiles, st);
+  return launch_direct_nw<4, 8, SWIGLU, OUT_BF16>(a, pick_nw(steps, 8, 4), max_tiles, st);
 }
 
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {

@@ -49,33 +49,41 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------
-// Block-wide exclusive scan of n ints held in LDS (n <= 4 * blockDim.x).
-// `data` is replaced by its exclusive prefix sums; returns the total.
-// `tmp` needs blockDim.x + 1 ints.  All threads of the block must call it.
+// Block-wide exclusive scan of n ints held in LDS (n <= 4 * blockDim.x,
+// blockDim.x a multiple of 64 and at most 1024).  `data` is replaced by its
+// exclusive prefix sums; returns the total.  Per-thread chunk sums are
+// scanned inside each wave with shuffles, then across waves through `tmp`
+// (at least blockDim.x / 64 ints): one barrier in the middle, one at the end.
+// All threads of the block must call it, after `data` is visible to all.
 // ---------------------------------------------------------------------------
 __device__ inline int block_exclusive_scan(int* data, int n, int* tmp) {
   const int tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & 63, wid = tid >> 6, nw = nt >> 6;
   const int per = (n + nt - 1) / nt;
   const int b = tid * per;
   int local = 0;
   for (int i = 0; i < per; ++i)
     if (b + i < n) local += data[b + i];
-  tmp[tid] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread sums.
-  for (int off = 1; off < nt; off <<= 1) {
-    int v = (tid >= off) ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
+  int v = local;  // inclusive scan inside the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
   }
-  int run = tmp[tid] - local;
-  const int total = tmp[nt - 1];
+  if (lane == 63) tmp[wid] = v;
+  __syncthreads();
+  int wbase = 0, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = tmp[w];
+    if (w < wid) wbase += t;
+    total += t;
+  }
+  int run = wbase + v - local;
   for (int i = 0; i < per; ++i)
     if (b + i < n) {
-      const int v = data[b + i];
+      const int x = data[b + i];
       data[b + i] = run;
-      run += v;
+      run += x;
     }
   __syncthreads();
   return total;

@@ -191,10 +191,10 @@ static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, i
 }
 
 // ---------------------------------------------------------------------------
-// Wave-wide reductions: DPP inside each 16-lane row (pairs at distance 1, 2,
-// then the half-row and row mirrors), then the four row results via
-// readlane.  Every lane ends with the result; the combination order is fixed,
-// so float sums are the same on every run.
+// Row reductions: DPP inside each 16-lane row -- pairs at distance 1 and 2,
+// then the half-row and row mirrors -- leave every lane of the row with the
+// row's result; the combination order is fixed, so float sums are the same
+// on every run.
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -211,65 +211,48 @@ constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIR
 __device__ __forceinline__ bool better(float ok, int oi, float k, int i) {
   return ok > k || (ok == k && oi < i);
 }
+// (key, id, logit) arg-max step between this lane and the lane selected by
+// DPP pattern CTRL.
 template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& k, int& i) {
+__device__ __forceinline__ void argmax3_step(float& k, int& i, float& s) {
   const float ok = dpp_f<CTRL>(k);
   const int oi = dpp_i<CTRL>(i);
-  if (better(ok, oi, k, i)) { k = ok; i = oi; }
+  const float os = dpp_f<CTRL>(s);
+  if (better(ok, oi, k, i)) { k = ok; i = oi; s = os; }
 }
-__device__ __forceinline__ void wave_argmax(float& k, int& i) {
-  argmax_step<DPP_XOR1>(k, i);
-  argmax_step<DPP_XOR2>(k, i);
-  argmax_step<DPP_HALF_MIRROR>(k, i);
-  argmax_step<DPP_MIRROR>(k, i);
-  float bk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k), 0));
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) {
-    const float ok = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k), r));
-    const int oi = __builtin_amdgcn_readlane(i, r);
-    if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
-  }
-  k = bk;
-  i = bi;
-}
-__device__ __forceinline__ float wave_sum(float v) {
+
+// Sum over each 16-lane row.
+__device__ __forceinline__ float row_sum(float v) {
   v += dpp_f<DPP_XOR1>(v);
   v += dpp_f<DPP_XOR2>(v);
   v += dpp_f<DPP_HALF_MIRROR>(v);
   v += dpp_f<DPP_MIRROR>(v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return (r0 + r1) + (r2 + r3);
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<DPP_XOR1>(v));
-  v = fmaxf(v, dpp_f<DPP_XOR2>(v));
-  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
-  v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  return v;
 }
 
 // ---------------------------------------------------------------------------
-// Gating + routing metadata for one tile of TOK_TILE tokens (NW waves; a
-// wave takes tokens wid, wid + NW, ...; the next token's logits are loaded
-// while the current one is processed).
+// Gating + routing metadata for one tile of TOK_TILE tokens.
 //
-// Selection: k rounds of a wave-wide arg-max over (key descending, id
-// ascending); the key is the logit, or logit + sel_bias in float32 for the
-// sigmoid mode.  Exact comparisons only, so the chosen ids are a function of
-// the float32 logits alone.
+// Selection: each 16-lane row of a wave owns one token; with 16 waves the
+// tile's 64 tokens are all in flight at once (four waves per SIMD hide the
+// DPP and LDS latencies).  Lane `sub` holds experts sub, sub + 16, ... (EPR
+// of them).  k rounds of a row-wide arg-max over (key descending, id
+// ascending) -- four DPP steps -- pick the experts in order; every lane of
+// the row sees the winner, the lane holding it retires it, and lane r % 16
+// keeps choice r.  The key is the logit, or logit + sel_bias in float32 for
+// the sigmoid mode; only exact comparisons decide, so the chosen ids are a
+// function of the float32 logits alone.  The round loop is not unrolled:
+// this kernel runs once per layer call, so its code is kept small.  The
+// tile's logits are staged in LDS (E <= 256) with a row pitch that puts the
+// 64 lanes of a wave in 64 distinct banks.  The gate weights are finished in
+// the row too (sums by DPP) and written straight out.
 //
-// Histogram and ranks (no atomics): after the tile's ids are in LDS, thread
-// e walks the tile's (token, slot) pairs in order and numbers the ones routed
-// to local expert e.  The rank of a pair inside its expert's segment of the
-// tile is that number, so rows keep ascending token order.
+// Histogram and ranks (no atomics): the tile's (token, slot) pairs are cut
+// into C chunks; thread (chunk, e) counts the pairs of its chunk routed to
+// local expert e, and after a barrier walks the chunk again numbering them
+// from the counts of the chunks before it.  The rank of a pair inside its
+// expert's segment of the tile is that number, so rows keep ascending token
+// order.
 //
 // single != 0 (the whole batch is this one tile): the block also finishes the
 // permutation -- counts, offsets, dst_row, src_token and the GEMM tile map.
@@ -277,132 +260,195 @@ __device__ __forceinline__ float wave_max(float v) {
 // scan and scatter kernels.
 // do_gate == 0: ids come from ids_in (permutation only, no gating).
 // ---------------------------------------------------------------------------
-template <int EPL, int NW>
-__global__ __launch_bounds__(NW * 64) void gate_tile_kernel(GateTileArgs a) {
+constexpr int GATE_STAGE_E = 256;                       // largest E staged in LDS
+constexpr int GATE_PITCH_MAX = GATE_STAGE_E + 4;
+
+template <int EPR>
+struct GateWaves {
+  // 16 waves while a lane's experts fit comfortably in 128 VGPRs
+  static constexpr int value = EPR <= 16 ? 16 : 4;
+};
+
+template <int EPR, bool STAGE>
+__global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(GateTileArgs a) {
+  constexpr int NW = GateWaves<EPR>::value;
+  constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) int s_ids[TOK_TILE * KMAX];
   __shared__ int s_rank[TOK_TILE * KMAX];
+  __shared__ __attribute__((aligned(16))) float s_logits[STAGE ? TOK_TILE * GATE_PITCH_MAX : 4];
   __shared__ int s_cnt[1024];
+  __shared__ int s_part[1024];
   __shared__ int s_off[1025];
   __shared__ int s_scr[1024];
-  __shared__ int s_tmp[NW * 64 + 1];
+  __shared__ int s_tmp[NT + 1];
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int t0 = tile * TOK_TILE;
   const int ntok = max(0, min(TOK_TILE, a.T - t0));
   const int k = a.k, E = a.E;
-  const bool sig = a.mode == 3;
+  const int mode = a.mode;
+  const bool sig = mode == 3;
 
   if (a.do_gate) {
-    float s_next[EPL];
-    auto load = [&](int tt, float* s) {
+    const int P = ((E + 63) & ~63) + 4;               // LDS row pitch (floats)
+    if (STAGE) {
+      const float* src = a.logits + (size_t)t0 * E;
+      const int nval = ntok * E;
+      if ((E & 3) == 0) {
+        // 16-byte loads, up to four in flight per thread; a 16-byte group
+        // never straddles two rows when E is a multiple of 4
+        const int nv4 = nval >> 2;
+        const float4* src4 = reinterpret_cast<const float4*>(src);
+        for (int i0 = threadIdx.x; i0 < nv4; i0 += 4 * NT) {
+          float4 v[4];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        s[i] = (tt < ntok && e < E) ? a.logits[(size_t)(t0 + tt) * E + e] : 0.f;
+          for (int u = 0; u < 4; ++u) v[u] = src4[min(i0 + u * NT, nv4 - 1)];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = (i0 + u * NT) * 4;
+            if (i < nval) {
+              const int r = i / E, c = i - r * E;
+              *reinterpret_cast<float4*>(s_logits + r * P + c) = v[u];
+            }
+          }
+        }
+      } else {
+        for (int i = threadIdx.x; i < nval; i += NT) s_logits[(i / E) * P + i % E] = src[i];
       }
-    };
-    load(wid, s_next);
-    for (int tt = wid; tt < ntok; tt += NW) {
-      const int t = t0 + tt;
-      float s[EPL], key[EPL];
+      __syncthreads();
+    }
+    const int row = lane >> 4, sub = lane & 15;
+    for (int pass = 0; pass * NW * 4 < ntok; ++pass) {
+      const int tt = pass * NW * 4 + wid * 4 + row;
+      const bool live = tt < ntok;
+      float s[EPR], key[EPR];
+      bool avail[EPR];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) s[i] = s_next[i];
-      load(tt + NW, s_next);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = e < E ? s[i] : -INFINITY;
-        if (sig && a.sel_bias && e < E) key[i] = s[i] + a.sel_bias[e];
+      for (int i = 0; i < EPR; ++i) {
+        const int e = sub + 16 * i;
+        avail[i] = live && e < E;
+        s[i] = avail[i] ? (STAGE ? s_logits[tt * P + e] : a.logits[(size_t)(t0 + tt) * E + e])
+                        : 0.f;
+        key[i] = avail[i] ? ((sig && a.sel_bias) ? s[i] + a.sel_bias[e] : s[i]) : -INFINITY;
       }
-      bool avail[EPL];
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) avail[i] = lane + 64 * i < E;
-      int sel_id = -1;       // lane j < k keeps the j-th choice
-      float sel_s = 0.f;
+      // choices sub and sub + 16 of this token (k <= 32)
+      int id0 = -1, id1 = -1;
+      float v0 = 0.f, v1 = 0.f, first_s = 0.f;
       for (int r = 0; r < k; ++r) {
-        float bk = -INFINITY;
+        float bk = -INFINITY, bs = 0.f;
         int bi = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          const int e = lane + 64 * i;
-          if (avail[i] && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
-        }
-        wave_argmax(bk, bi);
-        // the owner lane retires the winner; every lane learns its logit
-        float win_s = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          if (lane + 64 * i == bi) {
-            avail[i] = false;
-            win_s = s[i];
+        for (int i = 0; i < EPR; ++i)
+          if (avail[i] && better(key[i], sub + 16 * i, bk, bi)) {
+            bk = key[i];
+            bi = sub + 16 * i;
+            bs = s[i];
           }
-        win_s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, win_s),
-                                                                    bi & 63));
-        if (lane == r) {
-          sel_id = bi;
-          sel_s = win_s;
+        argmax3_step<DPP_XOR1>(bk, bi, bs);
+        argmax3_step<DPP_XOR2>(bk, bi, bs);
+        argmax3_step<DPP_HALF_MIRROR>(bk, bi, bs);
+        argmax3_step<DPP_MIRROR>(bk, bi, bs);
+        if (r == 0) first_s = bs;
+        if (sub == (r & 15)) {
+          if (r < 16) { id0 = bi; v0 = bs; }
+          else { id1 = bi; v1 = bs; }
         }
+#pragma unroll
+        for (int i = 0; i < EPR; ++i)
+          if (sub + 16 * i == bi) avail[i] = false;
       }
-      // gate weights of the k choices (lanes 0..k-1)
-      const bool mine = lane < k;
-      float wv;
-      if (a.mode == 0) {
-        const float m = wave_max(mine ? sel_s : -INFINITY);
-        const float ev = mine ? expf(sel_s - m) : 0.f;
-        wv = ev / wave_sum(ev);
-      } else if (a.mode == 1 || a.mode == 2) {
-        // softmax over all E; the largest logit is the first choice
-        const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sel_s), 0));
+      // gate weights of the chosen experts
+      const bool h0 = live && sub < k, h1 = live && sub + 16 < k;
+      float g0, g1;
+      if (mode == 3) {
+        g0 = h0 ? 1.0f / (1.0f + expf(-v0)) : 0.f;
+        g1 = h1 ? 1.0f / (1.0f + expf(-v1)) : 0.f;
+        const float z = row_sum(g0 + g1);
+        g0 = g0 / z;
+        g1 = g1 / z;
+      } else if (mode == 0) {
+        // softmax over the k chosen logits; the first choice is the largest
+        g0 = h0 ? expf(v0 - first_s) : 0.f;
+        g1 = h1 ? expf(v1 - first_s) : 0.f;
+        const float z = row_sum(g0 + g1);
+        g0 = g0 / z;
+        g1 = g1 / z;
+      } else {
+        // softmax over all E, then (mode 2) renormalised over the k chosen
         float z = 0.f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          if (lane + 64 * i < E) z += expf(s[i] - m);
-        z = wave_sum(z);
-        float p = mine ? expf(sel_s - m) / z : 0.f;
-        if (a.mode == 2) p = p / wave_sum(p);
-        wv = p;
-      } else {
-        const float sg = mine ? 1.0f / (1.0f + expf(-sel_s)) : 0.f;
-        wv = sg / wave_sum(sg);
+        for (int i = 0; i < EPR; ++i)
+          if (live && sub + 16 * i < E) z += expf(s[i] - first_s);
+        z = row_sum(z);
+        g0 = h0 ? expf(v0 - first_s) / z : 0.f;
+        g1 = h1 ? expf(v1 - first_s) / z : 0.f;
+        if (mode == 2) {
+          const float ps = row_sum(g0 + g1);
+          g0 = g0 / ps;
+          g1 = g1 / ps;
+        }
       }
-      if (mine) {
-        a.ids_out[(size_t)t * k + lane] = sel_id;
-        a.w_out[(size_t)t * k + lane] = wv;
-        s_ids[tt * k + lane] = sel_id;
+      if (h0) {
+        s_ids[tt * k + sub] = id0;
+        a.ids_out[(size_t)(t0 + tt) * k + sub] = id0;
+        a.w_out[(size_t)(t0 + tt) * k + sub] = g0;
+      }
+      if (h1) {
+        s_ids[tt * k + sub + 16] = id1;
+        a.ids_out[(size_t)(t0 + tt) * k + sub + 16] = id1;
+        a.w_out[(size_t)(t0 + tt) * k + sub + 16] = g1;
       }
     }
   } else {
-    for (int i = threadIdx.x; i < ntok * k; i += NW * 64) s_ids[i] = a.ids_in[(size_t)t0 * k + i];
+    for (int i = threadIdx.x; i < ntok * k; i += NT) s_ids[i] = a.ids_in[(size_t)t0 * k + i];
   }
   if (!a.do_permute) return;
   const int npair = ntok * k;
   // pad the id list to a multiple of 16 with an id no expert has
-  for (int p = npair + threadIdx.x; p < ((npair + 15) & ~15); p += NW * 64) s_ids[p] = -1;
+  for (int p = npair + threadIdx.x; p < ((npair + 15) & ~15); p += NT) s_ids[p] = -1;
   __syncthreads();
 
-  // atomic-free histogram and in-tile ranks, 16 ids per LDS pass
+  // atomic-free histogram and in-tile ranks, 16 ids per LDS read
   const int E_loc = a.e_end - a.e_begin;
-  for (int el = threadIdx.x; el < E_loc; el += NW * 64) {
-    const int e = a.e_begin + el;
+  const int C = E_loc >= NT ? 1 : min(16, NT / E_loc);     // chunks of the pair list
+  const int L = ((npair + C - 1) / C + 15) & ~15;          // pairs per chunk
+  for (int job = threadIdx.x; job < C * E_loc; job += NT) {
+    const int ch = job / E_loc, e = a.e_begin + (job - ch * E_loc);
+    const int p1 = min(npair, (ch + 1) * L);
     int c = 0;
-    for (int p = 0; p < npair; p += 16) {
+    for (int p = ch * L; p < p1; p += 16) {
       const int4* q = reinterpret_cast<const int4*>(s_ids + p);
-      const int4 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
-      const int ids16[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                             v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+      const int4 w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+      c += (w0.x == e) + (w0.y == e) + (w0.z == e) + (w0.w == e) + (w1.x == e) + (w1.y == e) +
+           (w1.z == e) + (w1.w == e) + (w2.x == e) + (w2.y == e) + (w2.z == e) + (w2.w == e) +
+           (w3.x == e) + (w3.y == e) + (w3.z == e) + (w3.w == e);
+    }
+    s_part[job] = c;
+  }
+  __syncthreads();
+  for (int job = threadIdx.x; job < C * E_loc; job += NT) {
+    const int ch = job / E_loc, el = job - ch * E_loc, e = a.e_begin + el;
+    int c = 0;
+    for (int q = 0; q < ch; ++q) c += s_part[q * E_loc + el];
+    if (ch == C - 1) s_cnt[el] = c + s_part[job];
+    const int p1 = min(npair, (ch + 1) * L);
+    for (int p = ch * L; p < p1; p += 16) {
+      const int4* q = reinterpret_cast<const int4*>(s_ids + p);
+      const int4 w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+      const int ids16[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
+                             w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (ids16[j] == e) s_rank[p + j] = c++;
     }
-    s_cnt[el] = c;
   }
   __syncthreads();
 
   if (!a.single) {
-    for (int el = threadIdx.x; el < E_loc; el += NW * 64)
+    for (int el = threadIdx.x; el < E_loc; el += NT)
       a.tile_counts[(size_t)tile * E_loc + el] = s_cnt[el];
-    for (int p = threadIdx.x; p < npair; p += NW * 64) {
+    for (int p = threadIdx.x; p < npair; p += NT) {
       const int e = s_ids[p];
       const bool local = e >= a.e_begin && e < a.e_end;
       a.rank_out[(size_t)t0 * k + p] = local ? s_rank[p] : -1;
@@ -410,15 +456,15 @@ __global__ __launch_bounds__(NW * 64) void gate_tile_kernel(GateTileArgs a) {
     return;
   }
 
-  // single tile: finish the permutation here
-  for (int el = threadIdx.x; el < E_loc; el += NW * 64) s_off[el] = s_cnt[el];
+// single tile: finish the permutation here
+  for (int el = threadIdx.x; el < E_loc; el += NT) s_off[el] = s_cnt[el];
   __syncthreads();
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
   if (threadIdx.x == 0) s_off[E_loc] = total;
   __syncthreads();
-  for (int el = threadIdx.x; el < E_loc; el += NW * 64) a.counts[el] = s_cnt[el];
-  for (int el = threadIdx.x; el <= E_loc; el += NW * 64) a.offsets[el] = s_off[el];
-  for (int p = threadIdx.x; p < npair; p += NW * 64) {
+  for (int el = threadIdx.x; el < E_loc; el += NT) a.counts[el] = s_cnt[el];
+  for (int el = threadIdx.x; el <= E_loc; el += NT) a.offsets[el] = s_off[el];
+  for (int p = threadIdx.x; p < npair; p += NT) {
     const int e = s_ids[p];
     int row = -1;
     if (e >= a.e_begin && e < a.e_end) {
@@ -438,7 +484,7 @@ __global__ __launch_bounds__(NW * 64) void gate_tile_kernel(GateTileArgs a) {
 hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,
                                 const float* bias, float* logits, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const bool mfma_shape = dt == 1 && T > 32 && H % RT_K == 0 &&
+  const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 &&
                           (E == 32 || E == 64 || E == 128 || E == 256);
   if (!mfma_shape) {
     dim3 grid(E, (T + 7) / 8);
@@ -460,21 +506,23 @@ hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, in
   }
 }
 
-template <int NW>
-static void launch_gate_nw(const GateTileArgs& a, int grid, hipStream_t st) {
-  const int epl = (a.E + 63) / 64;
-  if (epl <= 1) gate_tile_kernel<1, NW><<<grid, NW * 64, 0, st>>>(a);
-  else if (epl <= 2) gate_tile_kernel<2, NW><<<grid, NW * 64, 0, st>>>(a);
-  else if (epl <= 4) gate_tile_kernel<4, NW><<<grid, NW * 64, 0, st>>>(a);
-  else if (epl <= 8) gate_tile_kernel<8, NW><<<grid, NW * 64, 0, st>>>(a);
-  else gate_tile_kernel<16, NW><<<grid, NW * 64, 0, st>>>(a);
+// E <= 256 (at most 16 experts per lane) stages the logits in LDS.
+template <int EPR>
+static void launch_gate_epr(const GateTileArgs& a, int grid, hipStream_t st) {
+  constexpr bool stage = EPR * 16 <= GATE_STAGE_E;
+  gate_tile_kernel<EPR, stage><<<grid, GateWaves<EPR>::value * 64, 0, st>>>(a);
 }
 
 hipError_t launch_gate_tiles(const GateTileArgs& a, int n_tiles_tok, hipStream_t st) {
   const int grid = n_tiles_tok > 0 ? n_tiles_tok : 1;
-  // one tile (decode-sized batch): 16 waves share its 64 tokens
-  if (grid == 1) launch_gate_nw<16>(a, grid, st);
-  else launch_gate_nw<4>(a, grid, st);
+  const int epr = (a.E + 15) / 16;          // experts per lane of a 16-lane row
+  if (epr <= 1) launch_gate_epr<1>(a, grid, st);
+  else if (epr <= 2) launch_gate_epr<2>(a, grid, st);
+  else if (epr <= 4) launch_gate_epr<4>(a, grid, st);
+  else if (epr <= 8) launch_gate_epr<8>(a, grid, st);
+  else if (epr <= 16) launch_gate_epr<16>(a, grid, st);
+  else if (epr <= 32) launch_gate_epr<32>(a, grid, st);
+  else launch_gate_epr<64>(a, grid, st);
   return hipGetLastError();
 }
 
