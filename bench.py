@@ -254,13 +254,18 @@ def cpu_baseline(bench, n_sample):
 # ---------------------------------------------------------------------------
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "qwen3_ep_all128_T8192_gemm_gate_up_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "mixture_experts_layer_amd", "csrc", "ffn.hip")
+# every source the gate/up GEMM kernel is compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_amd", "csrc", f)
+                  for f in ("ffn.hip", "moe_device.h", "moe_kernels.h")]
 
 
 def kernel_source_sha256():
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def committed_traffic(workload, T):

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
       g += red[w * NACC * 4 * PITCH + base];
       if (SWIGLU) u += red[w * NACC * 4 * PITCH + base + 4 * PITCH];
     }
-    const float out = SWIGLU ? silu(g) * u : g;
+    const float out = SWIGLU ? silu_fast(g) * u : g;
     const size_t yi = (size_t)row * a.N_out + n0 + n;
     if (OUT_BF16) reinterpret_cast<bf16_t*>(a.Y)[yi] = f32_to_bf16(out);
     else reinterpret_cast<float*>(a.Y)[yi] = out;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
           float h[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            h[r] = silu(acc[mi][ni][4 * q + r]) * acc[mi][ni + HALF][4 * q + r];
+            h[r] = silu_fast(acc[mi][ni][4 * q + r]) * acc[mi][ni + HALF][4 * q + r];
           uint2 o = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
           *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.Y) + (size_t)row * a.N_out +
                                     col0 + 8 * q) = o;
@@ -519,8 +519,10 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc) {
   if (dt == 0) return 16;
   if (mean_rows >= 64 && ffn_tile_ok(H, I_loc))
     return mean_rows >= BIG_TILE_MIN_ROWS ? TileBig::TM : TileMed::TM;
-  if (mean_rows <= 16) return 16;
-  if (mean_rows <= 32) return 32;
+  // routed counts spread well past the mean, so the tile is sized for about
+  // twice the mean: an expert split over two tiles streams its weights twice
+  if (mean_rows <= 8) return 16;
+  if (mean_rows <= 16) return 32;
   return 64;
 }
 

@@ -47,6 +47,12 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// Hardware exp and reciprocal (about 1 ulp each): for epilogues whose result
+// is rounded to bfloat16 anyway.  Large negative z gives exp -> inf and
+// rcp -> 0, so the result tends to -0 as it should.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of n ints held in LDS (n <= 4 * blockDim.x,
