@@ -59,7 +59,10 @@ def test_route_worked_example():
     np.testing.assert_allclose(w[0], g["derived"]["softmax_then_topk_weights"], atol=1e-6)
 
 
-@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (128, 8), (256, 8), (300, 5), (8, 8)])
+# E covers every experts-per-lane width of the gating kernel (1 .. 64, staged
+# and unstaged logits); k > 16 uses the second choice slot of each lane
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (128, 8), (256, 8), (300, 5), (8, 8),
+                                 (32, 17), (256, 32), (512, 20), (1024, 32)])
 @pytest.mark.parametrize("mode", [0, 1, 2, 3])
 def test_route_modes_exact_ids(E, k, mode):
     r = np.random.default_rng(E * 10 + k + mode)
@@ -146,7 +149,8 @@ def test_permute_worked_example():
 
 @pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 130, 1000, 4097])
 @pytest.mark.parametrize("E,k,eb,ee", [(16, 4, 0, 16), (128, 8, 0, 128), (128, 8, 16, 32),
-                                       (256, 8, 200, 256), (8, 2, 3, 4)])
+                                       (256, 8, 200, 256), (8, 2, 3, 4), (1024, 32, 0, 1024),
+                                       (1024, 32, 512, 640)])
 def test_permute_exact(T, E, k, eb, ee):
     r = np.random.default_rng(T + E + k + eb)
     # skewed, distinct-per-token ids
@@ -242,6 +246,17 @@ def test_layer_small(name, H, I, E, T):
         s = 1.0 / H ** 0.5
         L.w13_shared = (torch.randn((2 * I, H), device=DEV) * s).to(torch.bfloat16)
         L.w2_shared = (torch.randn((H, I), device=DEV) * s).to(torch.bfloat16)
+    gl = GpuLayer(L)
+    check_layer(gl, gl.run(T), T)
+
+
+# the ABI's limits: many experts and k > 16 (gating with 4-wave tiles and
+# unstaged logits, two choice slots per lane)
+@pytest.mark.parametrize("E,k,T", [(512, 20, 1), (512, 20, 70), (1024, 32, 64), (1024, 32, 129)])
+def test_layer_many_experts(E, k, T):
+    import dataclasses
+    cfg = dataclasses.replace(W.CONFIGS["qwen3_ep_all128"], E=E, k=k)
+    L = W.make_layer(cfg, device=DEV, seed=7, T_max=T, H=256, I=64, E=E)
     gl = GpuLayer(L)
     check_layer(gl, gl.run(T), T)
 
