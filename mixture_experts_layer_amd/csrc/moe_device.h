@@ -54,6 +54,15 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// Workgroup barrier for LDS traffic: each wave's LDS operations have
+// completed when the others pass it.  __syncthreads() also drains every
+// outstanding global store of the wave (vmcnt(0)), a memory round trip that
+// the routing kernels -- which never read back what they store -- need not
+// pay at each of their barriers.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of n ints held in LDS (n <= 4 * blockDim.x,
 // blockDim.x a multiple of 64 and at most 1024).  `data` is replaced by its
@@ -77,7 +86,7 @@ __device__ inline int block_exclusive_scan(int* data, int n, int* tmp) {
     if (lane >= o) v += u;
   }
   if (lane == 63) tmp[wid] = v;
-  __syncthreads();
+  lds_barrier();
   int wbase = 0, total = 0;
   for (int w = 0; w < nw; ++w) {
     const int t = tmp[w];
@@ -91,7 +100,7 @@ __device__ inline int block_exclusive_scan(int* data, int n, int* tmp) {
       data[b + i] = run;
       run += x;
     }
-  __syncthreads();
+  lds_barrier();
   return total;
 }
 
@@ -115,7 +124,7 @@ __device__ inline void block_build_tile_map(const int* cnt, const int* off, int 
                                             int4* tile_map, int* n_tiles) {
   for (int e = threadIdx.x; e < E_loc; e += blockDim.x)
     scratch[e] = tiles_of(cnt[e], off[e], BM, max_rows);
-  __syncthreads();
+  lds_barrier();
   const int total = block_exclusive_scan(scratch, E_loc, tmp);
   for (int e = threadIdx.x; e < E_loc; e += blockDim.x) {
     const int nt = tiles_of(cnt[e], off[e], BM, max_rows);

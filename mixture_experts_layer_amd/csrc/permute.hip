@@ -48,10 +48,10 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __res
     s_cnt[el] = run;
     s_off[el] = run;
   }
-  __syncthreads();
+  lds_barrier();
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
   if (threadIdx.x == 0) s_off[E_loc] = total;
-  __syncthreads();
+  lds_barrier();
   for (int el = threadIdx.x; el < E_loc; el += blockDim.x) counts[el] = s_cnt[el];
   for (int el = threadIdx.x; el <= E_loc; el += blockDim.x) offsets[el] = s_off[el];
   if (tile_map)
@@ -102,9 +102,9 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
   __shared__ int s_scr[1024];
   __shared__ int s_tmp[257];
   for (int e = threadIdx.x; e <= E_loc; e += blockDim.x) s_off[e] = offsets[e];
-  __syncthreads();
+  lds_barrier();
   for (int e = threadIdx.x; e < E_loc; e += blockDim.x) s_cnt[e] = s_off[e + 1] - s_off[e];
-  __syncthreads();
+  lds_barrier();
   block_build_tile_map(s_cnt, s_off, E_loc, BM, max_rows, max_tiles, s_scr, s_tmp, tile_map,
                        n_tiles);
 }

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const Tin* __restrict_
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     if (lane == 0) red[wid][i] = v;
   }
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x < ntok) {
     const int i = threadIdx.x;
     float v = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
       } else {
         for (int i = threadIdx.x; i < nval; i += NT) s_logits[(i / E) * P + i % E] = src[i];
       }
-      __syncthreads();
+      lds_barrier();
     }
     const int row = lane >> 4, sub = lane & 15;
     for (int pass = 0; pass * NW * 4 < ntok; ++pass) {
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
   const int npair = ntok * k;
   // pad the id list to a multiple of 16 with an id no expert has
   for (int p = npair + threadIdx.x; p < ((npair + 15) & ~15); p += NT) s_ids[p] = -1;
-  __syncthreads();
+  lds_barrier();
 
   // atomic-free histogram and in-tile ranks, 16 ids per LDS read
   const int E_loc = a.e_end - a.e_begin;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
     }
     s_part[job] = c;
   }
-  __syncthreads();
+  lds_barrier();
   for (int job = threadIdx.x; job < C * E_loc; job += NT) {
     const int ch = job / E_loc, el = job - ch * E_loc, e = a.e_begin + el;
     int c = 0;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
         if (ids16[j] == e) s_rank[p + j] = c++;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   if (!a.single) {
     for (int el = threadIdx.x; el < E_loc; el += NT)
@@ -458,10 +458,10 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 
 // single tile: finish the permutation here
   for (int el = threadIdx.x; el < E_loc; el += NT) s_off[el] = s_cnt[el];
-  __syncthreads();
+  lds_barrier();
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
   if (threadIdx.x == 0) s_off[E_loc] = total;
-  __syncthreads();
+  lds_barrier();
   for (int el = threadIdx.x; el < E_loc; el += NT) a.counts[el] = s_cnt[el];
   for (int el = threadIdx.x; el <= E_loc; el += NT) a.offsets[el] = s_off[el];
   for (int p = threadIdx.x; p < npair; p += NT) {
