@@ -9,6 +9,8 @@
 // every block reads its (expert, row range) from a tile map built by the
 // routing kernels; blocks past the map's length exit at once.  Nothing is
 // read back to the host.
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -253,12 +255,17 @@ struct TileCfg {
   static constexpr int XLOADS = TM / RPI / NWAVE;   // load instructions per wave per stage
   static constexpr int WLOADS = TN / RPI / NWAVE;
   static constexpr int NLOADS = XLOADS + WLOADS;
+  // a tile holding at most TM/2 rows ("half" tile) loads only the x-load
+  // instructions of its first TM/2 rows
+  static constexpr int XLOADS_H = (TM / 2) / RPI / NWAVE;
+  static constexpr int NLOADS_H = XLOADS_H + WLOADS;
   static constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
   static constexpr int MFM = WTM / 32, MFN = WTN / 32;
   static constexpr int LDS = STAGES * SBYTES;
   static_assert(TM % (RPI * NWAVE) == 0 && TN % (RPI * NWAVE) == 0, "load split");
   static_assert(WTM % 32 == 0 && WTN % 64 == 0, "wave tile");
   static_assert(TK % 16 == 0, "k step");
+  static_assert((TM / 2) % (RPI * NWAVE) == 0 && WM == 2, "half tiles: x loads and waves split at TM/2");
 };
 
 template <class C>
@@ -344,12 +351,18 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
     wsrc[j] = We + (size_t)wrow * a.K + (pchunk ^ tile_swz<C>(rt)) * 8;
   }
 
-  auto issue = [&](int ks, int buf) {
+  // An expert's last tile is often at most half full: then the x rows of the
+  // upper half (padding) are not loaded and the waves that own them skip
+  // their LDS reads and MFMAs, leaving their SIMD's MFMA pipe to the other
+  // wave.  They still take part in the loads of weights and in every barrier.
+  const bool half = r1 - r0 <= C::TM / 2;
+  auto issue = [&](int ks, int buf, auto half_c) {
+    constexpr int XL = decltype(half_c)::value ? C::XLOADS_H : C::XLOADS;
     unsigned char* sx = smem + buf * C::SBYTES;
     unsigned char* sw = sx + C::XBYTES;
     const int ko = ks * C::TK;
 #pragma unroll
-    for (int j = 0; j < C::XLOADS; ++j)
+    for (int j = 0; j < XL; ++j)
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[j] + ko),
                                        (lds_void_t*)(sx + (wid + C::NWAVE * j) * 1024), 16, 0, 0);
 #pragma unroll
@@ -360,6 +373,7 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
 
   const int wm = wid / C::WN, wn = wid % C::WN;
   const int lrow = lane & 31;
+  const bool idle = half && wm * C::WTM >= C::TM / 2;
   const int khalf = lane >> 5;
   // weight-row bases of the wave's N subtiles inside the TN-row tile
   int nbase[C::MFN];
@@ -407,24 +421,31 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
     for (int ni = 0; ni < C::MFN; ++ni)
       wf[ni] = *reinterpret_cast<const bf16x8_t*>(sw + woff[ni] + ((c ^ wsw[ni]) * 16));
   };
+  // One stage loop, instantiated for full tiles, for the computing waves of
+  // half tiles and for their idle waves; the choice is made once per wave.
+  auto stage_loop = [&](auto half_c, auto compute_c) {
+  constexpr bool HALF = decltype(half_c)::value;
+  constexpr int NL = HALF ? C::NLOADS_H : C::NLOADS;
 #pragma unroll
   for (int s0 = 0; s0 < C::STAGES - 1; ++s0)
-    if (s0 < nk) issue(s0, s0);
+    if (s0 < nk) issue(s0, s0, half_c);
   for (int ks = 0; ks < nk; ++ks) {
     // Stage ks has landed for this wave once at most the loads of the
     // STAGES-2 younger stages are outstanding; the barrier makes that true
     // for every wave.  The fragments of the previous stage were consumed by
     // its MFMAs, so no LDS read of the buffer refilled below is in flight.
     // (A __syncthreads() here would also drain the younger stages.)
+    // (NL loads per stage: a half tile issues fewer)
     const int younger = min(nk - 1 - ks, C::STAGES - 2);
     switch (younger) {
       case 0: wait_stage_barrier<0>(); break;
-      case 1: wait_stage_barrier<C::NLOADS>(); break;
-      case 2: wait_stage_barrier<(C::STAGES > 3 ? 2 : 1) * C::NLOADS>(); break;
-      case 3: wait_stage_barrier<(C::STAGES > 4 ? 3 : 1) * C::NLOADS>(); break;
-      default: wait_stage_barrier<(C::STAGES > 5 ? 4 : 1) * C::NLOADS>(); break;
+      case 1: wait_stage_barrier<NL>(); break;
+      case 2: wait_stage_barrier<(C::STAGES > 3 ? 2 : 1) * NL>(); break;
+      case 3: wait_stage_barrier<(C::STAGES > 4 ? 3 : 1) * NL>(); break;
+      default: wait_stage_barrier<(C::STAGES > 5 ? 4 : 1) * NL>(); break;
     }
-    if (ks + C::STAGES - 1 < nk) issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES);
+    if (ks + C::STAGES - 1 < nk) issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES, half_c);
+    if constexpr (!decltype(compute_c)::value) continue;
     const unsigned char* sx = smem + (ks % C::STAGES) * C::SBYTES;
     const unsigned char* sw = sx + C::XBYTES;
     bf16x8_t xf[2][C::MFM], wf[2][C::MFN];
@@ -443,6 +464,10 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
                                                                 acc[mi][ni], 0, 0, 0);
     }
   }
+  };
+  if (!half) stage_loop(std::false_type{}, std::true_type{});
+  else if (!idle) stage_loop(std::true_type{}, std::true_type{});
+  else stage_loop(std::true_type{}, std::false_type{});
 
   // ---- epilogue
   using O = TileOut<C, SWIGLU, OUT_BF16>;
@@ -452,6 +477,7 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
     lds_barrier();
 #pragma unroll
     for (int mi = 0; mi < C::MFM; ++mi) {
+      if (idle) break;
       unsigned char* so = smem + (wm * C::WTM + mi * 32 + lrow) * O::PITCH;
       if (SWIGLU) {
         constexpr int HALF = C::MFN / 2;
