@@ -93,9 +93,11 @@ __device__ __forceinline__ int rt_swz(int r) { return (r >> 1) & 7; }
 template <int EW>
 __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wr, int T,
-                                                          int H, const float* __restrict__ bias,
+                                                          int H, int E_all,
+                                                          const float* __restrict__ bias,
                                                           float* __restrict__ logits) {
-  constexpr int E = 32 * EW;
+  constexpr int E = 32 * EW;                // experts of this block: e0 .. e0 + E - 1
+  const int e0 = blockIdx.y * E;
   constexpr int XB = RT_TOK * 128;          // token chunk bytes
   constexpr int WB = E * 128;               // W_r chunk bytes
   constexpr int SB = XB + WB;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 #pragma unroll
   for (int j = 0; j < EW; ++j) {
     const int rt = (wid + 4 * j) * 8 + prow;
-    wsrc[j] = wr + (size_t)rt * H + (pch ^ rt_swz(rt)) * 8;
+    wsrc[j] = wr + (size_t)(e0 + rt) * H + (pch ^ rt_swz(rt)) * 8;
   }
   auto issue = [&](int ks, int buf) {
     unsigned char* sx = smem + buf * SB;
@@ -165,18 +167,21 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
   if (t < T) {
 #pragma unroll
     for (int nb = 0; nb < E / 16; ++nb) {
-      const int e = nb * 16 + 4 * kq;
+      const int e = e0 + nb * 16 + 4 * kq;
       float4 v = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
       if (bias) {
         v.x += bias[e]; v.y += bias[e + 1]; v.z += bias[e + 2]; v.w += bias[e + 3];
       }
-      *reinterpret_cast<float4*>(logits + (size_t)t * E + e) = v;
+      *reinterpret_cast<float4*>(logits + (size_t)t * E_all + e) = v;
     }
   }
 }
 
+// Each block covers 64 tokens and 32*EW experts; E is split over the grid's
+// second dimension so that a large E gives more blocks (and each block a
+// smaller share of W_r to stream through LDS).
 template <int EW>
-static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, int H,
+static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, int H, int E,
                                      const float* bias, float* logits, hipStream_t st) {
   static bool attr_set = false;
   const int lds = RT_STAGES * (RT_TOK * 128 + 32 * EW * 128);
@@ -186,7 +191,8 @@ static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, i
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  router_mfma_kernel<EW><<<(T + RT_TOK - 1) / RT_TOK, 256, lds, st>>>(x, wr, T, H, bias, logits);
+  const dim3 grid((T + RT_TOK - 1) / RT_TOK, E / (32 * EW));
+  router_mfma_kernel<EW><<<grid, 256, lds, st>>>(x, wr, T, H, E, bias, logits);
   return hipGetLastError();
 }
 
@@ -484,8 +490,7 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,
                                 const float* bias, float* logits, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 &&
-                          (E == 32 || E == 64 || E == 128 || E == 256);
+  const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 && (E == 32 || E % 64 == 0);
   if (!mfma_shape) {
     dim3 grid(E, (T + 7) / 8);
     if (dt == 0)
@@ -498,12 +503,8 @@ hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, in
   }
   const bf16_t* xb = (const bf16_t*)x;
   const bf16_t* wb = (const bf16_t*)wr;
-  switch (E) {
-    case 32: return launch_router_mfma<1>(xb, wb, T, H, bias, logits, st);
-    case 64: return launch_router_mfma<2>(xb, wb, T, H, bias, logits, st);
-    case 128: return launch_router_mfma<4>(xb, wb, T, H, bias, logits, st);
-    default: return launch_router_mfma<8>(xb, wb, T, H, bias, logits, st);
-  }
+  if (E == 32) return launch_router_mfma<1>(xb, wb, T, H, E, bias, logits, st);
+  return launch_router_mfma<2>(xb, wb, T, H, E, bias, logits, st);
 }
 
 // E <= 256 (at most 16 experts per lane) stages the logits in LDS.
