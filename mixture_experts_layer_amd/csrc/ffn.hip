@@ -643,14 +643,11 @@ static bool is_tile_bm(int BM) { return BM == TileBig::TM || BM == TileMed::TM; 
 
 template <class C, bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, TileOut<C, SWIGLU, OUT_BF16>::LDS);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t err = ensure_lds_limit(
+      reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16>),
+      TileOut<C, SWIGLU, OUT_BF16>::LDS, lds_set);
+  if (err != hipSuccess) return err;
   const int ntn = a.N_out / (SWIGLU ? C::TN / 2 : C::TN);
   ffn_tile_kernel<C, SWIGLU, OUT_BF16>
       <<<max_tiles * ntn, C::NTHR, TileOut<C, SWIGLU, OUT_BF16>::LDS, st>>>(a);

@@ -1,9 +1,28 @@
 // Host-side launchers of the gfx950 kernels (internal to the library).
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
 #include <stdint.h>
 
 namespace moe {
+
+// Raise a kernel's dynamic-LDS limit on the current device, once per
+// (kernel, device): the attribute belongs to the device, so a process that
+// drives several GPUs sets it on each.  `done` holds one bit per device id
+// below 64 (higher ids set it on every launch); a lost race only repeats the
+// call.
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return err;
+}
 
 constexpr int TOK_TILE = 64;   // tokens per routing-metadata tile
 constexpr int KMAX = 32;       // largest supported top-k

@@ -118,7 +118,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 #pragma unroll
   for (int j = 0; j < EW; ++j) {
     const int rt = (wid + 4 * j) * 8 + prow;
-    wsrc[j] = wr + (size_t)(e0 + rt) * H + (pch ^ rt_swz(rt)) * 8;
+    // rows past E (a block covering the last E % 32 experts) read row E-1;
+    // their results are never stored
+    wsrc[j] = wr + (size_t)min(e0 + rt, E_all - 1) * H + (pch ^ rt_swz(rt)) * 8;
   }
   auto issue = [&](int ks, int buf) {
     unsigned char* sx = smem + buf * SB;
@@ -168,6 +170,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 #pragma unroll
     for (int nb = 0; nb < E / 16; ++nb) {
       const int e = e0 + nb * 16 + 4 * kq;
+      if (e >= E_all) continue;                 // E is a multiple of 4
       float4 v = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
       if (bias) {
         v.x += bias[e]; v.y += bias[e + 1]; v.z += bias[e + 2]; v.w += bias[e + 3];
@@ -179,19 +182,18 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 
 // Each block covers 64 tokens and 32*EW experts; E is split over the grid's
 // second dimension so that a large E gives more blocks (and each block a
-// smaller share of W_r to stream through LDS).
+// smaller share of W_r to stream through LDS).  EW = 2 when 64 divides E,
+// else EW = 1 with a partial last block (few experts: the tokens are still
+// read once, where a per-expert GEMV would read them E times).
 template <int EW>
 static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, int H, int E,
                                      const float* bias, float* logits, hipStream_t st) {
-  static bool attr_set = false;
+  static std::atomic<uint64_t> lds_set{0};
   const int lds = RT_STAGES * (RT_TOK * 128 + 32 * EW * 128);
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_mfma_kernel<EW>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
-  const dim3 grid((T + RT_TOK - 1) / RT_TOK, E / (32 * EW));
+  hipError_t err =
+      ensure_lds_limit(reinterpret_cast<const void*>(&router_mfma_kernel<EW>), lds, lds_set);
+  if (err != hipSuccess) return err;
+  const dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + 32 * EW - 1) / (32 * EW));
   router_mfma_kernel<EW><<<grid, 256, lds, st>>>(x, wr, T, H, E, bias, logits);
   return hipGetLastError();
 }
@@ -490,7 +492,8 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,
                                 const float* bias, float* logits, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 && (E == 32 || E % 64 == 0);
+  // bf16 prefill batches with E a multiple of 4 (16-byte logit stores)
+  const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 && E % 4 == 0;
   if (!mfma_shape) {
     dim3 grid(E, (T + 7) / 8);
     if (dt == 0)
@@ -503,8 +506,8 @@ hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, in
   }
   const bf16_t* xb = (const bf16_t*)x;
   const bf16_t* wb = (const bf16_t*)wr;
-  if (E == 32) return launch_router_mfma<1>(xb, wb, T, H, E, bias, logits, st);
-  return launch_router_mfma<2>(xb, wb, T, H, E, bias, logits, st);
+  if (E % 64 == 0) return launch_router_mfma<2>(xb, wb, T, H, E, bias, logits, st);
+  return launch_router_mfma<1>(xb, wb, T, H, E, bias, logits, st);
 }
 
 // E <= 256 (at most 16 experts per lane) stages the logits in LDS.

@@ -79,7 +79,8 @@ def test_route_modes_exact_ids(E, k, mode):
 
 
 @pytest.mark.parametrize("T", [1, 16, 33, 64, 300])
-@pytest.mark.parametrize("E,H", [(8, 512), (128, 4096), (256, 1024)])
+@pytest.mark.parametrize("E,H", [(8, 512), (128, 4096), (256, 1024), (20, 256), (96, 512),
+                                 (10, 256)])
 def test_router_logits_bf16(T, E, H):
     g = torch.Generator(device=DEV)
     g.manual_seed(T * 1000 + E)
