@@ -52,7 +52,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
   constexpr int BN = 16 * NT;
   constexpr int NACC = MT * NT * NS;
   constexpr int PITCH = 65;
-  constexpr int U = MT == 1 ? 8 : (MT == 2 ? 6 : 4);   // K steps per load batch
+  // K steps per load batch: about 24 16-byte loads in flight per wave
+  constexpr int LPS = NT * NS + MT;                     // loads per K step
+  constexpr int U = 24 / LPS < 2 ? 2 : (24 / LPS > 8 ? 8 : 24 / LPS);
   __shared__ float red[NW > 1 ? NW * NACC * 4 * PITCH : 1];
 
   const int n_ntiles = a.N_out / BN;
@@ -675,25 +677,34 @@ static int pick_nw(int steps, int max_nw, int batch) {
   return nw;
 }
 
-template <int MT, int NW, bool SWIGLU, bool OUT_BF16>
+template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_direct_t(const DirectArgs& a, int max_tiles, hipStream_t st) {
-  const int grid = max_tiles * (a.N_out / 16);
-  ffn_direct_kernel<MT, 1, NW, SWIGLU, OUT_BF16><<<grid, NW * 64, 0, st>>>(a);
+  const int grid = max_tiles * (a.N_out / (16 * NT));
+  ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16><<<grid, NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <int MT, int MAX_NW, bool SWIGLU, bool OUT_BF16>
+template <int MT, int NT, bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_direct_nw(const DirectArgs& a, int nw, int max_tiles, hipStream_t st) {
   switch (nw) {
-    case 1: return launch_direct_t<MT, 1, SWIGLU, OUT_BF16>(a, max_tiles, st);
-    case 2: return launch_direct_t<MT, 2, SWIGLU, OUT_BF16>(a, max_tiles, st);
-    case 4: return launch_direct_t<MT, 4, SWIGLU, OUT_BF16>(a, max_tiles, st);
-    default:
-      if constexpr (MAX_NW >= 16) {
-        if (nw >= 16) return launch_direct_t<MT, 16, SWIGLU, OUT_BF16>(a, max_tiles, st);
-      }
-      return launch_direct_t<MT, 8, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    case 1: return launch_direct_t<MT, NT, 1, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    case 2: return launch_direct_t<MT, NT, 2, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    case 4: return launch_direct_t<MT, NT, 4, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    default: return launch_direct_t<MT, NT, 8, SWIGLU, OUT_BF16>(a, max_tiles, st);
   }
+}
+
+// 16-column output tiles per block for each row tile (BM = 16, 32, 64).  With
+// 32 or 64 rows, two output tiles per wave share each activation fragment:
+// the activation loads had been as many as the weight loads, and halving
+// them ran the layer 14-15% faster at 16-32 rows per expert; with 16 rows
+// the extra registers cost more than the loads saved.
+constexpr int DIRECT_NT16 = 1, DIRECT_NT32 = 2, DIRECT_NT64 = 2;
+
+template <int MT, int NT, bool SWIGLU>
+constexpr int direct_batch() {
+  constexpr int lps = NT * (SWIGLU ? 2 : 1) + MT;
+  return 24 / lps < 2 ? 2 : (24 / lps > 8 ? 8 : 24 / lps);
 }
 
 template <bool SWIGLU, bool OUT_BF16>
@@ -702,9 +713,14 @@ static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, hipS
   // at most 8 waves, so two blocks share a CU: one block's LDS reduction and
   // stores overlap the other's weight loads (16-wave blocks left the CU's
   // loads idle during them; 8 ran the gate/up GEMM 9-11% faster)
-  if (BM == 16) return launch_direct_nw<1, 8, SWIGLU, OUT_BF16>(a, pick_nw(steps, 8, 8), max_tiles, st);
-  if (BM == 32) return launch_direct_nw<2, 8, SWIGLU, OUT_BF16>(a, pick_nw(steps, 8, 6), max_tiles, st);
-  return launch_direct_nw<4, 8, SWIGLU, OUT_BF16>(a, pick_nw(steps, 8, 4), max_tiles, st);
+  if (BM == 16)
+    return launch_direct_nw<1, DIRECT_NT16, SWIGLU, OUT_BF16>(
+        a, pick_nw(steps, 8, direct_batch<1, DIRECT_NT16, SWIGLU>()), max_tiles, st);
+  if (BM == 32)
+    return launch_direct_nw<2, DIRECT_NT32, SWIGLU, OUT_BF16>(
+        a, pick_nw(steps, 8, direct_batch<2, DIRECT_NT32, SWIGLU>()), max_tiles, st);
+  return launch_direct_nw<4, DIRECT_NT64, SWIGLU, OUT_BF16>(
+      a, pick_nw(steps, 8, direct_batch<4, DIRECT_NT64, SWIGLU>()), max_tiles, st);
 }
 
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {
