@@ -710,12 +710,17 @@ constexpr int direct_batch() {
 template <bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, hipStream_t st) {
   const int steps = a.K / 32;
-  // at most 8 waves, so two blocks share a CU: one block's LDS reduction and
-  // stores overlap the other's weight loads (16-wave blocks left the CU's
-  // loads idle during them; 8 ran the gate/up GEMM 9-11% faster)
+  // 16-row tiles: at most 8 waves, so two blocks share a CU: one block's LDS
+  // reduction and stores overlap the other's weight loads (16-wave blocks
+  // left the CU's loads idle during them; 8 ran the gate/up GEMM 9-11%
+  // faster).  Measured further: the gate/up GEMM over a long K (>= 192
+  // steps, e.g. H = 7168) ran 6% faster with 4 waves; the down projection
+  // 10-18% faster with 2 waves (longer per-wave streams, a cheaper
+  // reduction).
+  const int max_nw16 = SWIGLU ? (steps >= 192 ? 4 : 8) : 2;
   if (BM == 16)
     return launch_direct_nw<1, DIRECT_NT16, SWIGLU, OUT_BF16>(
-        a, pick_nw(steps, 8, direct_batch<1, DIRECT_NT16, SWIGLU>()), max_tiles, st);
+        a, pick_nw(steps, max_nw16, direct_batch<1, DIRECT_NT16, SWIGLU>()), max_tiles, st);
   if (BM == 32)
     return launch_direct_nw<2, DIRECT_NT32, SWIGLU, OUT_BF16>(
         a, pick_nw(steps, 8, direct_batch<2, DIRECT_NT32, SWIGLU>()), max_tiles, st);
