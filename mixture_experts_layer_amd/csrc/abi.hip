@@ -94,7 +94,8 @@ size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w) {
   const int eb = elt_bytes(d->dt);
   const int max_rows = T * (d->k < E_loc ? d->k : E_loc);
   const int n_tt = cdiv(T, TOK_TILE);
-  const int BM = ffn_row_tile(d->dt, mean_rows(T, d->k, d->E), d->H, d->I_loc);
+  const int BM = ffn_row_tile(d->dt, mean_rows(T, d->k, d->E), d->H, d->I_loc,
+                              T * d->k < E_loc ? T * d->k : E_loc);
   const int max_tiles = max_tiles_for(max_rows, E_loc, BM);
   Carver c(base);
   LayerWs l;
@@ -241,7 +242,8 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e
 
 size_t moe_grouped_ffn_workspace_size(int max_rows, int E_loc, int H, int I_loc, int dt) {
   if (max_rows < 0 || E_loc < 1 || H <= 0 || I_loc <= 0 || !valid_dt(dt)) return 0;
-  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc), H, I_loc);
+  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc), H, I_loc,
+                              max_rows < E_loc ? max_rows : E_loc);
   const int mt = max_tiles_for(max_rows, E_loc, BM);
   return align_up((size_t)max_rows * I_loc * elt_bytes(dt)) + align_up((size_t)mt * sizeof(int4)) +
          align_up(4);
@@ -265,7 +267,8 @@ int moe_grouped_ffn(const void* x_perm, const void* x, const int32_t* src_token,
   if (max_rows == 0) return MOE_OK;
   const size_t need = moe_grouped_ffn_workspace_size(max_rows, E_loc, H, I_loc, dt);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc), H, I_loc);
+  const int BM = ffn_row_tile(dt, cdiv(max_rows, E_loc), H, I_loc,
+                              max_rows < E_loc ? max_rows : E_loc);
   const int mt = max_tiles_for(max_rows, E_loc, BM);
   Carver c(ws);
   void* h = c.take<char>((size_t)max_rows * I_loc * elt_bytes(dt));
@@ -372,7 +375,7 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
   MOE_TRY(mark(3));
   // a8: shared expert over every token
   if (d->I_shared > 0) {
-    const int BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared);
+    const int BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared, 1);
     FfnArgs g{};
     g.x = x; g.src_token = nullptr; g.tile_map = nullptr; g.n_tiles = nullptr;
     g.M_dense = T; g.max_tiles = cdiv(T, BMs); g.mean_rows = T;

@@ -630,10 +630,24 @@ bool ffn_tile_ok(int H, int I_loc) {
   return H % TL_K == 0 && H % TL_N == 0 && I_loc % TL_K == 0 && I_loc % (TL_N / 2) == 0;
 }
 
-int ffn_row_tile(int dt, int mean_rows, int H, int I_loc) {
+int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
   if (dt == 0) return 16;
-  if (mean_rows >= 64 && ffn_tile_ok(H, I_loc))
-    return mean_rows >= BIG_TILE_MIN_ROWS ? TileBig::TM : TileMed::TM;
+  if (ffn_tile_ok(H, I_loc)) {
+    if (mean_rows >= 64) return mean_rows >= BIG_TILE_MIN_ROWS ? TileBig::TM : TileMed::TM;
+    // From a few rows per expert up, the LDS-tiled kernel streams each
+    // expert's weights faster than the direct kernel (its 256-row weight
+    // tiles move in 1 KB contiguous loads shared by all 8 waves; a mostly
+    // empty tile skips its padding's work): 3-35% per layer at 4-48 rows per
+    // expert, and from 2 rows with a long contraction (H >= 6144), where the
+    // direct kernel's per-wave streams fall further behind.  The condition:
+    // 16 rows per expert, or enough down-projection blocks (one per 128-row
+    // tile and 256 columns) to cover the 256 CUs -- with few experts (8) and
+    // a handful of rows each the direct kernel stays ahead.
+    const int min_rows = H >= 6144 ? 2 : 4;
+    const long long blocks = (long long)experts * ((mean_rows + TileMed::TM - 1) / TileMed::TM) *
+                             (H / TileMed::TN);
+    if (mean_rows >= min_rows && (blocks >= 256 || mean_rows >= 16)) return TileMed::TM;
+  }
   // routed counts spread well past the mean, so the tile is sized for about
   // twice the mean: an expert split over two tiles streams its weights twice
   if (mean_rows <= 8) return 16;

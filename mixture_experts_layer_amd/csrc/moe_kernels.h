@@ -87,7 +87,10 @@ struct FfnArgs {
   void* y;                  // [rows][H], dtype y_dt
   int dt, y_dt;
 };
-int ffn_row_tile(int dt, int mean_rows, int H, int I_loc);
+// Row tile of the expert GEMMs: 16/32/64 (direct kernel) or 128/256 (LDS-
+// tiled kernel), from the expected rows per expert and the number of experts
+// the rows spread over.
+int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts);
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st);
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st);
