@@ -568,6 +568,10 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
 // 128-row tiles, which waste less on each expert's partial last tile.
 using TileBig = TileCfg<256, 256, 64, 2, 2, 4, 1>;
 using TileMed = TileCfg<128, 256, 64, 3, 2, 4, 1>;
+// gate/up with an output width that is a multiple of 64 but not of 128 (a
+// tensor-parallel share such as 1536 / 8 = 192): 64 gate + 64 up rows per
+// tile, four waves of 64 x 64
+using TileNarrow = TileCfg<128, 128, 64, 3, 2, 2, 1>;
 constexpr int BIG_TILE_MIN_ROWS = 384;
 static_assert(TileBig::TN == TileMed::TN && TileBig::TK == TileMed::TK, "shared shape limits");
 constexpr int TL_N = TileMed::TN, TL_K = TileMed::TK;
@@ -627,13 +631,15 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(F32Args a) {
 // host side
 // ---------------------------------------------------------------------------
 bool ffn_tile_ok(int H, int I_loc) {
-  return H % TL_K == 0 && H % TL_N == 0 && I_loc % TL_K == 0 && I_loc % (TL_N / 2) == 0;
+  return H % TL_K == 0 && H % TL_N == 0 && I_loc % TL_K == 0 && I_loc % (TileNarrow::TN / 2) == 0;
 }
 
 int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
   if (dt == 0) return 16;
   if (ffn_tile_ok(H, I_loc)) {
-    if (mean_rows >= 64) return mean_rows >= BIG_TILE_MIN_ROWS ? TileBig::TM : TileMed::TM;
+    // (256-row tiles need gate/up widths that are multiples of 128)
+    if (mean_rows >= 64)
+      return mean_rows >= BIG_TILE_MIN_ROWS && I_loc % (TL_N / 2) == 0 ? TileBig::TM : TileMed::TM;
     // From a few rows per expert up, the LDS-tiled kernel streams each
     // expert's weights faster than the direct kernel (its 256-row weight
     // tiles move in 1 KB contiguous loads shared by all 8 waves; a mostly
@@ -643,7 +649,9 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
     // 16 rows per expert, or enough down-projection blocks (one per 128-row
     // tile and 256 columns) to cover the 256 CUs -- with few experts (8) and
     // a handful of rows each the direct kernel stays ahead.
-    const int min_rows = H >= 6144 ? 2 : 4;
+    // (narrow gate/up tiles -- widths not a multiple of 128 -- run one wave
+    // per SIMD and only pay from 16 rows per expert)
+    const int min_rows = I_loc % (TL_N / 2) != 0 ? 16 : (H >= 6144 ? 2 : 4);
     const long long blocks = (long long)experts * ((mean_rows + TileMed::TM - 1) / TileMed::TM) *
                              (H / TileMed::TN);
     if (mean_rows >= min_rows && (blocks >= 256 || mean_rows >= 16)) return TileMed::TM;
@@ -680,6 +688,9 @@ static hipError_t launch_tile(TileArgs a, int BM, int mean_rows, int max_tiles, 
   const int ntn = a.N_out / (SWIGLU ? TL_N / 2 : TL_N);
   a.group = tile_group(mean_rows, BM, ntn);
   if (BM == TileBig::TM) return launch_tile_cfg<TileBig, SWIGLU, OUT_BF16>(a, max_tiles, st);
+  if constexpr (SWIGLU) {
+    if (a.N_out % (TL_N / 2) != 0) return launch_tile_cfg<TileNarrow, SWIGLU, OUT_BF16>(a, max_tiles, st);
+  }
   return launch_tile_cfg<TileMed, SWIGLU, OUT_BF16>(a, max_tiles, st);
 }
 

@@ -269,6 +269,7 @@ TILE = [
     ("mixtral_8x7b", 512, 384, 8, 1000),
     ("qwen3_ep_all128", 256, 128, 16, 1111),
     ("deepseek_v3", 512, 256, 32, 700),
+    ("qwen3_ep_all128", 512, 192, 16, 700),     # gate/up width 192: 64-column tiles
 ]
 
 
