@@ -283,6 +283,8 @@ int moe_grouped_ffn(const void* x_perm, const void* x, const int32_t* src_token,
   a.mean_rows = cdiv(max_rows, E_loc);
   a.H = H; a.I_loc = I_loc; a.w13 = w13; a.w2 = w2; a.h = h; a.y = y_perm;
   a.dt = dt; a.y_dt = y_dt;
+  a.x_rows = x_perm ? max_rows : 0;     // the token count behind src_token is not passed
+  a.h_rows = max_rows;
   return hip_status(launch_grouped_ffn(a, BM, s));
 }
 
@@ -369,6 +371,7 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
   f.M_dense = 0; f.max_tiles = l.max_tiles; f.mean_rows = mean_rows(T, d->k, d->E);
   f.H = d->H; f.I_loc = d->I_loc; f.w13 = d->w13; f.w2 = d->w2;
   f.h = l.h; f.y = l.y_perm; f.dt = d->dt; f.y_dt = d->dt;
+  f.x_rows = T; f.h_rows = l.max_rows;
   MOE_TRY(launch_ffn_gate_up(f, l.BM, s));
   MOE_TRY(mark(2));
   MOE_TRY(launch_ffn_down(f, l.BM, s));
@@ -381,6 +384,7 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
     g.M_dense = T; g.max_tiles = cdiv(T, BMs); g.mean_rows = T;
     g.H = d->H; g.I_loc = d->I_shared; g.w13 = d->w13_shared; g.w2 = d->w2_shared;
     g.h = l.h_s; g.y = l.y_s; g.dt = d->dt; g.y_dt = d->dt;
+    g.x_rows = T; g.h_rows = T;
     MOE_TRY(launch_grouped_ffn(g, BMs, s));
   }
   MOE_TRY(mark(4));

@@ -242,6 +242,7 @@ struct TileArgs {
   int up_off;
   void* Y;
   int group;                // N-tiles per group
+  long long x_bytes;        // extent of X in bytes (buffer-load path)
 };
 
 template <int TM_, int TN_, int TK_, int STAGES_, int WM_, int WN_, int MINB_>
@@ -259,7 +260,8 @@ struct TileCfg {
   static constexpr int NLOADS = XLOADS + WLOADS;
   // a tile holding at most TM/2 rows ("half" tile) loads only the x-load
   // instructions of its first TM/2 rows
-  static constexpr int XLOADS_H = (TM / 2) / RPI / NWAVE;
+  static constexpr bool HALF_OK = (TM / 2) % (RPI * NWAVE) == 0 && WM == 2;
+  static constexpr int XLOADS_H = HALF_OK ? (TM / 2) / RPI / NWAVE : XLOADS;
   static constexpr int NLOADS_H = XLOADS_H + WLOADS;
   static constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
   static constexpr int MFM = WTM / 32, MFN = WTN / 32;
@@ -267,8 +269,21 @@ struct TileCfg {
   static_assert(TM % (RPI * NWAVE) == 0 && TN % (RPI * NWAVE) == 0, "load split");
   static_assert(WTM % 32 == 0 && WTN % 64 == 0, "wave tile");
   static_assert(TK % 16 == 0, "k step");
-  static_assert((TM / 2) % (RPI * NWAVE) == 0 && WM == 2, "half tiles: x loads and waves split at TM/2");
 };
+
+
+// 16 bytes per lane from base + voff + soff into LDS at lds + 16 * lane, as a
+// raw-buffer load of a buffer of nbytes: the address is a scalar base, one
+// 32-bit lane offset and a scalar step, so a load costs no vector
+// instructions; bytes past nbytes read as zero.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t nbytes, void* lds,
+                                                  uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+#endif
+}
 
 template <class C>
 __device__ __forceinline__ int tile_swz(int r) { return (r / C::RP256) % C::CPR; }
@@ -296,7 +311,9 @@ struct TileOut {
   static_assert(LDS <= 160 * 1024, "LDS per block");
 };
 
-template <class C, bool SWIGLU, bool OUT_BF16>
+// BUF: operands reach LDS by raw-buffer loads (X and each expert's weights
+// within 4 GiB); otherwise by global loads from 64-bit per-lane pointers.
+template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
 __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -357,20 +374,45 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
   // upper half (padding) are not loaded and the waves that own them skip
   // their LDS reads and MFMAs, leaving their SIMD's MFMA pipe to the other
   // wave.  They still take part in the loads of weights and in every barrier.
-  const bool half = r1 - r0 <= C::TM / 2;
+  const bool half = C::HALF_OK && r1 - r0 <= C::TM / 2;
+  // buffer path: byte offsets of the same addresses from the buffers' bases
+  uint32_t xo[C::XLOADS], wo[C::WLOADS];
+  if constexpr (BUF) {
+#pragma unroll
+    for (int j = 0; j < C::XLOADS; ++j)
+      xo[j] = (uint32_t)(reinterpret_cast<const unsigned char*>(xsrc[j]) -
+                         reinterpret_cast<const unsigned char*>(a.X));
+#pragma unroll
+    for (int j = 0; j < C::WLOADS; ++j)
+      wo[j] = (uint32_t)(reinterpret_cast<const unsigned char*>(wsrc[j]) -
+                         reinterpret_cast<const unsigned char*>(We));
+  }
+  const uint32_t x_nbytes = (uint32_t)a.x_bytes;
+  const uint32_t w_nbytes = (uint32_t)(a.w_stride * 2);
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
   auto issue = [&](int ks, int buf, auto half_c) {
     constexpr int XL = decltype(half_c)::value ? C::XLOADS_H : C::XLOADS;
     unsigned char* sx = smem + buf * C::SBYTES;
     unsigned char* sw = sx + C::XBYTES;
-    const int ko = ks * C::TK;
+    if constexpr (BUF) {
+      const uint32_t soff = (uint32_t)ks * (C::TK * 2);
 #pragma unroll
-    for (int j = 0; j < XL; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[j] + ko),
-                                       (lds_void_t*)(sx + (wid + C::NWAVE * j) * 1024), 16, 0, 0);
+      for (int j = 0; j < XL; ++j)
+        buffer_load_lds16(a.X, x_nbytes, sx + (wid_u + C::NWAVE * j) * 1024, xo[j], soff);
 #pragma unroll
-    for (int j = 0; j < C::WLOADS; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[j] + ko),
-                                       (lds_void_t*)(sw + (wid + C::NWAVE * j) * 1024), 16, 0, 0);
+      for (int j = 0; j < C::WLOADS; ++j)
+        buffer_load_lds16(We, w_nbytes, sw + (wid_u + C::NWAVE * j) * 1024, wo[j], soff);
+    } else {
+      const int ko = ks * C::TK;
+#pragma unroll
+      for (int j = 0; j < XL; ++j)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[j] + ko),
+                                         (lds_void_t*)(sx + (wid_u + C::NWAVE * j) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int j = 0; j < C::WLOADS; ++j)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[j] + ko),
+                                         (lds_void_t*)(sw + (wid_u + C::NWAVE * j) * 1024), 16, 0, 0);
+    }
   };
 
   const int wm = wid / C::WN, wn = wid % C::WN;
@@ -665,17 +707,27 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
 
 static bool is_tile_bm(int BM) { return BM == TileBig::TM || BM == TileMed::TM; }
 
-template <class C, bool SWIGLU, bool OUT_BF16>
-static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, hipStream_t st) {
+template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
+static hipError_t launch_tile_buf(const TileArgs& a, int max_tiles, hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t err = ensure_lds_limit(
-      reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16>),
+      reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF>),
       TileOut<C, SWIGLU, OUT_BF16>::LDS, lds_set);
   if (err != hipSuccess) return err;
   const int ntn = a.N_out / (SWIGLU ? C::TN / 2 : C::TN);
-  ffn_tile_kernel<C, SWIGLU, OUT_BF16>
+  ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF>
       <<<max_tiles * ntn, C::NTHR, TileOut<C, SWIGLU, OUT_BF16>::LDS, st>>>(a);
   return hipGetLastError();
+}
+
+// Raw-buffer loads (no vector address arithmetic per load: the gate/up GEMM
+// ran 7-9% faster) whenever X's extent is known and X and one expert's
+// weights each fit the 32-bit buffer range.
+template <class C, bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, hipStream_t st) {
+  const bool buf = a.x_bytes > 0 && a.x_bytes <= 0xffffffffLL && a.w_stride * 2 <= 0xffffffffLL;
+  if (buf) return launch_tile_buf<C, SWIGLU, OUT_BF16, true>(a, max_tiles, st);
+  return launch_tile_buf<C, SWIGLU, OUT_BF16, false>(a, max_tiles, st);
 }
 
 // N-tiles per group.  One N-tile per group (all M-tiles of an expert that
@@ -767,7 +819,8 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {
   }
   if (is_tile_bm(BM)) {
     TileArgs t{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
-               (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h, 1};
+               (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h, 1,
+               a.x_rows * a.H * 2};
     return launch_tile<true, true>(t, BM, a.mean_rows, a.max_tiles, st);
   }
   DirectArgs g1{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
@@ -785,7 +838,8 @@ hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st) {
   }
   if (is_tile_bm(BM)) {
     TileArgs t{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
-               (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y, 1};
+               (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y, 1,
+               a.h_rows * a.I_loc * 2};
     if (a.y_dt == 0) return launch_tile<false, false>(t, BM, a.mean_rows, a.max_tiles, st);
     return launch_tile<false, true>(t, BM, a.mean_rows, a.max_tiles, st);
   }

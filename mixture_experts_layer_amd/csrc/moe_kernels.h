@@ -86,6 +86,8 @@ struct FfnArgs {
   void* h;                  // [rows][I_loc], dtype dt
   void* y;                  // [rows][H], dtype y_dt
   int dt, y_dt;
+  long long x_rows;         // rows of x (0: not known)
+  long long h_rows;         // rows of h
 };
 // Row tile of the expert GEMMs: 16/32/64 (direct kernel) or 128/256 (LDS-
 // tiled kernel), from the expected rows per expert and the number of experts
