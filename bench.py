@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="qwen3_ep_all128", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--T", type=int, default=None, help="tokens per step (default: largest of the workload)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies to rotate over")
+    ap.add_argument("--path", default="auto", choices=["auto", "staged", "decode"],
+                    help="layer entry point: moe_layer (auto), moe_layer_staged, moe_layer_decode")
     ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
     ap.add_argument("--sweep-workloads", default="qwen3_ep_all128,qwen3_tp8_rank0",
                     help="workloads whose token counts are swept (comma list)")
@@ -89,12 +91,16 @@ def roofs(cfg):
 # GPU setup
 # ---------------------------------------------------------------------------
 
+LAYER_FN = {"auto": "moe_layer", "staged": "moe_layer_staged", "decode": "moe_layer_decode"}
+
+
 class Bench:
-    def __init__(self, name, T_max, copies):
+    def __init__(self, name, T_max, copies, path="auto"):
         import torch
         import mixture_experts_layer_amd as M
         import workloads as W
         self.torch, self.M, self.W = torch, M, W
+        self.layer_fn = getattr(M, LAYER_FN[path])
         self.cfg = cfg = W.CONFIGS[name]
         L = W.make_layer(cfg, device="cuda", seed=0, T_max=T_max)
         w13, w2 = W.share_weights(L.w13, L.w2, cfg.tp_P, cfg.tp_rank)
@@ -114,8 +120,8 @@ class Bench:
                              I_shared=cfg.I_shared, w13_shared=L.w13_shared,
                              w2_shared=L.w2_shared, logit_bias=L.logit_bias, sel_bias=L.sel_bias)
             self.layers.append((d, a, b, r))
-        self.ws_bytes = M.moe_layer_workspace_size(self.layers[0][0], T_max)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.ws = M.layer_workspace(self.layers[0][0], T_max)
+        self.ws_bytes = self.ws.numel()
         self.y_full = torch.empty((T_max, cfg.H), dtype=L.x.dtype, device="cuda")
         self.set_T(T_max)
         torch.cuda.synchronize()
@@ -130,13 +136,19 @@ class Bench:
         E_loc = self.cfg.E_loc
         counts = torch.empty((E_loc,), dtype=torch.int32, device="cuda")
         dbg = M.debug_out(counts=counts)
-        M.moe_layer(self.layers[0][0], self.T, self.x, self.y, self.ws, self.ws_bytes, dbg)
+        self.layer_fn(self.layers[0][0], self.T, self.x, self.y, self.ws, self.ws_bytes, dbg)
         torch.cuda.synchronize()
         return counts.cpu().tolist()
 
+    def path_of(self, T):
+        """The path the timed entry point takes at T ("decode" or "staged")."""
+        if self.layer_fn is self.M.moe_layer:
+            return self.M.moe_layer_path(self.layers[0][0], T)
+        return "decode" if self.layer_fn is self.M.moe_layer_decode else "staged"
+
     def step(self, i, dbg=None):
         d = self.layers[i % self.copies][0]
-        self.M.moe_layer(d, self.T, self.x, self.y, self.ws, self.ws_bytes, dbg)
+        self.layer_fn(d, self.T, self.x, self.y, self.ws, self.ws_bytes, dbg)
 
     def timed_eager(self, steps, warmup):
         """Exactly `steps` eager layer calls; every call records the six stage
@@ -193,6 +205,19 @@ def roofline_entry(cfg, work, t_g1_ms):
     ach = work["g1_bytes"] / (t_g1_ms * 1e-3) / 1e9
     return dict(bound="hbm", achieved=round(ach, 1), peak=hbm, unit="GB/s",
                 frac=round(ach / hbm, 4), traffic=None)
+
+
+def decode_roofline_entry(cfg, work, t_ms):
+    """Roofline of the single-launch decode kernel: the whole layer's
+    algorithmic bytes (or FLOPs, past the ridge) over the kernel's time."""
+    hbm, mfma = roofs(cfg)
+    if work["b_alg"] / (hbm * 1e9) >= work["f_alg"] / (mfma * 1e12):
+        ach = work["b_alg"] / (t_ms * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=round(ach, 1), peak=hbm, unit="GB/s",
+                    frac=round(ach / hbm, 4), traffic=None)
+    ach = work["f_alg"] / (t_ms * 1e-3) / 1e12
+    return dict(bound="mfma", achieved=round(ach, 2), peak=mfma, unit="TFLOP/s",
+                frac=round(ach / mfma, 4), traffic=None)
 
 
 def layer_roof_frac(cfg, work, ms):
@@ -313,16 +338,27 @@ def main():
     cfg = W.CONFIGS[args.workload]
     T = args.T or cfg.T_max
 
-    bench = Bench(args.workload, T, args.copies)
+    bench = Bench(args.workload, T, args.copies, args.path)
     counts = bench.counts()
     work = layer_work(cfg, T, counts, bench.I_loc, bench.elt)
     ms, split = bench.timed_eager(args.steps, args.warmup)
-    roof = roofline_entry(cfg, work, split["gemm_gate_up"])
-    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (moe_layer stage events 1 -> 2)"
-    roof["traffic"] = committed_traffic(WORKLOAD_NAMES[args.workload], T)
-    roof["algorithmic_bytes"] = work["g1_bytes"]
-    roof["avg_launch_ms"] = round(split["gemm_gate_up"], 4)
+    path = bench.path_of(T)
     l_bound, t_roof_ms, l_frac = layer_roof_frac(cfg, work, ms)
+    if path == "decode":
+        # one launch covers the whole layer, between stage events 0 and 1
+        # (events 1-5 are recorded back to back after it)
+        t_k = split["route_permute"]
+        roof = decode_roofline_entry(cfg, work, t_k)
+        roof["kernel"] = "single-launch decode kernel (moe_layer stage events 0 -> 1)"
+        roof["traffic"] = None
+        roof["algorithmic_bytes"] = work["b_alg"]
+        roof["avg_launch_ms"] = round(t_k, 4)
+    else:
+        roof = roofline_entry(cfg, work, split["gemm_gate_up"])
+        roof["kernel"] = "grouped gate/up GEMM + SwiGLU (moe_layer stage events 1 -> 2)"
+        roof["traffic"] = committed_traffic(WORKLOAD_NAMES[args.workload], T)
+        roof["algorithmic_bytes"] = work["g1_bytes"]
+        roof["avg_launch_ms"] = round(split["gemm_gate_up"], 4)
     ms_graph = bench.timed_graph(args.steps, args.warmup)
 
     sweep = []
@@ -332,13 +368,14 @@ def main():
             Ts = [T2 for T2 in c2.T_list if not (name == args.workload and T2 == T)]
             if not Ts:
                 continue
-            b2 = bench if name == args.workload else Bench(name, max(Ts), None)
+            b2 = bench if name == args.workload else Bench(name, max(Ts), None, args.path)
             for T2 in Ts:
                 b2.set_T(T2)
                 w2k = layer_work(c2, T2, b2.counts(), b2.I_loc, b2.elt)
                 ms2 = b2.timed_graph(max(args.steps, 20), args.warmup)
                 bd, tr, fr = layer_roof_frac(c2, w2k, ms2)
-                sweep.append(dict(workload=WORKLOAD_NAMES[name], T=T2, ms=round(ms2, 4),
+                sweep.append(dict(workload=WORKLOAD_NAMES[name], T=T2, path=b2.path_of(T2),
+                                  ms=round(ms2, 4),
                                   tokens_per_s=round(T2 / (ms2 * 1e-3), 1), bound=bd,
                                   roofline_ms=round(tr, 4), frac=round(fr, 4),
                                   touched_experts=w2k["touched"]))
@@ -370,7 +407,8 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.workload], "T": T, "H": cfg.H,
                    "I_loc": bench.I_loc, "E": cfg.E, "k": cfg.k, "gating_mode": cfg.mode,
                    "I_shared": cfg.I_shared, "weight_copies": bench.copies,
-                   "parallelism": "single-gpu share"},
+                   "parallelism": "single-gpu share", "entry_point": LAYER_FN[args.path],
+                "path": path},
         "roofline": roof,
         "layer_roofline": {"bound": l_bound, "t_roof_ms": round(t_roof_ms, 4),
                            "frac": round(l_frac, 4), "b_alg_bytes": work["b_alg"],

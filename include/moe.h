@@ -18,7 +18,9 @@
  * ---------------------------------------
  * - Pointers named x, w_*, y*, logits, topk_*, counts, offsets, src_token,
  *   dst_row, ws are DEVICE pointers; the caller owns every buffer.  The
- *   library never allocates or frees memory and keeps no state between calls.
+ *   library never allocates or frees memory and keeps no state of its own
+ *   between calls (the layer workspace's synchronisation block, below, lives
+ *   in the caller's buffer).
  * - Every device pointer must be 16-byte aligned.  Matrices are row-major with
  *   the contraction (K) dimension contiguous:
  *     x[T][H], w_router[E][H], w13[e][2*I_loc][H], w2[e][H][I_loc].
@@ -36,7 +38,8 @@
  * - Shape limits: 1 <= k <= 32, k <= E <= 1024, H and I_loc multiples of 32.
  *   Other shapes return MOE_ERR_UNSUPPORTED.
  * - Results are bitwise repeatable: no kernel uses atomics to combine
- *   floating-point values or to order rows.
+ *   floating-point values or to order rows (the decode path's atomics only
+ *   count finished work).
  * - Inference is dropless: every (token, slot) pair routed to a local expert
  *   is computed ([CS349D L8] section 1.4).
  * - Non-finite inputs are outside the contract.
@@ -219,10 +222,54 @@ typedef struct {
   void* stage_events[MOE_STAGE_EVENTS];
 } moe_debug_out;
 
-/* Workspace bytes for moe_layer with up to T_max tokens (0 on invalid desc). */
+/* Workspace bytes for moe_layer, moe_layer_decode and moe_layer_staged with
+ * up to T_max tokens (0 on invalid desc).
+ *
+ * The workspace starts with a 132 KiB synchronisation block (4 KiB of
+ * counters, then one 128-byte flag line per workgroup) that the single-launch
+ * decode path keeps between calls: ZERO IT ONCE (e.g. zero the whole
+ * workspace) before the first call that uses the workspace.  Every call
+ * leaves it valid for the next; the staged path never touches it.  Calls that
+ * share a workspace must be ordered (one stream, or events), as for any
+ * scratch buffer.  Bytes 4..7 hold an int32 error word that the decode path
+ * sets (bit 0: the router wait, bit 1: an expert wait) if a wait for another
+ * workgroup exceeds its bound -- a grid that could not be resident at once;
+ * that call's outputs are then undefined.  It stays set until the caller
+ * clears it. */
 size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max);
+
+/* The layer share, choosing the single-launch decode path (moe_layer_decode)
+ * for shapes it supports while the expert weights the call can touch
+ * (min(E_loc, T*k) routed experts plus the shared one, bf16) are at most
+ * 512 MB, and the staged path (moe_layer_staged) otherwise.  Both compute the same function; they
+ * differ in rounding only (the staged path rounds each expert's output to
+ * dtype dt before the combine, the decode path keeps it in float32). */
 int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y,
               void* ws, size_t ws_bytes, moe_debug_out* dbg, void* stream);
+
+/* Which path moe_layer takes for this description and T: 0 staged, 1 the
+ * single-launch decode path; negative (a moe_status, negated) for an invalid
+ * description or T < 0. */
+int moe_layer_path(const moe_layer_desc* d, int T);
+
+/* Staged path: one launch per step (router, gating + metadata, gate/up GEMM,
+ * down GEMM, shared expert, combine), any supported shape and T. */
+int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y,
+                     void* ws, size_t ws_bytes, moe_debug_out* dbg, void* stream);
+
+/* Single-launch decode path: router, gating, dispatch metadata, both expert
+ * GEMMs, the shared expert and the combine in ONE kernel launch whose
+ * workgroups hand work to one another through counters in the workspace's
+ * synchronisation block ([CS349D L8] section 6: a persistent kernel with
+ * device-side dependencies, for the launch and dependency floor of small
+ * decode batches).  Same arguments, results and debug copies as moe_layer;
+ * stage_events 1-5 are all recorded after the one launch.
+ * Supported: dt = MOE_BF16, 1 <= T <= 64, E <= 256, E_loc <= 256, k <= 16,
+ * T * k <= 512; otherwise MOE_ERR_UNSUPPORTED.  The grid is sized so that
+ * all its workgroups can be resident together (one per CU); a concurrent
+ * kernel delays it but cannot deadlock it. */
+int moe_layer_decode(const moe_layer_desc* d, int T, const void* x, void* y,
+                     void* ws, size_t ws_bytes, moe_debug_out* dbg, void* stream);
 
 #ifdef __cplusplus
 }

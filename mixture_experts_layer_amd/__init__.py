@@ -14,12 +14,14 @@ import os
 
 from ._abi import (MOE_F32, MOE_BF16, MOE_OK, GATE_TOPK_SOFTMAX, GATE_SOFTMAX_TOPK,  # noqa: F401
                    GATE_SOFTMAX_TOPK_RENORM, GATE_SIGMOID_BIAS_RENORM, MoELayerDesc, MoEDebugOut,
-                   EXPORTED_SYMBOLS, lib_path, load_library)
+                   EXPORTED_SYMBOLS, LAYER_SYNC_BYTES, lib_path, load_library)
 
 __all__ = [
     "MoEError", "lib", "get_lib", "moe_abi_version", "moe_status_str", "moe_route", "moe_permute",
     "moe_permute_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
-    "moe_combine", "moe_layer", "moe_layer_workspace_size", "layer_desc", "dtype_code",
+    "moe_combine", "moe_layer", "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
+    "moe_layer_workspace_size",
+    "layer_workspace", "layer_desc", "dtype_code", "LAYER_SYNC_BYTES",
     "MoELayerDesc", "MoEDebugOut",
 ]
 
@@ -141,6 +143,38 @@ def moe_layer(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut | None
     _check("moe_layer", lib.moe_layer(ctypes.byref(desc), T, _p(x), _p(y), _p(ws), ws_bytes,
                                       None if dbg is None else ctypes.byref(dbg),
                                       _stream(stream)))
+
+
+def moe_layer_path(desc: MoELayerDesc, T: int) -> str:
+    """"decode" or "staged": the path moe_layer takes for this call."""
+    r = lib.moe_layer_path(ctypes.byref(desc), T)
+    if r < 0:
+        raise MoEError("moe_layer_path", -r)
+    return "decode" if r == 1 else "staged"
+
+
+def moe_layer_staged(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut | None = None,
+                     stream=None):
+    _check("moe_layer_staged",
+           lib.moe_layer_staged(ctypes.byref(desc), T, _p(x), _p(y), _p(ws), ws_bytes,
+                                None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+
+
+def moe_layer_decode(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut | None = None,
+                     stream=None):
+    _check("moe_layer_decode",
+           lib.moe_layer_decode(ctypes.byref(desc), T, _p(x), _p(y), _p(ws), ws_bytes,
+                                None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+
+
+def layer_workspace(desc: MoELayerDesc, T_max: int, device="cuda"):
+    """A zeroed workspace tensor for the layer entry points (the decode path's
+    synchronisation block must start zeroed)."""
+    import torch
+    n = moe_layer_workspace_size(desc, T_max)
+    if n == 0:
+        raise ValueError("invalid layer description")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def debug_out(logits=None, topk_ids=None, topk_w=None, counts=None, offsets=None, src_token=None,

@@ -50,7 +50,14 @@ _SIGS = {
     "moe_layer_workspace_size": (c_size_t, [ctypes.POINTER(MoELayerDesc), c_int]),
     "moe_layer": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p, c_void_p,
                           c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
+    "moe_layer_path": (c_int, [ctypes.POINTER(MoELayerDesc), c_int]),
+    "moe_layer_staged": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p,
+                                 c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
+    "moe_layer_decode": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p,
+                                 c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
 }
+# bytes at the start of a layer workspace that the decode path keeps between calls
+LAYER_SYNC_BYTES = 4096 + 1024 * 128
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
 

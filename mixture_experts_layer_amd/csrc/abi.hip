@@ -55,6 +55,7 @@ int max_tiles_for(int max_rows, int E_loc, int BM) {
 }
 
 struct LayerWs {
+  int* sync;                 // DECODE_SYNC_BYTES at offset 0
   float* logits;
   int32_t *ids, *counts, *offsets, *src_token, *dst_row;
   float* w;
@@ -99,6 +100,9 @@ size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w) {
   const int max_tiles = max_tiles_for(max_rows, E_loc, BM);
   Carver c(base);
   LayerWs l;
+  // the single-launch decode path keeps its counters here, ahead of
+  // everything the other path writes, so the two can share a workspace
+  l.sync = c.take<int>(DECODE_SYNC_BYTES);
   l.logits = c.take<float>((size_t)T * d->E * 4);
   l.ids = c.take<int32_t>((size_t)T * d->k * 4);
   l.w = c.take<float>((size_t)T * d->k * 4);
@@ -126,13 +130,80 @@ size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w) {
   return c.used;
 }
 
-inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
-
 #define MOE_TRY(expr)                      \
   do {                                     \
     hipError_t _e = (expr);                \
     if (_e != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+bool decode_shape_ok(const moe_layer_desc* d, int T) {
+  return decode_supported(d->dt, T, d->E, d->e_end - d->e_begin, d->k, d->H, d->I_loc,
+                          d->I_shared);
+}
+
+// moe_layer takes the single-launch path while the expert weights a call can
+// touch -- min(E_loc, T*k) routed experts plus the shared one -- stay under
+// this many bytes: there the launch and dependency chain of the staged path
+// costs more than the single launch's lower streaming rate (measured
+// crossover on MI355X between about 0.3 and 0.6 GB).
+constexpr double DECODE_AUTO_BYTES = 512e6;
+
+bool decode_preferred(const moe_layer_desc* d, int T) {
+  const int E_loc = d->e_end - d->e_begin;
+  const long long pairs = (long long)T * d->k;
+  const double experts = (double)(pairs < E_loc ? pairs : E_loc);
+  const double bytes = 2.0 * 3.0 * (double)d->H * (experts * d->I_loc + (double)d->I_shared);
+  return bytes <= DECODE_AUTO_BYTES;
+}
+
+int check_layer_call(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
+                     size_t ws_bytes, const moe_debug_out* dbg) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  const size_t need = layer_layout(d, T, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (dbg) {
+    const void* ptrs[] = {dbg->logits, dbg->topk_ids, dbg->topk_w, dbg->counts,
+                          dbg->offsets, dbg->src_token, dbg->dst_row};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int run_decode(const moe_layer_desc* d, int T, const void* x, void* y, const LayerWs& l,
+               moe_debug_out* dbg, hipStream_t s) {
+  auto mark = [&](int i) -> hipError_t {
+    if (dbg && dbg->stage_events[i])
+      return hipEventRecord(static_cast<hipEvent_t>(dbg->stage_events[i]), s);
+    return hipSuccess;
+  };
+  DecodeLaunch a{};
+  a.x = x; a.w_router = d->w_router; a.logit_bias = d->logit_bias; a.sel_bias = d->sel_bias;
+  a.w13 = d->w13; a.w2 = d->w2; a.w13_shared = d->w13_shared; a.w2_shared = d->w2_shared;
+  a.y = y;
+  a.logits = (dbg && dbg->logits) ? dbg->logits : l.logits;
+  a.h = l.h;
+  a.h_shared = l.h_s;
+  a.sync = l.sync;
+  if (dbg) {
+    a.ids_out = dbg->topk_ids; a.w_out = dbg->topk_w; a.counts_out = dbg->counts;
+    a.offsets_out = dbg->offsets; a.src_out = dbg->src_token; a.dst_out = dbg->dst_row;
+  }
+  a.T = T; a.H = d->H; a.E = d->E; a.k = d->k; a.mode = d->mode;
+  a.I_loc = d->I_loc; a.I_shared = d->I_shared; a.e_begin = d->e_begin; a.e_end = d->e_end;
+  MOE_TRY(mark(0));
+  MOE_TRY(launch_decode(a, s));
+  for (int i = 1; i < MOE_STAGE_EVENTS; ++i) MOE_TRY(mark(i));
+  return MOE_OK;
+}
+
 
 }  // namespace
 
@@ -308,23 +379,36 @@ size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max) {
   return layer_layout(d, T_max, nullptr, nullptr);
 }
 
+int moe_layer_decode(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
+                     size_t ws_bytes, moe_debug_out* dbg, void* stream) {
+  int st = check_layer_call(d, T, x, y, ws, ws_bytes, dbg);
+  if (st || T == 0) return st;
+  if (!decode_shape_ok(d, T)) return MOE_ERR_UNSUPPORTED;
+  LayerWs l;
+  layer_layout(d, T, ws, &l);
+  return run_decode(d, T, x, y, l, dbg, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_path(const moe_layer_desc* d, int T) {
+  const int st = check_desc(d);
+  if (st) return -st;
+  if (T < 0) return -MOE_ERR_INVALID_ARG;
+  return (T > 0 && decode_shape_ok(d, T) && decode_preferred(d, T)) ? 1 : 0;
+}
+
 int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, size_t ws_bytes,
               moe_debug_out* dbg, void* stream) {
-  int st = check_desc(d);
-  if (st) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
-  const size_t need = layer_layout(d, T, nullptr, nullptr);
-  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (moe_layer_path(d, T) == 1) return moe_layer_decode(d, T, x, y, ws, ws_bytes, dbg, stream);
+  return moe_layer_staged(d, T, x, y, ws, ws_bytes, dbg, stream);
+}
+
+int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
+                     size_t ws_bytes, moe_debug_out* dbg, void* stream) {
+  int st = check_layer_call(d, T, x, y, ws, ws_bytes, dbg);
+  if (st || T == 0) return st;
   LayerWs l;
   layer_layout(d, T, ws, &l);
   if (dbg) {
-    const void* ptrs[] = {dbg->logits, dbg->topk_ids, dbg->topk_w, dbg->counts,
-                          dbg->offsets, dbg->src_token, dbg->dst_row};
-    for (const void* p : ptrs)
-      if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
     if (dbg->logits) l.logits = dbg->logits;
     if (dbg->topk_ids) l.ids = dbg->topk_ids;
     if (dbg->topk_w) l.w = dbg->topk_w;

@@ -101,4 +101,39 @@ hipError_t launch_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_
                           const float* w, int T, int k, int H, const void* y_shared, void* y,
                           int dt, hipStream_t st);
 
+// Single-launch decode path (decode.hip).
+constexpr int DECODE_MAX_T = 64;         // tokens: one 64-bit mask per expert
+constexpr int DECODE_MAX_E = 256;        // E and E_loc
+constexpr int DECODE_MAX_K = 16;
+constexpr int DECODE_MAX_PAIRS = 512;    // T * k
+constexpr int DECODE_MAX_BLOCKS = 1024;  // grid bound (workgroups resident at once)
+// sync block at the start of the workspace: a 4 KiB header, then one
+// 128-byte go-flag line per workgroup
+constexpr int DECODE_SYNC_BYTES = 4096 + DECODE_MAX_BLOCKS * 128;
+
+struct DecodeLaunch {
+  const void* x;
+  const void* w_router;
+  const float* logit_bias;
+  const float* sel_bias;
+  const void* w13;
+  const void* w2;
+  const void* w13_shared;
+  const void* w2_shared;
+  void* y;
+  float* logits;            // [T][E]
+  void* h;                  // [T*min(k, E_loc)][I_loc]
+  void* h_shared;           // [T][I_shared] or null
+  int* sync;                // DECODE_SYNC_BYTES, zeroed before first use
+  int32_t* ids_out;         // optional copies (may be null)
+  float* w_out;
+  int32_t* counts_out;
+  int32_t* offsets_out;
+  int32_t* src_out;
+  int32_t* dst_out;
+  int T, H, E, k, mode, I_loc, I_shared, e_begin, e_end;
+};
+bool decode_supported(int dt, int T, int E, int E_loc, int k, int H, int I, int Is);
+hipError_t launch_decode(const DecodeLaunch& d, hipStream_t st);
+
 }  // namespace moe

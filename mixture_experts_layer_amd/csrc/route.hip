@@ -5,73 +5,29 @@
 // Per-tile expert histogram and in-tile ranks feed the stable permutation of
 // "MoE 推理优化全景指南", section Dispatch 并不是一次普通 all-to-all.
 #include "moe_device.h"
+#include "moe_gate.h"
 #include "moe_kernels.h"
+#include "moe_router.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router logits, matrix-vector form: one block per expert and group of up to
-// TT tokens.  The 256 threads split H; partial dot products are reduced with
-// a fixed butterfly + LDS tree, so results are bitwise repeatable.  Used for
-// float32 inputs and for small token counts, where the whole of W_r must be
-// streamed once by many CUs.
+// Router logits, matrix-vector form: one wave per (expert, group of up to 8
+// tokens), four per block (router_dot_wave: lanes split H, a fixed butterfly
+// sums them, so results are bitwise repeatable and equal to the decode
+// kernel's).  Used for float32 inputs and for small token counts, where the
+// whole of W_r must be streamed once by many CUs.
 // ---------------------------------------------------------------------------
-template <typename Tin, int TT>
+template <typename Tin>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const Tin* __restrict__ x,
                                                           const Tin* __restrict__ wr, int T, int H,
                                                           int E, const float* __restrict__ bias,
                                                           float* __restrict__ logits) {
-  constexpr int VEC = 16 / sizeof(Tin);  // elements per 16-byte load
-  const int e = blockIdx.x;
-  const int t0 = blockIdx.y * TT;
-  const int ntok = min(TT, T - t0);
-  float acc[TT];
-#pragma unroll
-  for (int i = 0; i < TT; ++i) acc[i] = 0.f;
-
-  for (int h = threadIdx.x * VEC; h < H; h += 256 * VEC) {
-    float wv[8];
-    const uint4 wraw = *reinterpret_cast<const uint4*>(wr + (size_t)e * H + h);
-    if constexpr (VEC == 8) {
-      unpack_bf16x8(wraw, wv);
-    } else {
-      wv[0] = __uint_as_float(wraw.x); wv[1] = __uint_as_float(wraw.y);
-      wv[2] = __uint_as_float(wraw.z); wv[3] = __uint_as_float(wraw.w);
-    }
-#pragma unroll
-    for (int i = 0; i < TT; ++i) {
-      if (i < ntok) {
-        const uint4 xraw = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + i) * H + h);
-        float xv[8];
-        if constexpr (VEC == 8) {
-          unpack_bf16x8(xraw, xv);
-        } else {
-          xv[0] = __uint_as_float(xraw.x); xv[1] = __uint_as_float(xraw.y);
-          xv[2] = __uint_as_float(xraw.z); xv[3] = __uint_as_float(xraw.w);
-        }
-        float a = acc[i];
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) a = fmaf(xv[q], wv[q], a);
-        acc[i] = a;
-      }
-    }
-  }
-  __shared__ float red[4][TT];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < TT; ++i) {
-    float v = acc[i];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) red[wid][i] = v;
-  }
-  lds_barrier();
-  if (threadIdx.x < ntok) {
-    const int i = threadIdx.x;
-    float v = (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]);
-    if (bias) v += bias[e];
-    logits[(size_t)(t0 + i) * E + e] = v;
-  }
+  const int ntg = (T + 7) >> 3;
+  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= E * ntg) return;
+  const int e = u / ntg, t0 = (u - e * ntg) * 8;
+  router_dot_wave<Tin>(x, wr, H, E, e, t0, min(8, T - t0), bias, logits);
 }
 
 // ---------------------------------------------------------------------------
@@ -199,61 +155,15 @@ static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, i
 }
 
 // ---------------------------------------------------------------------------
-// Row reductions: DPP inside each 16-lane row -- pairs at distance 1 and 2,
-// then the half-row and row mirrors -- leave every lane of the row with the
-// row's result; the combination order is fixed, so float sums are the same
-// on every run.
-// ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
-
-// (key, id) arg-max: larger key wins, equal keys go to the smaller id.
-__device__ __forceinline__ bool better(float ok, int oi, float k, int i) {
-  return ok > k || (ok == k && oi < i);
-}
-// (key, id, logit) arg-max step between this lane and the lane selected by
-// DPP pattern CTRL.
-template <int CTRL>
-__device__ __forceinline__ void argmax3_step(float& k, int& i, float& s) {
-  const float ok = dpp_f<CTRL>(k);
-  const int oi = dpp_i<CTRL>(i);
-  const float os = dpp_f<CTRL>(s);
-  if (better(ok, oi, k, i)) { k = ok; i = oi; s = os; }
-}
-
-// Sum over each 16-lane row.
-__device__ __forceinline__ float row_sum(float v) {
-  v += dpp_f<DPP_XOR1>(v);
-  v += dpp_f<DPP_XOR2>(v);
-  v += dpp_f<DPP_HALF_MIRROR>(v);
-  v += dpp_f<DPP_MIRROR>(v);
-  return v;
-}
-
-// ---------------------------------------------------------------------------
 // Gating + routing metadata for one tile of TOK_TILE tokens.
 //
-// Selection: each 16-lane row of a wave owns one token; with 16 waves the
-// tile's 64 tokens are all in flight at once (four waves per SIMD hide the
-// DPP and LDS latencies).  Lane `sub` holds experts sub, sub + 16, ... (EPR
-// of them).  k rounds of a row-wide arg-max over (key descending, id
-// ascending) -- four DPP steps -- pick the experts in order; every lane of
-// the row sees the winner, the lane holding it retires it, and lane r % 16
-// keeps choice r.  The key is the logit, or logit + sel_bias in float32 for
-// the sigmoid mode; only exact comparisons decide, so the chosen ids are a
-// function of the float32 logits alone.  The round loop is not unrolled:
-// this kernel runs once per layer call, so its code is kept small.  The
-// tile's logits are staged in LDS (E <= 256) with a row pitch that puts the
-// 64 lanes of a wave in 64 distinct banks.  The gate weights are finished in
-// the row too (sums by DPP) and written straight out.
+// Selection: each 16-lane row of a wave owns one token (gate_row: k rounds
+// of a row-wide arg-max); with 16 waves the tile's 64 tokens are all in
+// flight at once (four waves per SIMD hide the DPP and LDS latencies).  Lane
+// `sub` holds experts sub, sub + 16, ... (EPR of them).  The tile's logits
+// are staged in LDS (E <= 256) with a row pitch that puts the 64 lanes of a
+// wave in 64 distinct banks.  The gate weights are finished in the row and
+// written straight out.
 //
 // Histogram and ranks (no atomics): the tile's (token, slot) pairs are cut
 // into C chunks; thread (chunk, e) counts the pairs of its chunk routed to
@@ -296,7 +206,6 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
   const int ntok = max(0, min(TOK_TILE, a.T - t0));
   const int k = a.k, E = a.E;
   const int mode = a.mode;
-  const bool sig = mode == 3;
 
   if (a.do_gate) {
     const int P = ((E + 63) & ~63) + 4;               // LDS row pitch (floats)
@@ -330,73 +239,18 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
     for (int pass = 0; pass * NW * 4 < ntok; ++pass) {
       const int tt = pass * NW * 4 + wid * 4 + row;
       const bool live = tt < ntok;
-      float s[EPR], key[EPR];
-      bool avail[EPR];
+      float s[EPR];
 #pragma unroll
       for (int i = 0; i < EPR; ++i) {
         const int e = sub + 16 * i;
-        avail[i] = live && e < E;
-        s[i] = avail[i] ? (STAGE ? s_logits[tt * P + e] : a.logits[(size_t)(t0 + tt) * E + e])
-                        : 0.f;
-        key[i] = avail[i] ? ((sig && a.sel_bias) ? s[i] + a.sel_bias[e] : s[i]) : -INFINITY;
+        s[i] = (live && e < E)
+                   ? (STAGE ? s_logits[tt * P + e] : a.logits[(size_t)(t0 + tt) * E + e])
+                   : 0.f;
       }
-      // choices sub and sub + 16 of this token (k <= 32)
-      int id0 = -1, id1 = -1;
-      float v0 = 0.f, v1 = 0.f, first_s = 0.f;
-      for (int r = 0; r < k; ++r) {
-        float bk = -INFINITY, bs = 0.f;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < EPR; ++i)
-          if (avail[i] && better(key[i], sub + 16 * i, bk, bi)) {
-            bk = key[i];
-            bi = sub + 16 * i;
-            bs = s[i];
-          }
-        argmax3_step<DPP_XOR1>(bk, bi, bs);
-        argmax3_step<DPP_XOR2>(bk, bi, bs);
-        argmax3_step<DPP_HALF_MIRROR>(bk, bi, bs);
-        argmax3_step<DPP_MIRROR>(bk, bi, bs);
-        if (r == 0) first_s = bs;
-        if (sub == (r & 15)) {
-          if (r < 16) { id0 = bi; v0 = bs; }
-          else { id1 = bi; v1 = bs; }
-        }
-#pragma unroll
-        for (int i = 0; i < EPR; ++i)
-          if (sub + 16 * i == bi) avail[i] = false;
-      }
-      // gate weights of the chosen experts
-      const bool h0 = live && sub < k, h1 = live && sub + 16 < k;
+      int id0, id1;
       float g0, g1;
-      if (mode == 3) {
-        g0 = h0 ? 1.0f / (1.0f + expf(-v0)) : 0.f;
-        g1 = h1 ? 1.0f / (1.0f + expf(-v1)) : 0.f;
-        const float z = row_sum(g0 + g1);
-        g0 = g0 / z;
-        g1 = g1 / z;
-      } else if (mode == 0) {
-        // softmax over the k chosen logits; the first choice is the largest
-        g0 = h0 ? expf(v0 - first_s) : 0.f;
-        g1 = h1 ? expf(v1 - first_s) : 0.f;
-        const float z = row_sum(g0 + g1);
-        g0 = g0 / z;
-        g1 = g1 / z;
-      } else {
-        // softmax over all E, then (mode 2) renormalised over the k chosen
-        float z = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPR; ++i)
-          if (live && sub + 16 * i < E) z += expf(s[i] - first_s);
-        z = row_sum(z);
-        g0 = h0 ? expf(v0 - first_s) / z : 0.f;
-        g1 = h1 ? expf(v1 - first_s) / z : 0.f;
-        if (mode == 2) {
-          const float ps = row_sum(g0 + g1);
-          g0 = g0 / ps;
-          g1 = g1 / ps;
-        }
-      }
+      gate_row<EPR>(s, live, sub, E, k, mode, a.sel_bias, id0, g0, id1, g1);
+      const bool h0 = live && sub < k, h1 = live && sub + 16 < k;
       if (h0) {
         s_ids[tt * k + sub] = id0;
         a.ids_out[(size_t)(t0 + tt) * k + sub] = id0;
@@ -495,13 +349,14 @@ hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, in
   // bf16 prefill batches with E a multiple of 4 (16-byte logit stores)
   const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 && E % 4 == 0;
   if (!mfma_shape) {
-    dim3 grid(E, (T + 7) / 8);
+    const long long units = (long long)E * ((T + 7) / 8);
+    const int grid = (int)((units + 3) / 4);
     if (dt == 0)
-      router_gemv_kernel<float, 8><<<grid, 256, 0, st>>>((const float*)x, (const float*)wr, T, H,
-                                                         E, bias, logits);
+      router_gemv_kernel<float><<<grid, 256, 0, st>>>((const float*)x, (const float*)wr, T, H, E,
+                                                      bias, logits);
     else
-      router_gemv_kernel<bf16_t, 8><<<grid, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)wr, T,
-                                                          H, E, bias, logits);
+      router_gemv_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, (const bf16_t*)wr, T, H,
+                                                       E, bias, logits);
     return hipGetLastError();
   }
   const bf16_t* xb = (const bf16_t*)x;

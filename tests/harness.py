@@ -77,7 +77,11 @@ class OracleShare:
 
 
 def ws_tensor(nbytes, device="cuda"):
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    # zeroed: a layer workspace starts with the decode path's sync block
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+LAYER_FNS = {"auto": "moe_layer", "staged": "moe_layer_staged", "decode": "moe_layer_decode"}
 
 
 class GpuLayer:
@@ -107,7 +111,7 @@ class GpuLayer:
         assert self.ws_bytes > 0
         self.ws = ws_tensor(self.ws_bytes)
 
-    def run(self, T, x=None, debug=True):
+    def run(self, T, x=None, debug=True, path="auto"):
         x = self.L.x[:T] if x is None else x
         dev = x.device
         E_loc = self.e_end - self.e_begin
@@ -125,8 +129,12 @@ class GpuLayer:
                 dst_row=torch.empty((T, self.k), dtype=torch.int32, device=dev))
             dbg = M.debug_out(out["logits"], out["ids"], out["w"], out["counts"], out["offsets"],
                               out["src_token"], out["dst_row"])
-        M.moe_layer(self.desc, T, x, y, self.ws, self.ws_bytes, dbg)
+        getattr(M, LAYER_FNS[path])(self.desc, T, x, y, self.ws, self.ws_bytes, dbg)
         return out
+
+    def sync_error(self):
+        """The decode path's error word (bytes 4..7 of the workspace)."""
+        return int(self.ws[4:8].view(torch.int32).item())
 
 
 def check_layer(gl: GpuLayer, out, T, sample=None, check_rows=True):

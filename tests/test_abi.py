@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(moe_\w+)", out))
@@ -133,3 +133,52 @@ def test_layer_rejects_bad_descriptors():
         M.moe_layer(d, 4, P, P, P, 10, stream=0)
     assert e.value.status == 3
     M.moe_layer(d, 0, P, P, P, 0, stream=0)   # T = 0 is a no-op
+
+
+def test_layer_paths_reject_before_launch():
+    base = dict(H=256, E=8, k=2, I_loc=128, e_begin=0, e_end=8, I_shared=0, mode=0, dt=1,
+                w_router=1 << 20, w13=1 << 21, w2=1 << 22)
+    d = M.MoELayerDesc(**base)
+    # shapes outside the single-launch path's limits
+    for change, T in ((dict(dt=0), 4), ({}, 65), (dict(E=300, e_end=300, k=2), 4),
+                      (dict(E=64, e_end=64, k=17), 4), (dict(E=16, e_end=16, k=9), 60)):
+        dd = M.MoELayerDesc(**{**base, **change})
+        with pytest.raises(M.MoEError) as e:
+            M.moe_layer_decode(dd, T, P, P, P, 1 << 30, stream=0)
+        assert e.value.status == 2, (change, T)
+    for fn in (M.moe_layer_decode, M.moe_layer_staged):
+        with pytest.raises(M.MoEError) as e:      # workspace too small
+            fn(d, 4, P, P, P, 10, stream=0)
+        assert e.value.status == 3
+        with pytest.raises(M.MoEError) as e:      # misaligned output
+            fn(d, 4, P, MIS, P, 1 << 30, stream=0)
+        assert e.value.status == 1
+        fn(d, 0, P, P, P, 0, stream=0)            # T = 0 is a no-op
+
+
+def test_layer_workspace_starts_with_sync_block():
+    d = M.MoELayerDesc(H=256, E=8, k=2, I_loc=128, e_begin=0, e_end=8, I_shared=0, mode=0, dt=1,
+                       w_router=1 << 20, w13=1 << 21, w2=1 << 22)
+    n1 = M.moe_layer_workspace_size(d, 1)
+    # logits, ids, weights, metadata, h and the expert outputs of one token follow the block
+    assert n1 >= M.LAYER_SYNC_BYTES + 8 * 4 + 2 * 128 * 2 + 2 * 256 * 2
+
+
+def test_layer_path_choice():
+    def desc(**kw):
+        base = dict(H=4096, E=128, k=8, I_loc=192, e_begin=0, e_end=128, I_shared=0, mode=2, dt=1,
+                    w_router=1 << 20, w13=1 << 21, w2=1 << 22)
+        base.update(kw)
+        return M.MoELayerDesc(**base)
+    tp = desc()                                   # tensor-parallel share: 4.7 MB per expert
+    # 13 * 8 experts * 4.72 MB = 491 MB; 14 * 8 * 4.72 MB = 528 MB
+    assert [M.moe_layer_path(tp, T) for T in (1, 8, 13, 14, 64, 65)] == \
+        ["decode", "decode", "decode", "staged", "staged", "staged"]
+    ep = desc(I_loc=1536)                         # whole experts: 37.7 MB each
+    assert [M.moe_layer_path(ep, T) for T in (1, 2)] == ["decode", "staged"]
+    assert M.moe_layer_path(desc(dt=0), 1) == "staged"        # float32 layers
+    assert M.moe_layer_path(tp, 0) == "staged"
+    with pytest.raises(M.MoEError):
+        M.moe_layer_path(tp, -1)
+    with pytest.raises(M.MoEError):
+        M.moe_layer_path(desc(k=0), 1)

@@ -11,6 +11,7 @@ import gc
 import pytest
 import torch
 
+import mixture_experts_layer_amd as M
 import workloads as W
 from harness import GpuLayer, check_layer
 
@@ -40,7 +41,24 @@ def test_full_size_layer(name, T):
     out = gl.run(T)
     sample = W.sample_rows(T, N_SAMPLE[name], seed=T).numpy()
     res = check_layer(gl, out, T, sample=sample)
-    print(f"{name} T={T}: {res}", flush=True)
+    print(f"{name} T={T} ({M.moe_layer_path(gl.desc, T)}): {res}", flush=True)
+
+
+# decode-sized batches also through the path moe_layer does not take, so
+# both the staged and the single-launch path are checked at full size
+ALT = [(name, T) for name, T in CASES if T <= 64 and W.CONFIGS[name].dtype == "bf16"]
+
+
+@pytest.mark.parametrize("name,T", ALT)
+def test_full_size_layer_other_path(name, T):
+    gl = _layer(name)
+    path = "staged" if M.moe_layer_path(gl.desc, T) == "decode" else "decode"
+    out = gl.run(T, path=path)
+    sample = W.sample_rows(T, N_SAMPLE[name], seed=T + 1).numpy()
+    res = check_layer(gl, out, T, sample=sample)
+    if path == "decode":
+        assert gl.sync_error() == 0
+    print(f"{name} T={T} ({path}): {res}", flush=True)
 
 
 def teardown_module():
