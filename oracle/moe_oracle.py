@@ -26,7 +26,9 @@ in the design notes of the repository):
     of the stacked axis by the same range, and the down projection's input
     dimension by that range;
   * the selection-only bias of the sigmoid gating is added to the logit;
-  * a shared expert is added with weight 1 after the routed sum.
+  * a shared expert is added with weight 1 after the routed sum;
+  * token copies packed for the expert-parallel dispatch are ordered by
+    destination rank, then by token (one copy per token and rank).
 
 Parity status: every function below is pinned by the `-m "not gpu"` tests in
 tests/test_oracle_pins.py (worked examples printed on the pages, closed forms,
@@ -212,6 +214,83 @@ def permute(ids, e_begin, e_end):
                 dst_row[t, j] = row
                 src_token[row] = t
     return counts, offsets, src_token, dst_row
+
+
+# ---------------------------------------------------------------------------
+# Expert-parallel dispatch: token copies packed by destination rank
+# ---------------------------------------------------------------------------
+
+def owner_rank(e, E, P):
+    """Rank holding expert e when E experts are split into P contiguous ranges
+    of E/P: [MoE guide] section "一个 token 为什么要跨 GPU" (8 experts on 4 GPUs,
+    GPU r holding experts 2r and 2r + 1); [Moebius notes] eq. (4)."""
+    if E % P:
+        raise ValueError("E must be divisible by P")
+    return int(e) // (E // P)
+
+
+def pack_by_rank(ids, E, P):
+    """Token copies packed by destination rank, the step before the dispatch
+    all-to-all.
+
+    [MoE guide] section "一个 token 为什么要跨 GPU": count / prefix sum /
+    permute by destination, so that each destination's copies are contiguous.
+    [CS349D L8] section 3.1: a token that chose two experts held by one
+    device is sent there once, its gate weights travelling with it.
+
+    A copy is a (rank r, token t) pair such that some slot j of t has
+    owner_rank(ids[t][j]) == r.  Copies are ordered by rank, then by token
+    (reading: inside a rank a copy may serve several experts, so the token
+    order -- the order the page keeps inside a segment -- is the stable one).
+
+    Returns send_counts [P], send_offsets [P + 1], send_token [rows] (the
+    token each copy carries) and send_row [T, k] (the copy carrying slot j).
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    counts = np.zeros(P, dtype=np.int64)
+    for t in range(T):
+        for r in set(owner_rank(e, E, P) for e in ids[t]):
+            counts[r] += 1
+    offsets = exclusive_offsets(counts)
+    send_token = np.empty(int(offsets[-1]), dtype=np.int64)
+    send_row = np.full((T, k), -1, dtype=np.int64)
+    row = 0
+    for r in range(P):
+        for t in range(T):
+            slots = [j for j in range(k) if owner_rank(ids[t, j], E, P) == r]
+            if slots:
+                send_token[row] = t
+                for j in slots:
+                    send_row[t, j] = row
+                row += 1
+    return counts, offsets, send_token, send_row
+
+
+def unpack_sum(y_ret, send_row, dtype=np.float64):
+    """The source rank's sum after the combine all-to-all: y[t] is the sum of
+    the partial outputs returned for t's copies, in rank order (each copy
+    once, however many of t's slots it served).  [CS349D L8] section 3.1
+    step 4 (results sent back and added); the gate weights were applied on
+    the ranks that computed the experts.
+
+    y_ret: [rows, H]; send_row: [T, k] as from pack_by_rank.  Returns [T, H].
+    """
+    y_ret = _as(y_ret, dtype)
+    send_row = np.asarray(send_row)
+    T = send_row.shape[0]
+    y = np.zeros((T, y_ret.shape[1]), dtype=dtype)
+    for t in range(T):
+        for row in sorted(set(int(r) for r in send_row[t] if r >= 0)):
+            y[t] += y_ret[row]
+    return y
+
+
+def dispatch_volume_bytes(T, k, D, H, elem_bytes):
+    """Bytes one device sends per layer and direction under uniform routing:
+    T * k * (D - 1) / D token vectors of H elements.  [CS349D L8] section 3.1
+    (communication volume)."""
+    return T * k * (D - 1) / D * H * elem_bytes
 
 
 # ---------------------------------------------------------------------------

@@ -197,6 +197,106 @@ def test_permute_expert_range():
     assert np.array_equal(src, order // k)
 
 
+# ---------------------------------------------------------------- dispatch packing by rank
+
+def test_pack_by_rank_worked_example():
+    g = golden("dispatch_by_rank_worked_example.json")
+    ids = np.array(g["expert_ids"])[:, None]
+    counts, offsets, send_token, send_row = O.pack_by_rank(ids, g["E"], g["P"])
+    d = g["derived"]
+    assert counts.tolist() == d["send_counts"]
+    assert offsets.tolist() == d["send_offsets"]
+    assert send_token.tolist() == d["send_token"]
+    assert send_row[:, 0].tolist() == d["send_row"]
+    # grouping the printed expert permutation by owner GPU gives the same copies
+    owner = {f"t{t}": g["expert_ids"][t] // (g["E"] // g["P"]) for t in range(len(g["expert_ids"]))}
+    by_gpu = [sorted((tok for seg in g["printed_expert_permutation"] for tok in seg
+                      if owner[tok] == r), key=lambda s: int(s[1:])) for r in range(g["P"])]
+    assert by_gpu == [[f"t{send_token[i]}" for i in range(offsets[r], offsets[r + 1])]
+                      for r in range(g["P"])]
+
+
+def test_pack_sends_a_token_once_per_device():
+    # [CS349D L8] section 3.1: two experts of one device -> one copy
+    ids = np.array([[0, 1], [0, 2], [7, 6], [5, 3]])
+    counts, offsets, send_token, send_row = O.pack_by_rank(ids, 8, 4)
+    assert counts.tolist() == [2, 2, 1, 1]
+    assert send_token.tolist() == [0, 1, 1, 3, 3, 2]
+    assert send_row.tolist() == [[0, 0], [1, 2], [5, 5], [4, 3]]
+
+
+def test_pack_equals_library_sort_of_deduplicated_pairs():
+    r = rng(31)
+    T, k, E, P = 200, 6, 32, 8
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)])
+    counts, offsets, send_token, send_row = O.pack_by_rank(ids, E, P)
+    ranks = ids // (E // P)
+    pairs = np.array(sorted({(int(ranks[t, j]), t) for t in range(T) for j in range(k)}))
+    order = np.lexsort((pairs[:, 1], pairs[:, 0]))      # library sort: rank, then token
+    assert np.array_equal(send_token, pairs[order, 1])
+    assert np.array_equal(counts, np.bincount(pairs[:, 0], minlength=P))
+    for t in range(T):
+        for j in range(k):
+            row = send_row[t, j]
+            assert send_token[row] == t
+            assert offsets[ranks[t, j]] <= row < offsets[ranks[t, j] + 1]
+
+
+def test_pack_with_one_expert_per_rank_is_the_expert_permutation():
+    r = rng(32)
+    T, k, E = 150, 4, 16
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)])
+    pc, po, ps, pr = O.pack_by_rank(ids, E, E)
+    ec, eo, es, er = O.permute(ids, 0, E)
+    assert np.array_equal(pc, ec) and np.array_equal(po, eo)
+    assert np.array_equal(ps, es) and np.array_equal(pr, er)
+
+
+def test_dispatch_volume_exercise_and_expectation():
+    g = golden("dispatch_volume_exercise.json")
+    T, D, k, H = g["T"], g["D"], g["assumed"]["k"], g["assumed"]["H"]
+    assert round(O.dispatch_volume_bytes(T, k, D, H, 1) / 1e6, 1) == g["printed_MB"]["dispatch_fp8"]
+    assert round(O.dispatch_volume_bytes(T, k, D, H, 2) / 1e6, 1) == g["printed_MB"]["combine_bf16"]
+    # with one expert per device no copy is merged, and under uniform routing a
+    # device sends k (D - 1) / D copies per token to the others on average
+    r = rng(33)
+    D, k, T, me = 16, 4, 4000, 5
+    ids = np.stack([r.permutation(D)[:k] for _ in range(T)])
+    counts, _, _, _ = O.pack_by_rank(ids, D, D)
+    assert counts.sum() == T * k
+    sent = counts.sum() - counts[me]
+    assert abs(sent / (T * k * (D - 1) / D) - 1) < 0.01
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_dispatch_round_trip_equals_the_full_layer(mode):
+    """Pack by rank, let every rank run its experts on the copies it received
+    (routing travelling with them), return the partial sums and add them at
+    the source: the full layer's output."""
+    L = tiny_layer(34, T=9, E=8)
+    E, P, k = 8, 4, 3
+    y_full, aux = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode,
+                              sel_bias=L["sel_bias"])
+    ids, w = aux["ids"], aux["w"]
+    counts, offsets, send_token, send_row = O.pack_by_rank(ids, E, P)
+    y_ret = np.zeros((int(offsets[-1]), L["x"].shape[1]))
+    for r in range(P):
+        rows = np.arange(offsets[r], offsets[r + 1])
+        lo, hi = r * E // P, (r + 1) * E // P
+        toks = send_token[rows]
+        c, o, src, dst = O.permute(ids[toks], lo, hi)
+        y_perm = O.grouped_ffn(L["x"][toks], src, o, L["w13"][lo:hi], L["w2"][lo:hi])
+        y_ret[rows] = O.combine(y_perm, dst, w[toks])
+    y = O.unpack_sum(y_ret, send_row)
+    np.testing.assert_allclose(y, y_full, rtol=0, atol=1e-13 * np.abs(y_full).max())
+
+
+def test_unpack_sum_adds_each_copy_once_in_rank_order():
+    send_row = np.array([[2, 2, 0], [1, -1, 1]])
+    y_ret = np.array([[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]])
+    assert O.unpack_sum(y_ret, send_row).tolist() == [[101.0, 202.0], [10.0, 20.0]]
+
+
 # ---------------------------------------------------------------- experts
 
 def test_silu_identities():
