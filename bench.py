@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--sweep-workloads", default="qwen3_ep_all128,qwen3_tp8_rank0",
                     help="workloads whose token counts are swept (comma list)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dispatch", action="store_true",
+                    help="skip the expert-parallel dispatch packing measurement")
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
@@ -228,6 +230,87 @@ def layer_roof_frac(cfg, work, ms):
 
 
 # ---------------------------------------------------------------------------
+# Expert-parallel dispatch packing (the source rank's side of the exchange)
+# ---------------------------------------------------------------------------
+
+def dispatch_bench(steps, warmup, P=8, Ts=(64, 4096)):
+    """moe_pack_by_rank (copies by destination rank + their x rows) and
+    moe_unpack_sum (the sum of the returned rows) on the DeepSeek-V3-shaped
+    layer's routing, as one of P expert-parallel ranks would run them, timed
+    by HIP-graph replay.  Algorithmic bytes: pack reads x once per token and
+    the routing, writes every copy's row and routing; unpack reads every
+    returned row once and writes y."""
+    import torch
+    import mixture_experts_layer_amd as M
+    import workloads as W
+    cfg = W.CONFIGS["deepseek_v3"]
+    T_max = max(Ts)
+    L = W.make_layer(cfg, device="cuda", seed=0, T_max=T_max, experts=False)
+    H, E, k = cfg.H, cfg.E, cfg.k
+    dt = M.dtype_code(L.x)
+    logits = torch.empty((T_max, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T_max, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T_max, k), dtype=torch.float32, device="cuda")
+    M.moe_route(L.x, L.w_r, dt, T_max, H, E, k, cfg.mode, L.logit_bias, L.sel_bias, logits, ids, w)
+    rows_max = T_max * min(k, P)
+    counts = torch.empty((P,), dtype=torch.int32, device="cuda")
+    offsets = torch.empty((P + 1,), dtype=torch.int32, device="cuda")
+    send_token = torch.empty((rows_max,), dtype=torch.int32, device="cuda")
+    send_row = torch.empty((T_max, k), dtype=torch.int32, device="cuda")
+    send_ids = torch.empty((rows_max, k), dtype=torch.int32, device="cuda")
+    send_w = torch.empty((rows_max, k), dtype=torch.float32, device="cuda")
+    x_send = torch.empty((rows_max, H), dtype=L.x.dtype, device="cuda")
+    y = torch.empty((T_max, H), dtype=L.x.dtype, device="cuda")
+    nb = M.moe_pack_workspace_size(T_max, k, P)
+    ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+    out = []
+    for T in Ts:
+        def pack():
+            M.moe_pack_by_rank(ids, w, T, k, E, P, L.x, H, dt, counts, offsets, send_token,
+                               send_row, send_ids, send_w, x_send, ws, nb)
+
+        def unpack():
+            M.moe_unpack_sum(x_send, dt, send_row, T, k, H, y, dt)
+
+        pack()
+        torch.cuda.synchronize()
+        rows = int(offsets[P].item())
+        res = dict(workload="deepseek_v3_moe_layer_shared1 routing, one of %d expert-parallel ranks"
+                   % P, T=T, P=P, copies=rows,
+                   copies_to_other_ranks_per_token=None)
+        for name, fn, nbytes in (
+                ("pack_by_rank", pack, 2 * T * H + T * k * 8 + rows * (2 * H + 8 * k + 4) + T * k * 4),
+                ("unpack_sum", unpack, rows * 2 * H + T * 2 * H + T * k * 4)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(10):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, steps // 10)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / (reps * 10)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            res[name] = dict(ms=round(ms, 4), algorithmic_bytes=int(nbytes),
+                             achieved_GBs=round(gbs, 1), peak_GBs=HBM_PEAK_GBS,
+                             frac=round(gbs / HBM_PEAK_GBS, 4))
+        c = counts.cpu().tolist()
+        # rank 0 stands for the source's own rank
+        res["copies_to_other_ranks_per_token"] = round((rows - c[0]) / T, 3)
+        out.append(res)
+        print(f"# dispatch T={T}: pack {res['pack_by_rank']['ms']} ms "
+              f"({res['pack_by_rank']['frac']}), unpack {res['unpack_sum']['ms']} ms "
+              f"({res['unpack_sum']['frac']})", file=sys.stderr, flush=True)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ---------------------------------------------------------------------------
 
@@ -386,6 +469,10 @@ def main():
                 torch.cuda.empty_cache()
             bench.set_T(T)
 
+    dispatch = None
+    if not args.no_dispatch:
+        dispatch = dispatch_bench(max(args.steps, 20), args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, args.cpu_sample)
@@ -418,6 +505,7 @@ def main():
         "routing": {"rows": work["rows"], "touched_experts": work["touched"],
                     "imbalance_ratio": round(imb, 3)},
         "sweep": sweep,
+        "dispatch": dispatch,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -176,6 +176,55 @@ int moe_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row, const
                 int T, int k, int H, const void* y_shared, void* y, int dt, void* stream);
 
 /*
+ * moe_pack_by_rank -- token copies packed by destination rank, the step
+ * before the expert-parallel dispatch all-to-all.
+ *   [MoE guide] section "一个 token 为什么要跨 GPU" (count / prefix sum /
+ *   permute by destination; 8 experts on 4 GPUs, GPU r holding experts 2r,
+ *   2r + 1); [CS349D L8] section 3.1 (a token that chose two experts held by
+ *   one device is sent there once; its gate weights travel with it).
+ *
+ *   Rank r holds experts [r*E/P, (r+1)*E/P) (E divisible by P).  A copy is a
+ *   (rank r, token t) pair such that some slot of t routes to an expert of r;
+ *   copies are ordered by rank, then by token.
+ *   send_counts[r]   = copies for rank r;  send_offsets[P + 1] their prefix sum.
+ *   send_token[row]  = the token copy `row` carries (first send_offsets[P]).
+ *   send_row[t][j]   = the copy carrying slot j of token t (-1 if topk_ids[t][j]
+ *                      is outside [0, E): such a slot is not sent).
+ *   send_ids[row][:] = topk_ids[t][:], send_w[row][:] = topk_w[t][:] for the
+ *                      token of the copy (all k slots: the receiving rank keeps
+ *                      the slots of its own experts); both may be NULL.
+ *   x_send[row][:]   = x[t][:] when x != NULL (dtype dt, H columns).
+ *
+ *   topk_ids[T][k] int32 (distinct within a token, as moe_route gives),
+ *   topk_w[T][k] float32 (needed only for send_w).  Rows are at most
+ *   T * min(k, P); size send_token, send_ids, send_w and x_send for that.
+ *   ws: at least moe_pack_workspace_size(T, k, P) bytes (may be NULL when
+ *   T <= 64).  Limits: 1 <= P <= 64, k <= 32, E <= 1024.  T = 0 writes zero
+ *   counts and offsets.
+ */
+size_t moe_pack_workspace_size(int T, int k, int P);
+int moe_pack_by_rank(const int32_t* topk_ids, const float* topk_w, int T, int k, int E, int P,
+                     const void* x, int H, int dt,
+                     int32_t* send_counts, int32_t* send_offsets, int32_t* send_token,
+                     int32_t* send_row, int32_t* send_ids, float* send_w, void* x_send,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_unpack_sum -- the source rank's sum after the combine all-to-all.
+ *   [CS349D L8] section 3.1 (results sent back to the token's device and
+ *   added; the gate weights were applied where the experts ran).
+ *
+ *   y[t] = sum over the distinct rows of send_row[t] (each copy once, in
+ *   ascending row = rank order) of y_ret[row], accumulated in float32 and
+ *   rounded once to dtype dt.  A token with no copy gets zeros.
+ *   y_ret[rows][H] dtype y_ret_dt (the partial outputs returned for the
+ *   copies, in the order moe_pack_by_rank sent them); send_row[T][k] as
+ *   moe_pack_by_rank wrote it; y[T][H] dtype dt.
+ */
+int moe_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int T, int k, int H,
+                   void* y, int dt, void* stream);
+
+/*
  * moe_layer -- the whole share of the layer in one call:
  *   route -> permute -> grouped SwiGLU GEMMs (gather fused) -> shared expert
  *   -> combine, all enqueued on `stream` without host synchronisation.

@@ -19,7 +19,8 @@ from ._abi import (MOE_F32, MOE_BF16, MOE_OK, GATE_TOPK_SOFTMAX, GATE_SOFTMAX_TO
 __all__ = [
     "MoEError", "lib", "get_lib", "moe_abi_version", "moe_status_str", "moe_route", "moe_permute",
     "moe_permute_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
-    "moe_combine", "moe_layer", "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
+    "moe_combine", "moe_pack_by_rank", "moe_pack_workspace_size", "moe_unpack_sum", "moe_layer",
+    "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
     "moe_layer_workspace_size",
     "layer_workspace", "layer_desc", "dtype_code", "LAYER_SYNC_BYTES",
     "MoELayerDesc", "MoEDebugOut",
@@ -117,6 +118,24 @@ def moe_grouped_ffn(x_perm, x, src_token, offsets, E_loc, max_rows, H, I_loc, w1
 def moe_combine(y_perm, y_perm_dt, dst_row, topk_w, T, k, H, y_shared, y, dt, stream=None):
     _check("moe_combine", lib.moe_combine(_p(y_perm), y_perm_dt, _p(dst_row), _p(topk_w), T, k, H,
                                           _p(y_shared), _p(y), dt, _stream(stream)))
+
+
+def moe_pack_workspace_size(T, k, P) -> int:
+    return lib.moe_pack_workspace_size(T, k, P)
+
+
+def moe_pack_by_rank(topk_ids, topk_w, T, k, E, P, x, H, dt, send_counts, send_offsets, send_token,
+                     send_row, send_ids, send_w, x_send, ws, ws_bytes, stream=None):
+    _check("moe_pack_by_rank",
+           lib.moe_pack_by_rank(_p(topk_ids), _p(topk_w), T, k, E, P, _p(x), H, dt,
+                                _p(send_counts), _p(send_offsets), _p(send_token), _p(send_row),
+                                _p(send_ids), _p(send_w), _p(x_send), _p(ws), ws_bytes,
+                                _stream(stream)))
+
+
+def moe_unpack_sum(y_ret, y_ret_dt, send_row, T, k, H, y, dt, stream=None):
+    _check("moe_unpack_sum", lib.moe_unpack_sum(_p(y_ret), y_ret_dt, _p(send_row), T, k, H, _p(y),
+                                                dt, _stream(stream)))
 
 
 def layer_desc(H, E, k, I_loc, mode, dt, w_router, w13, w2, e_begin=0, e_end=None, I_shared=0,

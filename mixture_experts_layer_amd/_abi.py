@@ -47,6 +47,12 @@ _SIGS = {
                                 c_void_p]),
     "moe_combine": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p,
                             c_void_p, c_int, c_void_p]),
+    "moe_pack_workspace_size": (c_size_t, [c_int, c_int, c_int]),
+    "moe_pack_by_rank": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int,
+                                 c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_unpack_sum": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p, c_int,
+                               c_void_p]),
     "moe_layer_workspace_size": (c_size_t, [ctypes.POINTER(MoELayerDesc), c_int]),
     "moe_layer": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p, c_void_p,
                           c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),

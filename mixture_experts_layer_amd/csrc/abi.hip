@@ -374,6 +374,72 @@ int moe_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row, const
                                    static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_pack_workspace_size(int T, int k, int P) {
+  if (T < 0 || k < 1 || P < 1 || P > 64) return 0;
+  const size_t n_tiles = (size_t)cdiv(T, 64);
+  return align_up((size_t)T * 8) + 2 * align_up(n_tiles * P * 4);
+}
+
+int moe_pack_by_rank(const int32_t* topk_ids, const float* topk_w, int T, int k, int E, int P,
+                     const void* x, int H, int dt, int32_t* send_counts, int32_t* send_offsets,
+                     int32_t* send_token, int32_t* send_row, int32_t* send_ids, float* send_w,
+                     void* x_send, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || k > E || P < 1) return MOE_ERR_INVALID_ARG;
+  if (E % P) return MOE_ERR_INVALID_ARG;
+  if (k > KMAX || E > 1024 || P > 64) return MOE_ERR_UNSUPPORTED;
+  if (!send_counts || !send_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !send_token || !send_row)) return MOE_ERR_INVALID_ARG;
+  if (send_w && !topk_w) return MOE_ERR_INVALID_ARG;
+  int st = MOE_OK;
+  if (x) {
+    if (!valid_dt(dt) || !x_send) return MOE_ERR_INVALID_ARG;
+    if ((st = check_hidden(H))) return st;
+  }
+  {
+    const void* ptrs[] = {topk_ids, topk_w, send_counts, send_offsets, send_token, send_row,
+                          send_ids, send_w, x, x_send, ws};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  }
+  const bool single = T <= 64;
+  if (!single && (!ws || ws_bytes < moe_pack_workspace_size(T, k, P))) return MOE_ERR_WORKSPACE;
+  PackArgs a{};
+  a.ids = topk_ids; a.w = topk_w;
+  a.T = T; a.k = k; a.E = E; a.P = P; a.per = E / P;
+  a.send_counts = send_counts; a.send_offsets = send_offsets; a.send_token = send_token;
+  a.send_row = send_row; a.send_ids = send_ids; a.send_w = send_w;
+  if (!single) {
+    Carver c(ws);
+    const size_t n_tiles = (size_t)cdiv(T, 64);
+    a.masks = c.take<unsigned long long>((size_t)T * 8);
+    a.tile_counts = c.take<int32_t>(n_tiles * P * 4);
+    a.tile_base = c.take<int32_t>(n_tiles * P * 4);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    // zero counts and offsets, as for moe_permute
+    a.T = 0;
+    return hip_status(launch_pack_by_rank(a, nullptr, 0, 0, nullptr, 0, s));
+  }
+  const int max_rows = T * (k < P ? k : P);
+  return hip_status(launch_pack_by_rank(a, x, H, elt_bytes(dt), x_send, max_rows, s));
+}
+
+int moe_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int T, int k, int H,
+                   void* y, int dt, void* stream) {
+  if (!valid_dt(dt) || !valid_dt(y_ret_dt) || T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  int st = check_hidden(H);
+  if (st) return st;
+  if (k > KMAX) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_ret || !send_row || !y) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {y_ret, send_row, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+  return hip_status(
+      launch_unpack_sum(y_ret, y_ret_dt, send_row, T, k, H, y, dt, static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max) {
   if (check_desc(d) != MOE_OK || T_max < 0) return 0;
   return layer_layout(d, T_max, nullptr, nullptr);

@@ -238,10 +238,12 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
   const int base = has_sh ? 1 : 0;
   if (wid == 0) {
     for (int i = lane; i < E_loc; i += 64) s_mask[i] = 0ull;
+    wave_lds_sync();
     for (int q = lane; q < npair; q += 64) {
       const int el = s_ids[q] - a.e_begin;
       if (el >= 0 && el < E_loc) atomicOr(&s_mask[el], 1ull << (q / k));
     }
+    wave_lds_sync();
     // lane l owns experts [4l, 4l + 4) (E_loc <= 256): counts, then
     // exclusive scans of rows and of active experts across the wave
     int c[4], rows = 0, act = 0;
@@ -284,6 +286,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
         s_slot_n[0] = T;
       }
     }
+    wave_lds_sync();
     for (int q = lane; q < npair; q += 64) {
       const int t = q / k, el = s_ids[q] - a.e_begin;
       int row = -1;

@@ -1,0 +1,329 @@
+// Token copies packed by destination rank for the expert-parallel dispatch,
+// and the source rank's sum after the return.
+//
+// "MoE 推理优化全景指南", section 一个 token 为什么要跨 GPU: before the dispatch
+// all-to-all the tokens are counted, prefix-summed and permuted by destination
+// so that each destination's copies are contiguous.  "Lecture 8 · 混合专家模型
+// 的推理" (CS349D notes) section 3.1: a token that chose two experts held by
+// one device is sent there once, its gate weights travelling with it, and the
+// results come back to be added.
+//
+// Rank r holds experts [r*E/P, (r+1)*E/P).  A copy is a (rank, token) pair;
+// copies are ordered by rank, then by token.  Each token's destinations are a
+// 64-bit mask (P <= 64), so per rank a wave ballot over a 64-token tile gives
+// the tile's count (popcount) and every token's place in it (popcount of the
+// lanes below): no sort and no atomics.
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int PK_TILE = 64;   // tokens per wave tile
+
+__device__ __forceinline__ unsigned long long lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// A token's routing held in registers (KP >= k slots, loaded once): every
+// copy of the token is written from these, with no load between its stores.
+template <int KP>
+struct TokenRoute {
+  int id[KP];
+  float w[KP];
+  unsigned long long mask;   // destination ranks (ids outside [0, E) are not sent)
+
+  __device__ __forceinline__ void load(const PackArgs& a, int t, bool live) {
+    mask = 0ull;
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      id[j] = (live && j < a.k) ? a.ids[(size_t)t * a.k + j] : -1;
+      w[j] = (live && j < a.k && a.send_w) ? a.w[(size_t)t * a.k + j] : 0.f;
+      if (id[j] >= 0 && id[j] < a.E) mask |= 1ull << (id[j] / a.per);
+    }
+  }
+
+  // token t's copy to rank r at `row`: the token, its routing (all k slots,
+  // so the receiving rank can pick its own experts), and the row of every
+  // slot the copy serves
+  __device__ __forceinline__ void write_copy(const PackArgs& a, int t, int r, int row) const {
+    a.send_token[row] = t;
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      if (j < a.k) {
+        if (a.send_ids) a.send_ids[(size_t)row * a.k + j] = id[j];
+        if (a.send_w) a.send_w[(size_t)row * a.k + j] = w[j];
+        if (id[j] >= 0 && id[j] < a.E && id[j] / a.per == r) a.send_row[(size_t)t * a.k + j] = row;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void clear_rows(const PackArgs& a, int t) const {
+#pragma unroll
+    for (int j = 0; j < KP; ++j)
+      if (j < a.k) a.send_row[(size_t)t * a.k + j] = -1;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// One wave, T <= 64: counts, offsets and the copy table in one pass.
+// ---------------------------------------------------------------------------
+template <int KP>
+__global__ __launch_bounds__(64) void pack_single_kernel(PackArgs a) {
+  const int t = threadIdx.x;
+  const bool live = t < a.T;
+  TokenRoute<KP> tr;
+  tr.load(a, t, live);
+  const unsigned long long m = tr.mask;
+  if (live) tr.clear_rows(a, t);
+  // lane r ends with rank r's count; exclusive scan over the lanes
+  int cnt = 0;
+  for (int r = 0; r < a.P; ++r) {
+    const unsigned long long b = __ballot((m >> r) & 1ull);
+    if (t == r) cnt = __popcll(b);
+  }
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (t >= o) inc += u;
+  }
+  const int off = inc - cnt;
+  if (t < a.P) {
+    a.send_counts[t] = cnt;
+    a.send_offsets[t] = off;
+  }
+  if (t == a.P - 1) a.send_offsets[a.P] = inc;
+  for (int r = 0; r < a.P; ++r) {
+    const unsigned long long b = __ballot((m >> r) & 1ull);
+    const int base = __shfl(off, r);
+    if ((m >> r) & 1ull) tr.write_copy(a, t, r, base + __popcll(b & lanes_below()));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-tile path.  1: per tile and rank, the number of copies.
+// ---------------------------------------------------------------------------
+template <int KP>
+__global__ __launch_bounds__(256) void pack_count_kernel(PackArgs a) {
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n_tiles = (a.T + PK_TILE - 1) / PK_TILE;
+  if (tile >= n_tiles) return;
+  const int t = tile * PK_TILE + lane;
+  const bool live = t < a.T;
+  TokenRoute<KP> tr;
+  tr.load(a, t, live);
+  const unsigned long long m = tr.mask;
+  if (live) {
+    a.masks[t] = m;
+    tr.clear_rows(a, t);
+  }
+  int cnt = 0;
+  for (int r = 0; r < a.P; ++r) {
+    const unsigned long long b = __ballot((m >> r) & 1ull);
+    if (lane == r) cnt = __popcll(b);
+  }
+  if (lane < a.P) a.tile_counts[(size_t)tile * a.P + lane] = cnt;
+}
+
+// 2: per rank, exclusive scan of its tile counts (one wave per rank, 64
+// tiles per step with a carry), then the rank offsets.
+__global__ __launch_bounds__(1024) void pack_scan_kernel(PackArgs a) {
+  __shared__ int s_total[64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int n_tiles = (a.T + PK_TILE - 1) / PK_TILE;
+  for (int r = wid; r < a.P; r += nw) {
+    int carry = 0;
+    for (int t0 = 0; t0 < n_tiles; t0 += 64) {
+      const int tile = t0 + lane;
+      const int c = tile < n_tiles ? a.tile_counts[(size_t)tile * a.P + r] : 0;
+      int inc = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+      }
+      if (tile < n_tiles) a.tile_base[(size_t)tile * a.P + r] = carry + inc - c;
+      carry += __shfl(inc, 63);
+    }
+    if (lane == 0) s_total[r] = carry;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const int c = lane < a.P ? s_total[lane] : 0;
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o);
+      if (lane >= o) inc += u;
+    }
+    if (lane < a.P) {
+      a.send_counts[lane] = c;
+      a.send_offsets[lane] = inc - c;
+    }
+    if (lane == a.P - 1) a.send_offsets[a.P] = inc;
+  }
+}
+
+// 3: the copy table.
+template <int KP>
+__global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n_tiles = (a.T + PK_TILE - 1) / PK_TILE;
+  if (tile >= n_tiles) return;
+  const int t = tile * PK_TILE + lane;
+  const bool live = t < a.T;
+  TokenRoute<KP> tr;
+  tr.load(a, t, live);
+  const unsigned long long m = tr.mask;
+  const int rb = lane < a.P ? a.send_offsets[lane] + a.tile_base[(size_t)tile * a.P + lane] : 0;
+  for (int r = 0; r < a.P; ++r) {
+    const unsigned long long b = __ballot((m >> r) & 1ull);
+    const int base = __shfl(rb, r);
+    if ((m >> r) & 1ull) tr.write_copy(a, t, r, base + __popcll(b & lanes_below()));
+  }
+}
+
+// x_send[row] = x[send_token[row]] for the rows that exist (send_offsets[P]
+// on the device); one wave per row, every 16-byte load of a lane issued
+// before its stores.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* __restrict__ x,
+                                                        const int32_t* __restrict__ send_token,
+                                                        const int32_t* __restrict__ n_rows, int P,
+                                                        int row_vecs, uint4* __restrict__ out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows[P]) return;
+  // 16-byte vectors as a clang vector type: an array of them stays in
+  // registers (an array of the HIP uint4 struct would go to scratch)
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u* src = reinterpret_cast<const v4u*>(x) + (size_t)send_token[row] * row_vecs;
+  v4u* dst = reinterpret_cast<v4u*>(out) + (size_t)row * row_vecs;
+  constexpr int B = 8;
+  for (int c0 = lane; c0 < row_vecs; c0 += 64 * B) {
+    v4u v[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) v[i] = src[min(c0 + 64 * i, row_vecs - 1)];
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+      if (c0 + 64 * i < row_vecs) dst[c0 + 64 * i] = v[i];
+  }
+}
+
+// y[t] = sum of y_ret over t's distinct copy rows, ascending (rank order),
+// in float32, rounded once.  One 256-thread block per token; thread i takes
+// the 16-byte columns i, i + 256, ...
+template <int KP, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(256) void unpack_sum_kernel(const void* __restrict__ y_ret,
+                                                         const int32_t* __restrict__ send_row,
+                                                         int T, int k, int H,
+                                                         void* __restrict__ y) {
+  const int t = blockIdx.x;
+  // t's distinct copy rows, ascending, computed by every thread in registers
+  int rj[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) rj[j] = j < k ? send_row[(size_t)t * k + j] : -1;
+  int rows[KP];
+  int n_rows = 0, last = -1;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    int row = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < KP; ++j)
+      if (rj[j] > last && rj[j] < row) row = rj[j];
+    rows[i] = row;
+    if (row != 0x7fffffff) {
+      last = row;
+      n_rows = i + 1;
+    }
+  }
+  constexpr int EPV = 8;                            // columns per step (8 bf16 or 2 x 4 f32)
+  const int nv = H / EPV;
+#pragma unroll 2
+  for (int c = threadIdx.x; c < nv; c += 256) {
+    float acc[EPV];
+#pragma unroll
+    for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      if (i >= n_rows) break;
+      const int row = rows[i];
+      float v[EPV];
+      if constexpr (IN_BF16) {
+        const uint4 raw = reinterpret_cast<const uint4*>(y_ret)[(size_t)row * nv + c];
+        unpack_bf16x8(raw, v);
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(y_ret) + ((size_t)row * nv + c) * 2;
+        const float4 u0 = p[0], u1 = p[1];
+        v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+        v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+      }
+#pragma unroll
+      for (int q = 0; q < EPV; ++q) acc[q] += v[q];
+    }
+    if constexpr (OUT_BF16) {
+      reinterpret_cast<uint4*>(y)[(size_t)t * nv + c] =
+          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    } else {
+      float4* p = reinterpret_cast<float4*>(y) + ((size_t)t * nv + c) * 2;
+      p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+template <int KP>
+hipError_t launch_unpack_kp(const void* y_ret, int y_ret_dt, const int32_t* send_row, int T, int k,
+                            int H, void* y, int dt, hipStream_t st) {
+  const int blocks = T;
+  if (y_ret_dt == 1 && dt == 1)
+    unpack_sum_kernel<KP, true, true><<<blocks, 256, 0, st>>>(y_ret, send_row, T, k, H, y);
+  else if (y_ret_dt == 1)
+    unpack_sum_kernel<KP, true, false><<<blocks, 256, 0, st>>>(y_ret, send_row, T, k, H, y);
+  else if (dt == 1)
+    unpack_sum_kernel<KP, false, true><<<blocks, 256, 0, st>>>(y_ret, send_row, T, k, H, y);
+  else
+    unpack_sum_kernel<KP, false, false><<<blocks, 256, 0, st>>>(y_ret, send_row, T, k, H, y);
+  return hipGetLastError();
+}
+
+template <int KP>
+void launch_pack_kp(const PackArgs& a, hipStream_t st) {
+  if (a.T <= PK_TILE) {   // also T = 0: zero counts and offsets
+    pack_single_kernel<KP><<<1, 64, 0, st>>>(a);
+  } else {
+    const int n_tiles = (a.T + PK_TILE - 1) / PK_TILE;
+    const int blocks = (n_tiles + 3) / 4;
+    pack_count_kernel<KP><<<blocks, 256, 0, st>>>(a);
+    pack_scan_kernel<<<1, 1024, 0, st>>>(a);
+    pack_scatter_kernel<KP><<<blocks, 256, 0, st>>>(a);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_by_rank(const PackArgs& a, const void* x, int H, int elt_bytes, void* x_send,
+                               int max_rows, hipStream_t st) {
+  if (a.k <= 8) launch_pack_kp<8>(a, st);
+  else launch_pack_kp<32>(a, st);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !x || max_rows <= 0) return err;
+  copy_rows_kernel<<<(max_rows + 3) / 4, 256, 0, st>>>(
+      static_cast<const uint4*>(x), a.send_token, a.send_offsets, a.P, H * elt_bytes / 16,
+      static_cast<uint4*>(x_send));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int T, int k,
+                             int H, void* y, int dt, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (k <= 8) return launch_unpack_kp<8>(y_ret, y_ret_dt, send_row, T, k, H, y, dt, st);
+  return launch_unpack_kp<32>(y_ret, y_ret_dt, send_row, T, k, H, y, dt, st);
+}
+
+}  // namespace moe

@@ -63,6 +63,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Order one wave's LDS accesses across its lanes: what any lane wrote before
+// this point is what every lane reads after it.  The hardware keeps a wave's
+// LDS operations in order; the fences and the wave barrier stop the compiler
+// from moving a lane's reads above other lanes' writes (it may, for a lane
+// that skips those writes, in its single-thread view).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of n ints held in LDS (n <= 4 * blockDim.x,
 // blockDim.x a multiple of 64 and at most 1024).  `data` is replaced by its

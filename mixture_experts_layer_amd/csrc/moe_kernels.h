@@ -101,6 +101,26 @@ hipError_t launch_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_
                           const float* w, int T, int k, int H, const void* y_shared, void* y,
                           int dt, hipStream_t st);
 
+// Token copies packed by destination rank (dispatch.hip).
+struct PackArgs {
+  const int32_t* ids;       // [T][k]
+  const float* w;           // [T][k] or null (when send_w is null)
+  int T, k, E, P, per;      // per = E / P experts per rank
+  int32_t* send_counts;     // [P]
+  int32_t* send_offsets;    // [P + 1]
+  int32_t* send_token;      // [rows]
+  int32_t* send_row;        // [T][k]
+  int32_t* send_ids;        // [rows][k] or null
+  float* send_w;            // [rows][k] or null
+  unsigned long long* masks;  // [T] (multi-tile path)
+  int32_t* tile_counts;     // [n_tiles][P]
+  int32_t* tile_base;       // [n_tiles][P]
+};
+hipError_t launch_pack_by_rank(const PackArgs& a, const void* x, int H, int elt_bytes, void* x_send,
+                               int max_rows, hipStream_t st);
+hipError_t launch_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int T, int k,
+                             int H, void* y, int dt, hipStream_t st);
+
 // Single-launch decode path (decode.hip).
 constexpr int DECODE_MAX_T = 64;         // tokens: one 64-bit mask per expert
 constexpr int DECODE_MAX_E = 256;        // E and E_loc

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(moe_\w+)", out))
@@ -182,3 +182,28 @@ def test_layer_path_choice():
         M.moe_layer_path(tp, -1)
     with pytest.raises(M.MoEError):
         M.moe_layer_path(desc(k=0), 1)
+
+
+def test_pack_and_unpack_reject_before_launch():
+    with pytest.raises(M.MoEError) as e:     # E not divisible by P
+        M.moe_pack_by_rank(P, None, 4, 2, 10, 4, None, 0, 0, P, P, P, P, None, None, None, None, 0,
+                           stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:     # more than 64 ranks
+        M.moe_pack_by_rank(P, None, 4, 2, 128, 128, None, 0, 0, P, P, P, P, None, None, None,
+                           None, 0, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(M.MoEError) as e:     # weights requested without topk_w
+        M.moe_pack_by_rank(P, None, 4, 2, 8, 4, None, 0, 0, P, P, P, P, None, P, None, None, 0,
+                           stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:     # multi-tile batch without workspace
+        M.moe_pack_by_rank(P, None, 100, 2, 8, 4, None, 0, 0, P, P, P, P, None, None, None, None,
+                           0, stream=0)
+    assert e.value.status == 3
+    assert M.moe_pack_workspace_size(100, 2, 4) >= 100 * 8
+    assert M.moe_pack_workspace_size(10, 2, 65) == 0
+    with pytest.raises(M.MoEError) as e:
+        M.moe_unpack_sum(P, 1, P, 4, 2, 100, P, 1, stream=0)   # H not a multiple of 32
+    assert e.value.status == 2
+    M.moe_unpack_sum(P, 1, P, 0, 2, 256, P, 1, stream=0)      # T = 0 is a no-op
