@@ -28,7 +28,9 @@ in the design notes of the repository):
   * the selection-only bias of the sigmoid gating is added to the logit;
   * a shared expert is added with weight 1 after the routed sum;
   * token copies packed for the expert-parallel dispatch are ordered by
-    destination rank, then by token (one copy per token and rank).
+    destination rank, then by token (one copy per token and rank);
+  * the EP <-> TP weight reshard cuts the same intermediate range from the
+    gate and the up half, as tp_shard does.
 
 Parity status: every function below is pinned by the `-m "not gpu"` tests in
 tests/test_oracle_pins.py (worked examples printed on the pages, closed forms,
@@ -454,6 +456,84 @@ def tp_shard(w13, w2, rank, P):
     w13_r = np.concatenate([w13[:, lo:hi, :], w13[:, i_dim + lo:i_dim + hi, :]], axis=1)
     w2_r = w2[:, :, lo:hi]
     return w13_r, w2_r
+
+
+def _tp_rows(I, P, p):
+    """Rows of the stacked gate/up axis that TP rank p holds: intermediate
+    indices [p*I/P, (p+1)*I/P) of the gate half, then the same of the up half
+    (the reading of tp_shard)."""
+    s = I // P
+    return np.concatenate([np.arange(p * s, (p + 1) * s), I + np.arange(p * s, (p + 1) * s)])
+
+
+def reshard_ep_to_tp_pack(w13_ep, w2_ep, P):
+    """Local pack of the EP -> TP weight reshard: for every peer p the slice of
+    this rank's experts that p holds after the switch, grouped by p.
+
+    [Moebius notes] section 3.1, Algorithm 1 steps 1-2 (chunk per peer,
+    concatenated into the All-to-All send buffer).  The algorithm writes the
+    chunk as a contiguous cut of the stacked 2I axis; read, as for tp_shard,
+    as the same intermediate range of the gate and of the up half (so SwiGLU
+    stays local), and W2 cut on its input columns by that range.
+
+    w13_ep: [E/P, 2I, H], w2_ep: [E/P, H, I]
+    -> send13 [P, E/P, 2I/P, H], send2 [P, E/P, H, I/P]
+    """
+    w13_ep = np.asarray(w13_ep)
+    w2_ep = np.asarray(w2_ep)
+    I = w2_ep.shape[2]
+    if I % P:
+        raise ValueError("I must be divisible by P")
+    s = I // P
+    send13 = np.stack([w13_ep[:, _tp_rows(I, P, p), :] for p in range(P)])
+    send2 = np.stack([w2_ep[:, :, p * s:(p + 1) * s] for p in range(P)])
+    return send13, send2
+
+
+def all_to_all(send):
+    """The exchange between P ranks, simulated: send[r][p] is what rank r
+    sends to rank p; recv[p][r] = send[r][p].  [Moebius notes] section 3.1,
+    Algorithm 1 step 3."""
+    P = len(send)
+    return [[send[r][p] for r in range(P)] for p in range(P)]
+
+
+def reshard_ep_to_tp_place(recv13, recv2):
+    """Algorithm 1 step 4: rank r's received chunks, in peer order, are its TP
+    layout.  recv13[p]: [E/P, 2I/P, H] from peer p -> W_TP [E, 2I/P, H];
+    recv2[p]: [E/P, H, I/P] -> W2_TP [E, H, I/P]."""
+    return np.concatenate(list(recv13), axis=0), np.concatenate(list(recv2), axis=0)
+
+
+def reshard_tp_to_ep_split(w13_tp, w2_tp, P):
+    """Algorithm 2 steps 1-2: the TP weights split by expert owner (peer p
+    receives experts [p*E/P, (p+1)*E/P) of this rank's slice).
+    w13_tp: [E, 2I/P, H], w2_tp: [E, H, I/P] -> ([P, E/P, 2I/P, H], [P, E/P, H, I/P])."""
+    w13_tp = np.asarray(w13_tp)
+    w2_tp = np.asarray(w2_tp)
+    E = w13_tp.shape[0]
+    n = E // P
+    return (np.stack([w13_tp[p * n:(p + 1) * n] for p in range(P)]),
+            np.stack([w2_tp[p * n:(p + 1) * n] for p in range(P)]))
+
+
+def reshard_tp_to_ep_interleave(recv13, recv2):
+    """Algorithm 2 step 4: each peer p's slice of every local expert is put
+    back at p's rows of the stacked axis (gate and up halves, the reading of
+    tp_shard) and p's input columns of W2.
+    recv13 [P, E/P, 2I/P, H], recv2 [P, E/P, H, I/P] -> W_EP [E/P, 2I, H],
+    W2_EP [E/P, H, I]."""
+    recv13 = np.asarray(recv13)
+    recv2 = np.asarray(recv2)
+    P, n, two_s, H = recv13.shape
+    s = two_s // 2
+    I = s * P
+    w13 = np.empty((n, 2 * I, H), dtype=recv13.dtype)
+    w2 = np.empty((n, recv2.shape[2], I), dtype=recv2.dtype)
+    for p in range(P):
+        w13[:, _tp_rows(I, P, p), :] = recv13[p]
+        w2[:, :, p * s:(p + 1) * s] = recv2[p]
+    return w13, w2
 
 
 def touched_experts_expected(E, k, n):

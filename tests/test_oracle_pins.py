@@ -297,6 +297,75 @@ def test_unpack_sum_adds_each_copy_once_in_rank_order():
     assert O.unpack_sum(y_ret, send_row).tolist() == [[101.0, 202.0], [10.0, 20.0]]
 
 
+# ---------------------------------------------------------------- EP <-> TP weight reshard
+
+def _ep_weights(seed, P=4, n=2, I=8, H=5):
+    r = rng(seed)
+    return r.standard_normal((P * n, 2 * I, H)), r.standard_normal((P * n, H, I))
+
+
+def test_reshard_ep_to_tp_gives_every_rank_its_tp_shard():
+    """Algorithm 1 on P simulated ranks: each rank ends with exactly the
+    tensor-parallel share of the full weights (tp_shard, pinned above)."""
+    P = 4
+    w13, w2 = _ep_weights(40, P=P)
+    n = w13.shape[0] // P
+    sends = [O.reshard_ep_to_tp_pack(w13[r * n:(r + 1) * n], w2[r * n:(r + 1) * n], P)
+             for r in range(P)]
+    recv13 = O.all_to_all([s[0] for s in sends])
+    recv2 = O.all_to_all([s[1] for s in sends])
+    for r in range(P):
+        t13, t2 = O.reshard_ep_to_tp_place(recv13[r], recv2[r])
+        ref13, ref2 = O.tp_shard(w13, w2, r, P)
+        assert np.array_equal(t13, ref13) and np.array_equal(t2, ref2)
+
+
+def test_reshard_tp_to_ep_inverts_ep_to_tp():
+    P = 4
+    w13, w2 = _ep_weights(41, P=P)
+    n = w13.shape[0] // P
+    tp = [O.tp_shard(w13, w2, r, P) for r in range(P)]
+    splits = [O.reshard_tp_to_ep_split(t13, t2, P) for t13, t2 in tp]
+    recv13 = O.all_to_all([sp[0] for sp in splits])
+    recv2 = O.all_to_all([sp[1] for sp in splits])
+    for r in range(P):
+        e13, e2 = O.reshard_tp_to_ep_interleave(recv13[r], recv2[r])
+        assert np.array_equal(e13, w13[r * n:(r + 1) * n])
+        assert np.array_equal(e2, w2[r * n:(r + 1) * n])
+
+
+def test_reshard_volume_invariance_and_traffic():
+    """[Moebius notes] eq. (6): a rank holds E * 2I * H / P gate/up elements in
+    both layouts; section 3.1: it sends (P - 1)/P of them to its peers."""
+    P = 4
+    w13, w2 = _ep_weights(42, P=P)
+    E, twoI, H = w13.shape
+    n = E // P
+    send13, _ = O.reshard_ep_to_tp_pack(w13[:n], w2[:n], P)
+    assert send13.size == w13[:n].size == E * twoI * H // P
+    assert O.tp_shard(w13, w2, 0, P)[0].size == E * twoI * H // P
+    to_peers = sum(send13[p].size for p in range(P) if p != 0)
+    assert to_peers == (P - 1) * send13.size // P
+
+
+def test_resharded_weights_compute_the_same_layer():
+    """The same function over byte-identical weights: the TP shares built by
+    the reshard sum to the EP shares' output."""
+    L = tiny_layer(43, T=6, E=8, I=8, H=8)
+    P, k, mode = 4, 2, 2
+    n = 8 // P
+    y_full, _ = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode)
+    sends = [O.reshard_ep_to_tp_pack(L["w13"][r * n:(r + 1) * n], L["w2"][r * n:(r + 1) * n], P)
+             for r in range(P)]
+    recv13 = O.all_to_all([s[0] for s in sends])
+    recv2 = O.all_to_all([s[1] for s in sends])
+    y_tp = 0
+    for r in range(P):
+        t13, t2 = O.reshard_ep_to_tp_place(recv13[r], recv2[r])
+        y_tp = y_tp + O.moe_layer(L["x"], L["w_r"], t13, t2, k, mode)[0]
+    np.testing.assert_allclose(y_tp, y_full, rtol=0, atol=1e-13 * np.abs(y_full).max())
+
+
 # ---------------------------------------------------------------- experts
 
 def test_silu_identities():
