@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dispatch", action="store_true",
                     help="skip the expert-parallel dispatch packing measurement")
+    ap.add_argument("--no-reshard", action="store_true",
+                    help="skip the EP <-> TP weight reshard measurement")
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
@@ -311,6 +313,61 @@ def dispatch_bench(steps, warmup, P=8, Ts=(64, 4096)):
 
 
 # ---------------------------------------------------------------------------
+# EP <-> TP weight reshard, the data movement on one rank
+# ---------------------------------------------------------------------------
+
+def reshard_bench(steps, warmup, P=8):
+    """moe_reshard_ep_to_tp_pack and moe_reshard_tp_to_ep_interleave on one
+    rank's share of the Qwen3-235B-A22B-shaped layer at P = 8 (16 whole
+    experts, I = 1536, H = 4096, bf16), timed by HIP-graph replay.
+    Algorithmic bytes: every weight byte of the share read once and written
+    once."""
+    import torch
+    import mixture_experts_layer_amd as M
+    import workloads as W
+    cfg = W.CONFIGS["qwen3_ep_all128"]
+    n, I, H = cfg.E // P, cfg.I, cfg.H
+    g = torch.Generator(device="cuda").manual_seed(0)
+    w13 = torch.randn((n, 2 * I, H), generator=g, device="cuda").to(torch.bfloat16)
+    w2 = torch.randn((n, H, I), generator=g, device="cuda").to(torch.bfloat16)
+    c13 = torch.empty((P, n, 2 * I // P, H), dtype=torch.bfloat16, device="cuda")
+    c2 = torch.empty((P, n, H, I // P), dtype=torch.bfloat16, device="cuda")
+    o13, o2 = torch.empty_like(w13), torch.empty_like(w2)
+    dt = M.dtype_code(w13)
+    nbytes = 2 * (w13.numel() + w2.numel()) * 2
+    res = dict(workload="qwen3_235b_a22b expert weights, one of %d ranks (%d experts, I=%d, H=%d)"
+               % (P, n, I, H), weight_bytes=(w13.numel() + w2.numel()) * 2)
+    for name, fn in (
+            ("ep_to_tp_pack", lambda: M.moe_reshard_ep_to_tp_pack(w13, w2, n, I, H, P, dt, c13, c2)),
+            ("tp_to_ep_interleave",
+             lambda: M.moe_reshard_tp_to_ep_interleave(c13, c2, n, I, H, P, dt, o13, o2))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(4):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // 4)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / (reps * 4)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = dict(ms=round(ms, 4), algorithmic_bytes=int(nbytes), achieved_GBs=round(gbs, 1),
+                         peak_GBs=HBM_PEAK_GBS, frac=round(gbs / HBM_PEAK_GBS, 4))
+    torch.cuda.synchronize()
+    assert torch.equal(o13, w13) and torch.equal(o2, w2), "reshard round trip changed the weights"
+    print(f"# reshard: pack {res['ep_to_tp_pack']['ms']} ms ({res['ep_to_tp_pack']['frac']}), "
+          f"interleave {res['tp_to_ep_interleave']['ms']} ms ({res['tp_to_ep_interleave']['frac']})",
+          file=sys.stderr, flush=True)
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ---------------------------------------------------------------------------
 
@@ -473,6 +530,10 @@ def main():
     if not args.no_dispatch:
         dispatch = dispatch_bench(max(args.steps, 20), args.warmup)
 
+    reshard = None
+    if not args.no_reshard:
+        reshard = reshard_bench(max(args.steps, 20), args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, args.cpu_sample)
@@ -506,6 +567,7 @@ def main():
                     "imbalance_ratio": round(imb, 3)},
         "sweep": sweep,
         "dispatch": dispatch,
+        "reshard": reshard,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -225,6 +225,40 @@ int moe_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int
                    void* y, int dt, void* stream);
 
 /*
+ * moe_reshard_ep_to_tp_pack / moe_reshard_tp_to_ep_interleave -- the two
+ * data movements of the EP <-> TP expert-weight reshard on one rank.
+ *   [Moebius notes] section 3 (eq. (6)-(8): the two layouts hold the same
+ *   volume per rank; Algorithm 1 steps 1-2 pack per peer before the
+ *   All-to-All, whose output is already the TP layout; Algorithm 2 step 4
+ *   interleaves the received slices into whole experts; Figure 2).
+ *
+ *   P ranks; E_rank = E/P experts per rank in the EP layout; s = I/P.
+ *   EP layout:    w13_ep[E_rank][2I][H] (gate rows [0, I), up rows [I, 2I)),
+ *                 w2_ep[E_rank][H][I].
+ *   Chunk layout: w13_chunks[P][E_rank][2s][H], w2_chunks[P][E_rank][H][s]:
+ *                 chunk p of expert e holds gate rows [p*s, (p+1)*s) then
+ *                 up rows I + [p*s, (p+1)*s) (the same intermediate range of
+ *                 both halves, so SwiGLU stays local to a TP rank), and the
+ *                 same input columns of W2.
+ *   pack:        EP layout -> chunks (chunk p goes to peer p).  After the
+ *                All-to-All, rank r's received chunks, in peer order, are its
+ *                TP layout w13_tp[E][2s][H], w2_tp[E][H][s].
+ *   interleave:  chunks received from each peer p (p's TP slice of this
+ *                rank's experts; in the TP layout they are rows
+ *                [r*E_rank, (r+1)*E_rank) of peer p's w13_tp / w2_tp) ->
+ *                EP layout.  The inverse of pack.
+ *   dtype dt; either the W13 or the W2 pair may be NULL (both members of a
+ *   pair NULL).  Requires I divisible by P, H*elt and s*elt multiples of 16
+ *   bytes, and each tensor below 32 GiB.  Source and destination must not
+ *   overlap.
+ */
+int moe_reshard_ep_to_tp_pack(const void* w13_ep, const void* w2_ep, int E_rank, int I, int H,
+                              int P, int dt, void* w13_send, void* w2_send, void* stream);
+int moe_reshard_tp_to_ep_interleave(const void* w13_recv, const void* w2_recv, int E_rank, int I,
+                                    int H, int P, int dt, void* w13_ep, void* w2_ep,
+                                    void* stream);
+
+/*
  * moe_layer -- the whole share of the layer in one call:
  *   route -> permute -> grouped SwiGLU GEMMs (gather fused) -> shared expert
  *   -> combine, all enqueued on `stream` without host synchronisation.

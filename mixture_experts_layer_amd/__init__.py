@@ -19,7 +19,8 @@ from ._abi import (MOE_F32, MOE_BF16, MOE_OK, GATE_TOPK_SOFTMAX, GATE_SOFTMAX_TO
 __all__ = [
     "MoEError", "lib", "get_lib", "moe_abi_version", "moe_status_str", "moe_route", "moe_permute",
     "moe_permute_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
-    "moe_combine", "moe_pack_by_rank", "moe_pack_workspace_size", "moe_unpack_sum", "moe_layer",
+    "moe_combine", "moe_pack_by_rank", "moe_pack_workspace_size", "moe_unpack_sum",
+    "moe_reshard_ep_to_tp_pack", "moe_reshard_tp_to_ep_interleave", "moe_layer",
     "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
     "moe_layer_workspace_size",
     "layer_workspace", "layer_desc", "dtype_code", "LAYER_SYNC_BYTES",
@@ -136,6 +137,20 @@ def moe_pack_by_rank(topk_ids, topk_w, T, k, E, P, x, H, dt, send_counts, send_o
 def moe_unpack_sum(y_ret, y_ret_dt, send_row, T, k, H, y, dt, stream=None):
     _check("moe_unpack_sum", lib.moe_unpack_sum(_p(y_ret), y_ret_dt, _p(send_row), T, k, H, _p(y),
                                                 dt, _stream(stream)))
+
+
+def moe_reshard_ep_to_tp_pack(w13_ep, w2_ep, E_rank, I, H, P, dt, w13_send, w2_send,
+                              stream=None):
+    _check("moe_reshard_ep_to_tp_pack",
+           lib.moe_reshard_ep_to_tp_pack(_p(w13_ep), _p(w2_ep), E_rank, I, H, P, dt, _p(w13_send),
+                                         _p(w2_send), _stream(stream)))
+
+
+def moe_reshard_tp_to_ep_interleave(w13_recv, w2_recv, E_rank, I, H, P, dt, w13_ep, w2_ep,
+                                    stream=None):
+    _check("moe_reshard_tp_to_ep_interleave",
+           lib.moe_reshard_tp_to_ep_interleave(_p(w13_recv), _p(w2_recv), E_rank, I, H, P, dt,
+                                               _p(w13_ep), _p(w2_ep), _stream(stream)))
 
 
 def layer_desc(H, E, k, I_loc, mode, dt, w_router, w13, w2, e_begin=0, e_end=None, I_shared=0,

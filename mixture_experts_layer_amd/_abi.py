@@ -53,6 +53,10 @@ _SIGS = {
                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_unpack_sum": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p, c_int,
                                c_void_p]),
+    "moe_reshard_ep_to_tp_pack": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                          c_void_p, c_void_p, c_void_p]),
+    "moe_reshard_tp_to_ep_interleave": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                                c_int, c_void_p, c_void_p, c_void_p]),
     "moe_layer_workspace_size": (c_size_t, [ctypes.POINTER(MoELayerDesc), c_int]),
     "moe_layer": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p, c_void_p,
                           c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoe_mi355x.so")
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "decode.hip", "dispatch.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "decode.hip", "dispatch.hip", "reshard.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -440,6 +440,35 @@ int moe_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int
       launch_unpack_sum(y_ret, y_ret_dt, send_row, T, k, H, y, dt, static_cast<hipStream_t>(stream)));
 }
 
+static int reshard_call(bool pack, const void* w13_src, const void* w2_src, int n, int I, int H,
+                        int P, int dt, void* w13_dst, void* w2_dst, void* stream) {
+  if (!valid_dt(dt) || n < 1 || I <= 0 || P < 1 || H <= 0) return MOE_ERR_INVALID_ARG;
+  if (I % P) return MOE_ERR_INVALID_ARG;
+  if (!w13_src != !w13_dst || !w2_src != !w2_dst) return MOE_ERR_INVALID_ARG;
+  if (!w13_src && !w2_src) return MOE_ERR_INVALID_ARG;
+  const int elt = elt_bytes(dt);
+  if ((H * elt) % 16 || ((I / P) * elt) % 16) return MOE_ERR_UNSUPPORTED;
+  const long long v13 = (long long)n * 2 * I * H * elt / 16;
+  const long long v2 = (long long)n * H * I * elt / 16;
+  if (v13 >= (1ll << 31) || v2 >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[] = {w13_src, w2_src, w13_dst, w2_dst};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_reshard(pack, w13_src, w2_src, n, I, H, P, elt, w13_dst, w2_dst,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int moe_reshard_ep_to_tp_pack(const void* w13_ep, const void* w2_ep, int E_rank, int I, int H,
+                              int P, int dt, void* w13_send, void* w2_send, void* stream) {
+  return reshard_call(true, w13_ep, w2_ep, E_rank, I, H, P, dt, w13_send, w2_send, stream);
+}
+
+int moe_reshard_tp_to_ep_interleave(const void* w13_recv, const void* w2_recv, int E_rank, int I,
+                                    int H, int P, int dt, void* w13_ep, void* w2_ep,
+                                    void* stream) {
+  return reshard_call(false, w13_recv, w2_recv, E_rank, I, H, P, dt, w13_ep, w2_ep, stream);
+}
+
 size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max) {
   if (check_desc(d) != MOE_OK || T_max < 0) return 0;
   return layer_layout(d, T_max, nullptr, nullptr);

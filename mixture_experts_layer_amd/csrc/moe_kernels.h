@@ -121,6 +121,12 @@ hipError_t launch_pack_by_rank(const PackArgs& a, const void* x, int H, int elt_
 hipError_t launch_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int T, int k,
                              int H, void* y, int dt, hipStream_t st);
 
+// EP <-> TP weight reshard, local halves (reshard.hip).  pack: EP weights ->
+// per-peer chunks; otherwise per-peer chunks -> EP weights.  Either pair of
+// pointers may be null.
+hipError_t launch_reshard(bool pack, const void* w13_src, const void* w2_src, int n, int I, int H,
+                          int P, int elt_bytes, void* w13_dst, void* w2_dst, hipStream_t st);
+
 // Single-launch decode path (decode.hip).
 constexpr int DECODE_MAX_T = 64;         // tokens: one 64-bit mask per expert
 constexpr int DECODE_MAX_E = 256;        // E and E_loc

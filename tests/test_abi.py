@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(moe_\w+)", out))
@@ -207,3 +207,15 @@ def test_pack_and_unpack_reject_before_launch():
         M.moe_unpack_sum(P, 1, P, 4, 2, 100, P, 1, stream=0)   # H not a multiple of 32
     assert e.value.status == 2
     M.moe_unpack_sum(P, 1, P, 0, 2, 256, P, 1, stream=0)      # T = 0 is a no-op
+
+
+def test_reshard_rejects_before_launch():
+    for args, status in (((P, P, 2, 100, 256, 8, 1, P, P), 1),       # I not divisible by P
+                         ((P, P, 2, 96, 256, 8, 1, P, P), 2),        # I/P * 2 bytes not 16-aligned
+                         ((P, None, 2, 128, 256, 8, 1, P, P), 1),    # half a W2 pair
+                         ((None, None, 2, 128, 256, 8, 1, None, None), 1),
+                         ((MIS, P, 2, 128, 256, 8, 1, P, P), 1)):
+        for fn in (M.moe_reshard_ep_to_tp_pack, M.moe_reshard_tp_to_ep_interleave):
+            with pytest.raises(M.MoEError) as e:
+                fn(*args, stream=0)
+            assert e.value.status == status, args
