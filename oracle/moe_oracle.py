@@ -30,7 +30,9 @@ in the design notes of the repository):
   * token copies packed for the expert-parallel dispatch are ordered by
     destination rank, then by token (one copy per token and rank);
   * the EP <-> TP weight reshard cuts the same intermediate range from the
-    gate and the up half, as tp_shard does.
+    gate and the up half, as tp_shard does;
+  * an expert over capacity keeps its first C (token, slot) pairs in token
+    order.
 
 Parity status: every function below is pinned by the `-m "not gpu"` tests in
 tests/test_oracle_pins.py (worked examples printed on the pages, closed forms,
@@ -218,6 +220,47 @@ def permute(ids, e_begin, e_end):
     return counts, offsets, src_token, dst_row
 
 
+def expert_capacity(capacity_factor, n_assign, E):
+    """C = ceil(capacity_factor * N_a / E).  [MoE guide] section "Capacity、
+    padding 与 token dropping"; [CS349D L8] section 1.4 (N_a = tokens * k)."""
+    return int(np.ceil(capacity_factor * n_assign / E))
+
+
+def permute_capacity(ids, e_begin, e_end, C):
+    """The permutation with a capacity of C (token, slot) pairs per expert.
+
+    [MoE guide] section "Capacity、padding 与 token dropping" and [CS349D L8]
+    section 1.4: an expert over capacity drops the extra assignments, whose
+    contribution becomes zero.  Reading (the pages do not say which pairs an
+    expert keeps): the first C in the stable order of permute(), i.e. token
+    order.
+
+    Returns counts [E_loc] (kept pairs), offsets [E_loc + 1], src_token
+    [kept], dst_row [T, k] (-1 for a pair that is dropped or not local) and
+    the number of dropped local pairs.
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    full, _, _, _ = permute(ids, e_begin, e_end)
+    counts = np.minimum(full, C)
+    offsets = exclusive_offsets(counts)
+    src_token = np.empty(int(offsets[-1]), dtype=np.int64)
+    dst_row = np.full((T, k), -1, dtype=np.int64)
+    seen = np.zeros(e_end - e_begin, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if e_begin <= e < e_end:
+                i = e - e_begin
+                if seen[i] < C:
+                    row = offsets[i] + seen[i]
+                    dst_row[t, j] = row
+                    src_token[row] = t
+                seen[i] += 1
+    dropped = int((full - counts).sum())
+    return counts, offsets, src_token, dst_row, dropped
+
+
 # ---------------------------------------------------------------------------
 # Expert-parallel dispatch: token copies packed by destination rank
 # ---------------------------------------------------------------------------
@@ -375,7 +418,7 @@ def combine(y_perm, dst_row, w, y_shared=None, dtype=np.float64):
 
 def moe_layer(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
               e_begin=0, e_end=None, w13_shared=None, w2_shared=None,
-              logits=None, dtype=np.float64):
+              logits=None, dtype=np.float64, capacity=None):
     """One GPU's share of the MoE layer forward through the permuted data path.
 
     [MoE guide] section "一个 token 为什么要跨 GPU": router -> top-k ids and
@@ -390,8 +433,10 @@ def moe_layer(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
     `logits` may be given (e.g. float32 logits from another implementation) to
     route on exactly those values; otherwise they are computed here.
 
+    `capacity`: C pairs per local expert (permute_capacity); None = dropless.
+
     Returns (y [T, H], aux dict with logits, ids, w, counts, offsets,
-    src_token, dst_row).
+    src_token, dst_row, dropped).
     """
     x = np.asarray(x)
     E = np.asarray(w_r).shape[0] if logits is None else np.asarray(logits).shape[1]
@@ -400,14 +445,19 @@ def moe_layer(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
     if logits is None:
         logits = router_logits(x, w_r, logit_bias, dtype)
     ids, w = route(logits, k, mode, sel_bias)
-    counts, offsets, src_token, dst_row = permute(ids, e_begin, e_end)
+    dropped = 0
+    if capacity is None:
+        counts, offsets, src_token, dst_row = permute(ids, e_begin, e_end)
+    else:
+        counts, offsets, src_token, dst_row, dropped = permute_capacity(ids, e_begin, e_end,
+                                                                         capacity)
     y_perm = grouped_ffn(x, src_token, offsets, w13, w2, dtype)
     y_shared = None
     if w13_shared is not None:
         y_shared = swiglu_expert(x, w13_shared, w2_shared, dtype)
     y = combine(y_perm, dst_row, w, y_shared, dtype)
     aux = dict(logits=logits, ids=ids, w=w, counts=counts, offsets=offsets,
-               src_token=src_token, dst_row=dst_row)
+               src_token=src_token, dst_row=dst_row, dropped=dropped)
     return y, aux
 
 

@@ -197,6 +197,83 @@ def test_permute_expert_range():
     assert np.array_equal(src, order // k)
 
 
+# ---------------------------------------------------------------- capacity and dropping
+
+def test_expert_capacity_formula():
+    # C = ceil(cf * N_a / E): 4096 tokens, k = 8, E = 128
+    assert O.expert_capacity(1.0, 4096 * 8, 128) == 256
+    assert O.expert_capacity(1.25, 4096 * 8, 128) == 320
+    assert O.expert_capacity(1.0, 10, 3) == 4
+
+
+def test_capacity_keeps_first_pairs_in_token_order_brute_force():
+    r = rng(50)
+    T, k, E, C = 120, 3, 8, 20
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)])
+    counts, offsets, src, dst, dropped = O.permute_capacity(ids, 0, E, C)
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")          # library stable sort
+    pos = np.empty_like(order)
+    for e in range(E):
+        sel = order[flat[order] == e]
+        pos[sel] = np.arange(len(sel))              # place in the expert's token order
+    kept = pos < C
+    assert dropped == int((~kept).sum()) == int(np.maximum(np.bincount(flat, minlength=E) - C, 0).sum())
+    assert np.array_equal(counts, np.minimum(np.bincount(flat, minlength=E), C))
+    for t in range(T):
+        for j in range(k):
+            q = t * k + j
+            if kept[q]:
+                e = ids[t, j]
+                assert dst[t, j] == offsets[e] + pos[q] and src[dst[t, j]] == t
+            else:
+                assert dst[t, j] == -1
+
+
+def test_large_capacity_is_dropless():
+    L = tiny_layer(51, T=20)
+    k, mode = 2, 2
+    y0, a0 = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode)
+    C = O.expert_capacity(8.0, 20 * k, 8)         # far above any count
+    y1, a1 = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode, capacity=C)
+    assert a1["dropped"] == 0
+    assert np.array_equal(y0, y1)
+    for key in ("counts", "offsets", "src_token", "dst_row"):
+        assert np.array_equal(a0[key], a1[key])
+
+
+def test_dropping_makes_outputs_depend_on_batch_neighbours():
+    """[CS349D L8] section 1.4: with a capacity, a token's output depends on
+    which other tokens share its batch; dropless it does not."""
+    L = tiny_layer(52, T=24)
+    k, mode = 2, 0
+    y_full, a = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode, capacity=3)
+    assert a["dropped"] > 0
+    # the last token alone keeps all its pairs
+    t = 23
+    y_alone, b = O.moe_layer(L["x"][t:], L["w_r"], L["w13"], L["w2"], k, mode, capacity=3)
+    assert b["dropped"] == 0
+    dropped_t = (a["dst_row"][t] < 0).any()
+    assert dropped_t, "the seed should drop a pair of the last token"
+    assert not np.allclose(y_alone[0], y_full[t])
+    y_free, _ = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode)
+    np.testing.assert_allclose(y_alone[0], y_free[t], rtol=1e-13, atol=1e-14)
+
+
+def test_dropped_pair_contributes_zero():
+    L = tiny_layer(53, T=10)
+    k, mode = 2, 2
+    y, a = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode, capacity=1)
+    ids, w = a["ids"], a["w"]
+    for t in range(10):
+        ref = np.zeros(L["x"].shape[1])
+        for j in range(k):
+            if a["dst_row"][t, j] >= 0:
+                e = ids[t, j]
+                ref += w[t, j] * O.swiglu_expert(L["x"][t:t + 1], L["w13"][e], L["w2"][e])[0]
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- dispatch packing by rank
 
 def test_pack_by_rank_worked_example():
