@@ -61,6 +61,8 @@ def parse():
                     help="skip the expert-parallel dispatch packing measurement")
     ap.add_argument("--no-reshard", action="store_true",
                     help="skip the EP <-> TP weight reshard measurement")
+    ap.add_argument("--no-capacity", action="store_true",
+                    help="skip the capacity-factor (token dropping) measurement")
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
@@ -190,11 +192,15 @@ class Bench:
         reps = max(1, math.ceil(steps / self.copies))
         g.replay()
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record()
         for _ in range(reps):
             g.replay()
+        e1.record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        self.graph_event_ms = e0.elapsed_time(e1) / (reps * self.copies)
         return (t1 - t0) * 1e3 / (reps * self.copies)
 
 
@@ -313,6 +319,44 @@ def dispatch_bench(steps, warmup, P=8, Ts=(64, 4096)):
 
 
 # ---------------------------------------------------------------------------
+# Capacity-factor variant (token dropping) on the timed workload
+# ---------------------------------------------------------------------------
+
+def capacity_bench(bench, steps, warmup, factors=(1.0, 1.25)):
+    """moe_layer_capacity on the bench's own layer and batch: C =
+    ceil(cf * T * k / E) pairs per expert; the hottest expert is capped, at
+    the price of the dropped (token, expert) pairs.  Graph-replayed time
+    beside the dropless time of the same batch."""
+    import torch
+    M, cfg, T = bench.M, bench.cfg, bench.T
+    if cfg.dtype != "bf16":
+        return None
+    dropped = torch.zeros((4,), dtype=torch.int32, device="cuda")
+    saved = bench.layer_fn
+    out = []
+    try:
+        for cf in factors:
+            C = int(math.ceil(cf * T * cfg.k / cfg.E))
+
+            def fn(d, T_, x, y, ws, nb, dbg=None, C=C):
+                M.moe_layer_capacity(d, T_, C, x, y, ws, nb, dbg, dropped)
+
+            bench.layer_fn = fn
+            bench.step(0)
+            torch.cuda.synchronize()
+            n_drop = int(dropped[0].item())
+            ms = bench.timed_graph(steps, warmup)
+            out.append(dict(capacity_factor=cf, capacity=C, dropped_pairs=n_drop,
+                            dropped_frac=round(n_drop / (T * cfg.k), 4), ms=round(ms, 4),
+                            tokens_per_s=round(T / (ms * 1e-3), 1)))
+            print(f"# capacity cf={cf}: C={C}, dropped {n_drop / (T * cfg.k):.3f} of the pairs, "
+                  f"{ms:.4f} ms", file=sys.stderr, flush=True)
+    finally:
+        bench.layer_fn = saved
+    return out
+
+
+# ---------------------------------------------------------------------------
 # EP <-> TP weight reshard, the data movement on one rank
 # ---------------------------------------------------------------------------
 
@@ -418,34 +462,42 @@ def cpu_baseline(bench, n_sample):
 # HBM traffic of the dominant kernel, from the committed counter summary
 # ---------------------------------------------------------------------------
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "qwen3_ep_all128_T8192_gemm_gate_up_traffic.md")
-# every source the gate/up GEMM kernel is compiled from
-KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_amd", "csrc", f)
-                  for f in ("ffn.hip", "moe_device.h", "moe_kernels.h")]
+def _csrc(*names):
+    return [os.path.join(ROOT, "mixture_experts_layer_amd", "csrc", f) for f in names]
 
 
-def kernel_source_sha256():
+# Counter summaries of the kernels a roofline entry is quoted on, each with
+# every source that kernel is compiled from.
+TRAFFIC_PROFILES = {
+    "gemm_gate_up": (os.path.join(ROOT, "profiles", "qwen3_ep_all128_T8192_gemm_gate_up_traffic.md"),
+                     _csrc("ffn.hip", "moe_device.h", "moe_kernels.h")),
+    "decode": (os.path.join(ROOT, "profiles", "qwen3_tp8_rank0_T1_decode_traffic.md"),
+               _csrc("decode.hip", "moe_gate.h", "moe_router.h", "moe_device.h", "moe_kernels.h")),
+}
+
+
+def kernel_source_sha256(kernel="gemm_gate_up"):
     import hashlib
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in TRAFFIC_PROFILES[kernel][1]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def committed_traffic(workload, T):
-    """Bytes per launch of the gate/up GEMM measured with FETCH_SIZE and
-    WRITE_SIZE (scaled by the copy-kernel calibration), if the summary was
-    taken on this workload and on the kernel source as it is now."""
+def committed_traffic(kernel, workload, T):
+    """Bytes per launch of `kernel` measured with FETCH_SIZE and WRITE_SIZE
+    (scaled by the copy-kernel calibration), if its summary was taken on this
+    workload and on the kernel source as it is now."""
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(TRAFFIC_PROFILES[kernel][0]) as f:
             line = next(l for l in f if l.startswith("traffic_json: "))
         rec = json.loads(line[len("traffic_json: "):])
     except (OSError, StopIteration, ValueError):
         return None
     if rec.get("workload") != workload or rec.get("T") != T:
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+    if rec.get("kernel_source_sha256") != kernel_source_sha256(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -484,22 +536,29 @@ def main():
     ms, split = bench.timed_eager(args.steps, args.warmup)
     path = bench.path_of(T)
     l_bound, t_roof_ms, l_frac = layer_roof_frac(cfg, work, ms)
+    ms_graph = bench.timed_graph(args.steps, args.warmup)
     if path == "decode":
-        # one launch covers the whole layer, between stage events 0 and 1
-        # (events 1-5 are recorded back to back after it)
-        t_k = split["route_permute"]
+        # One launch covers the whole layer.  Events around a single launch add
+        # a few microseconds to a kernel of about thirty; the events bracketing
+        # the graph replays (one launch per weight copy, back to back on this
+        # stream) add only the dispatch gap between launches.
+        t_k = bench.graph_event_ms
         roof = decode_roofline_entry(cfg, work, t_k)
-        roof["kernel"] = "single-launch decode kernel (moe_layer stage events 0 -> 1)"
-        roof["traffic"] = None
+        roof["kernel"] = "single-launch decode kernel (graph-replayed launches, events on the launch stream)"
+        roof["traffic"] = committed_traffic("decode", WORKLOAD_NAMES[args.workload], T)
         roof["algorithmic_bytes"] = work["b_alg"]
         roof["avg_launch_ms"] = round(t_k, 4)
     else:
         roof = roofline_entry(cfg, work, split["gemm_gate_up"])
         roof["kernel"] = "grouped gate/up GEMM + SwiGLU (moe_layer stage events 1 -> 2)"
-        roof["traffic"] = committed_traffic(WORKLOAD_NAMES[args.workload], T)
+        roof["traffic"] = committed_traffic("gemm_gate_up", WORKLOAD_NAMES[args.workload], T)
         roof["algorithmic_bytes"] = work["g1_bytes"]
         roof["avg_launch_ms"] = round(split["gemm_gate_up"], 4)
-    ms_graph = bench.timed_graph(args.steps, args.warmup)
+
+    capacity = None
+    if not args.no_capacity and path == "staged":
+        capacity = dict(dropless_ms_graph=round(ms_graph, 4),
+                        variants=capacity_bench(bench, args.steps, args.warmup))
 
     sweep = []
     if not args.no_sweep:
@@ -566,6 +625,7 @@ def main():
         "routing": {"rows": work["rows"], "touched_experts": work["touched"],
                     "imbalance_ratio": round(imb, 3)},
         "sweep": sweep,
+        "capacity": capacity,
         "dispatch": dispatch,
         "reshard": reshard,
         "cpu_baseline": cpu,

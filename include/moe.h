@@ -133,6 +133,27 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e
                 void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute_capacity -- moe_permute with a capacity of `capacity` (token,
+ * slot) pairs per local expert.
+ *   [MoE guide] section "Capacity、padding 与 token dropping" (C =
+ *   ceil(capacity factor * N_a / E); assignments beyond C may be dropped);
+ *   [CS349D L8] section 1.4 (a dropped assignment contributes nothing; the
+ *   output then depends on the other tokens of the batch, which is why the
+ *   default path here is dropless).
+ *
+ *   An expert keeps its first `capacity` pairs in token order; the others get
+ *   dst_row -1 and no row.  counts[i] = kept pairs (<= capacity), offsets and
+ *   src_token as in moe_permute over the kept pairs, so at most
+ *   E_loc * capacity rows exist.  dropped[0] (int32, may be NULL) = the number
+ *   of local pairs dropped.  capacity >= 0 (INT_MAX: moe_permute itself).
+ *   Other arguments and the workspace as for moe_permute.
+ */
+int moe_permute_capacity(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
+                         int capacity, const void* x, int H, int dt,
+                         int32_t* counts, int32_t* offsets, int32_t* src_token, int32_t* dst_row,
+                         void* x_perm, int32_t* dropped, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_grouped_ffn -- grouped SwiGLU expert MLPs over ragged row counts.
  *   [MoE guide] section "Expert GEMM 为什么经常不够大" (expert i computes
  *   [m_i, hidden] @ W_i in one schedule); [Moebius notes] eq. (2)-(4) and
@@ -339,6 +360,16 @@ int moe_layer_path(const moe_layer_desc* d, int T);
  * down GEMM, shared expert, combine), any supported shape and T. */
 int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y,
                      void* ws, size_t ws_bytes, moe_debug_out* dbg, void* stream);
+
+/* Staged path with a capacity of `capacity` pairs per local expert, dropping
+ * the rest as moe_permute_capacity does (the capacity-factor variant of
+ * [MoE guide] section "Capacity、padding 与 token dropping"; not the default,
+ * see [CS349D L8] section 1.4).  dropped[0] (int32, may be NULL) receives the
+ * number of local pairs dropped; debug copies show the kept counts and -1 for
+ * dropped pairs.  capacity >= 0; INT_MAX gives moe_layer_staged exactly. */
+int moe_layer_capacity(const moe_layer_desc* d, int T, int capacity, const void* x, void* y,
+                       void* ws, size_t ws_bytes, moe_debug_out* dbg, int32_t* dropped,
+                       void* stream);
 
 /* Single-launch decode path: router, gating, dispatch metadata, both expert
  * GEMMs, the shared expert and the combine in ONE kernel launch whose

@@ -18,7 +18,8 @@ from ._abi import (MOE_F32, MOE_BF16, MOE_OK, GATE_TOPK_SOFTMAX, GATE_SOFTMAX_TO
 
 __all__ = [
     "MoEError", "lib", "get_lib", "moe_abi_version", "moe_status_str", "moe_route", "moe_permute",
-    "moe_permute_workspace_size", "moe_grouped_ffn", "moe_grouped_ffn_workspace_size",
+    "moe_permute_workspace_size", "moe_permute_capacity", "moe_grouped_ffn",
+    "moe_grouped_ffn_workspace_size", "moe_layer_capacity",
     "moe_combine", "moe_pack_by_rank", "moe_pack_workspace_size", "moe_unpack_sum",
     "moe_reshard_ep_to_tp_pack", "moe_reshard_tp_to_ep_interleave", "moe_layer",
     "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
@@ -102,6 +103,14 @@ def moe_permute(topk_ids, T, k, E, e_begin, e_end, x, H, dt, counts, offsets, sr
     _check("moe_permute", lib.moe_permute(_p(topk_ids), T, k, E, e_begin, e_end, _p(x), H, dt,
                                           _p(counts), _p(offsets), _p(src_token), _p(dst_row),
                                           _p(x_perm), _p(ws), ws_bytes, _stream(stream)))
+
+
+def moe_permute_capacity(topk_ids, T, k, E, e_begin, e_end, capacity, x, H, dt, counts, offsets,
+                         src_token, dst_row, x_perm, dropped, ws, ws_bytes, stream=None):
+    _check("moe_permute_capacity",
+           lib.moe_permute_capacity(_p(topk_ids), T, k, E, e_begin, e_end, capacity, _p(x), H, dt,
+                                    _p(counts), _p(offsets), _p(src_token), _p(dst_row),
+                                    _p(x_perm), _p(dropped), _p(ws), ws_bytes, _stream(stream)))
 
 
 def moe_grouped_ffn_workspace_size(max_rows, E_loc, H, I_loc, dt) -> int:
@@ -192,6 +201,14 @@ def moe_layer_staged(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut
     _check("moe_layer_staged",
            lib.moe_layer_staged(ctypes.byref(desc), T, _p(x), _p(y), _p(ws), ws_bytes,
                                 None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+
+
+def moe_layer_capacity(desc: MoELayerDesc, T, capacity, x, y, ws, ws_bytes,
+                       dbg: MoEDebugOut | None = None, dropped=None, stream=None):
+    _check("moe_layer_capacity",
+           lib.moe_layer_capacity(ctypes.byref(desc), T, capacity, _p(x), _p(y), _p(ws), ws_bytes,
+                                  None if dbg is None else ctypes.byref(dbg), _p(dropped),
+                                  _stream(stream)))
 
 
 def moe_layer_decode(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut | None = None,

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <climits>
+
 #include "moe.h"
 #include "moe_kernels.h"
 
@@ -249,6 +251,7 @@ int moe_route(const void* x, const void* w_router, int dt, int T, int H, int E, 
   a.T = T; a.E = E; a.k = k; a.mode = mode;
   a.do_gate = 1; a.do_permute = 0;
   a.e_begin = 0; a.e_end = E;
+  a.capacity = INT_MAX;
   return hip_status(launch_gate_tiles(a, cdiv(T, TOK_TILE), s));
 }
 
@@ -258,10 +261,12 @@ size_t moe_permute_workspace_size(int T, int k, int E_loc) {
   return align_up((size_t)n_tt * E_loc * 4) * 2 + align_up((size_t)T * k * 4);
 }
 
-int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
-                const void* x, int H, int dt, int32_t* counts, int32_t* offsets,
-                int32_t* src_token, int32_t* dst_row, void* x_perm, void* ws, size_t ws_bytes,
-                void* stream) {
+static int permute_impl(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
+                        int capacity, const void* x, int H, int dt, int32_t* counts,
+                        int32_t* offsets, int32_t* src_token, int32_t* dst_row, void* x_perm,
+                        int32_t* dropped, void* ws, size_t ws_bytes, void* stream) {
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (dropped && !aligned16(dropped)) return MOE_ERR_INVALID_ARG;
   int st = check_route_shape(T, E, k, 0);
   if (st) return st;
   if (e_begin < 0 || e_end > E || e_begin >= e_end) return MOE_ERR_INVALID_ARG;
@@ -298,17 +303,34 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e
   a.single = single ? 1 : 0;
   a.counts = counts; a.offsets = offsets; a.src_token = src_token; a.dst_row = dst_row;
   a.BM = 16; a.tile_map = nullptr; a.n_tiles = nullptr;
+  a.capacity = capacity; a.dropped = dropped;
   MOE_TRY(launch_gate_tiles(a, n_tt, s));
   if (!single) {
     MOE_TRY(launch_permute_scan(tile_counts, n_tt, E_loc, tile_base, counts, offsets, 16, 0, 0,
-                                nullptr, nullptr, s));
+                                nullptr, nullptr, capacity, dropped, s));
     MOE_TRY(launch_permute_scatter(topk_ids, rank, tile_base, offsets, T, k, e_begin, e_end,
-                                   dst_row, src_token, s));
+                                   capacity, dst_row, src_token, s));
   }
   if (x && T > 0)
     MOE_TRY(launch_gather_rows(x, src_token, offsets, E_loc, T * (k < E_loc ? k : E_loc), H,
                                elt_bytes(dt), x_perm, s));
   return MOE_OK;
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
+                const void* x, int H, int dt, int32_t* counts, int32_t* offsets,
+                int32_t* src_token, int32_t* dst_row, void* x_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+  return permute_impl(topk_ids, T, k, E, e_begin, e_end, INT_MAX, x, H, dt, counts, offsets,
+                      src_token, dst_row, x_perm, nullptr, ws, ws_bytes, stream);
+}
+
+int moe_permute_capacity(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
+                         int capacity, const void* x, int H, int dt, int32_t* counts,
+                         int32_t* offsets, int32_t* src_token, int32_t* dst_row, void* x_perm,
+                         int32_t* dropped, void* ws, size_t ws_bytes, void* stream) {
+  return permute_impl(topk_ids, T, k, E, e_begin, e_end, capacity, x, H, dt, counts, offsets,
+                      src_token, dst_row, x_perm, dropped, ws, ws_bytes, stream);
 }
 
 size_t moe_grouped_ffn_workspace_size(int max_rows, int E_loc, int H, int I_loc, int dt) {
@@ -497,8 +519,9 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
   return moe_layer_staged(d, T, x, y, ws, ws_bytes, dbg, stream);
 }
 
-int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
-                     size_t ws_bytes, moe_debug_out* dbg, void* stream) {
+static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
+                             size_t ws_bytes, moe_debug_out* dbg, int capacity, int32_t* dropped,
+                             void* stream) {
   int st = check_layer_call(d, T, x, y, ws, ws_bytes, dbg);
   if (st || T == 0) return st;
   LayerWs l;
@@ -536,12 +559,14 @@ int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y, voi
   a.counts = l.counts; a.offsets = l.offsets; a.src_token = l.src_token; a.dst_row = l.dst_row;
   a.BM = l.BM; a.tile_map = l.tile_map; a.n_tiles = l.n_tiles;
   a.max_rows = l.max_rows; a.max_tiles = l.max_tiles;
+  a.capacity = capacity; a.dropped = dropped;
   MOE_TRY(launch_gate_tiles(a, l.n_tt, s));
   if (!single) {
     MOE_TRY(launch_permute_scan(l.tile_counts, l.n_tt, E_loc, l.tile_base, l.counts, l.offsets,
-                                l.BM, l.max_rows, l.max_tiles, l.tile_map, l.n_tiles, s));
+                                l.BM, l.max_rows, l.max_tiles, l.tile_map, l.n_tiles, capacity,
+                                dropped, s));
     MOE_TRY(launch_permute_scatter(l.ids, l.rank, l.tile_base, l.offsets, T, d->k, d->e_begin,
-                                   d->e_end, l.dst_row, l.src_token, s));
+                                   d->e_end, capacity, l.dst_row, l.src_token, s));
   }
   MOE_TRY(mark(1));
   // a6-a7: grouped SwiGLU GEMMs, gather fused into the first
@@ -572,6 +597,19 @@ int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y, voi
                          d->I_shared > 0 ? l.y_s : nullptr, y, d->dt, s));
   MOE_TRY(mark(5));
   return MOE_OK;
+}
+
+int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
+                     size_t ws_bytes, moe_debug_out* dbg, void* stream) {
+  return layer_staged_impl(d, T, x, y, ws, ws_bytes, dbg, INT_MAX, nullptr, stream);
+}
+
+int moe_layer_capacity(const moe_layer_desc* d, int T, int capacity, const void* x, void* y,
+                       void* ws, size_t ws_bytes, moe_debug_out* dbg, int32_t* dropped,
+                       void* stream) {
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (dropped && !aligned16(dropped)) return MOE_ERR_INVALID_ARG;
+  return layer_staged_impl(d, T, x, y, ws, ws_bytes, dbg, capacity, dropped, stream);
 }
 
 }  // extern "C"

@@ -50,6 +50,8 @@ struct GateTileArgs {
   int max_rows, max_tiles;  // bounds of the GEMM buffers the map drives
   int4* tile_map;           // [max_tiles] or null
   int32_t* n_tiles;         // [1]
+  int capacity;             // pairs kept per expert (INT_MAX: dropless)
+  int32_t* dropped;         // [1] or null: local pairs dropped by the capacity
 };
 
 hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,
@@ -57,13 +59,16 @@ hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, in
 hipError_t launch_gate_tiles(const GateTileArgs& a, int n_tiles_tok, hipStream_t st);
 
 // Multi-tile permutation: per-expert scan over tiles, then scatter.
+// capacity: pairs kept per expert, the first in token order (INT_MAX:
+// dropless); dropped (nullable) receives the number of local pairs dropped.
 hipError_t launch_permute_scan(const int32_t* tile_counts, int n_tiles_tok, int E_loc,
                                int32_t* tile_base, int32_t* counts, int32_t* offsets, int BM,
                                int max_rows, int max_tiles, int4* tile_map, int32_t* n_tiles,
-                               hipStream_t st);
+                               int capacity, int32_t* dropped, hipStream_t st);
 hipError_t launch_permute_scatter(const int32_t* ids, const int32_t* rank, const int32_t* tile_base,
                                   const int32_t* offsets, int T, int k, int e_begin, int e_end,
-                                  int32_t* dst_row, int32_t* src_token, hipStream_t st);
+                                  int capacity, int32_t* dst_row, int32_t* src_token,
+                                  hipStream_t st);
 hipError_t launch_gather_rows(const void* x, const int32_t* src_token, const int32_t* offsets,
                               int E_loc, int max_rows, int H, int elt_bytes, void* x_perm,
                               hipStream_t st);

@@ -5,7 +5,9 @@
 // token order.  The per-tile histograms and in-tile ranks come from the gating
 // kernel; here one block turns them into offsets and per-tile bases, and a
 // wide kernel writes dst_row / src_token.  No atomics anywhere, so the
-// permutation is the same on every run.
+// permutation is the same on every run.  An optional capacity keeps each
+// expert's first pairs in token order and drops the rest ("MoE 推理优化全景
+// 指南", section Capacity、padding 与 token dropping).
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -21,7 +23,9 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __res
                                                             int32_t* __restrict__ offsets, int BM,
                                                             int max_rows, int max_tiles,
                                                             int4* __restrict__ tile_map,
-                                                            int32_t* __restrict__ n_tiles) {
+                                                            int32_t* __restrict__ n_tiles,
+                                                            int capacity,
+                                                            int32_t* __restrict__ dropped) {
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1025];
   __shared__ int s_scr[1024];
@@ -45,10 +49,15 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __res
       tile_base[(size_t)tt * E_loc + el] = run;
       run += c;
     }
-    s_cnt[el] = run;
-    s_off[el] = run;
+    // an expert over capacity keeps its first `capacity` pairs
+    const int kept = min(run, capacity);
+    s_cnt[el] = kept;
+    s_off[el] = kept;
+    s_scr[el] = run - kept;
   }
   lds_barrier();
+  const int n_dropped = block_exclusive_scan(s_scr, E_loc, s_tmp);
+  if (dropped && threadIdx.x == 0) dropped[0] = n_dropped;
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
   if (threadIdx.x == 0) s_off[E_loc] = total;
   lds_barrier();
@@ -63,7 +72,8 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __res
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ tile_base, const int32_t* __restrict__ offsets, int T, int k,
-    int e_begin, int e_end, int32_t* __restrict__ dst_row, int32_t* __restrict__ src_token) {
+    int e_begin, int e_end, int capacity, int32_t* __restrict__ dst_row,
+    int32_t* __restrict__ src_token) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= T * k) return;
   const int t = p / k;
@@ -72,8 +82,13 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   if (e >= e_begin && e < e_end) {
     const int el = e - e_begin;
     const int E_loc = e_end - e_begin;
-    row = offsets[el] + tile_base[(size_t)(t / TOK_TILE) * E_loc + el] + rank[p];
-    src_token[row] = t;
+    // place of the pair in its expert's token order; beyond capacity it is
+    // dropped
+    const int pos = tile_base[(size_t)(t / TOK_TILE) * E_loc + el] + rank[p];
+    if (pos < capacity) {
+      row = offsets[el] + pos;
+      src_token[row] = t;
+    }
   }
   dst_row[p] = row;
 }
@@ -112,20 +127,23 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
 hipError_t launch_permute_scan(const int32_t* tile_counts, int n_tt, int E_loc,
                                int32_t* tile_base, int32_t* counts, int32_t* offsets, int BM,
                                int max_rows, int max_tiles, int4* tile_map, int32_t* n_tiles,
-                               hipStream_t st) {
+                               int capacity, int32_t* dropped, hipStream_t st) {
   const int threads = E_loc > 512 ? 1024 : (E_loc > 256 ? 512 : 256);
   permute_scan_kernel<<<1, threads, 0, st>>>(tile_counts, n_tt, E_loc, tile_base, counts, offsets,
-                                             BM, max_rows, max_tiles, tile_map, n_tiles);
+                                             BM, max_rows, max_tiles, tile_map, n_tiles, capacity,
+                                             dropped);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_scatter(const int32_t* ids, const int32_t* rank, const int32_t* tile_base,
                                   const int32_t* offsets, int T, int k, int e_begin, int e_end,
-                                  int32_t* dst_row, int32_t* src_token, hipStream_t st) {
+                                  int capacity, int32_t* dst_row, int32_t* src_token,
+                                  hipStream_t st) {
   const int n = T * k;
   if (n <= 0) return hipSuccess;
   permute_scatter_kernel<<<(n + 255) / 256, 256, 0, st>>>(ids, rank, tile_base, offsets, T, k,
-                                                          e_begin, e_end, dst_row, src_token);
+                                                          e_begin, e_end, capacity, dst_row,
+                                                          src_token);
   return hipGetLastError();
 }
 

@@ -318,9 +318,17 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
     return;
   }
 
-// single tile: finish the permutation here
-  for (int el = threadIdx.x; el < E_loc; el += NT) s_off[el] = s_cnt[el];
+// single tile: finish the permutation here (an expert over capacity keeps
+// its first pairs in token order: their ranks are below the capacity)
+  for (int el = threadIdx.x; el < E_loc; el += NT) {
+    const int kept = min(s_cnt[el], a.capacity);
+    s_scr[el] = s_cnt[el] - kept;
+    s_cnt[el] = kept;
+    s_off[el] = kept;
+  }
   lds_barrier();
+  const int n_dropped = block_exclusive_scan(s_scr, E_loc, s_tmp);
+  if (a.dropped && threadIdx.x == 0) a.dropped[0] = n_dropped;
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
   if (threadIdx.x == 0) s_off[E_loc] = total;
   lds_barrier();
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
   for (int p = threadIdx.x; p < npair; p += NT) {
     const int e = s_ids[p];
     int row = -1;
-    if (e >= a.e_begin && e < a.e_end) {
+    if (e >= a.e_begin && e < a.e_end && s_rank[p] < a.capacity) {
       row = s_off[e - a.e_begin] + s_rank[p];
       a.src_token[row] = p / k;
     }

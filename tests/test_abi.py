@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(moe_\w+)", out))
@@ -219,3 +219,22 @@ def test_reshard_rejects_before_launch():
             with pytest.raises(M.MoEError) as e:
                 fn(*args, stream=0)
             assert e.value.status == status, args
+
+
+def test_capacity_entries_reject_before_launch():
+    with pytest.raises(M.MoEError) as e:      # negative capacity
+        M.moe_permute_capacity(P, 4, 2, 8, 0, 8, -1, None, 0, 0, P, P, P, P, None, None, None, 0,
+                               stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:      # misaligned dropped counter
+        M.moe_permute_capacity(P, 4, 2, 8, 0, 8, 3, None, 0, 0, P, P, P, P, None, MIS, None, 0,
+                               stream=0)
+    assert e.value.status == 1
+    d = M.MoELayerDesc(H=256, E=8, k=2, I_loc=128, e_begin=0, e_end=8, I_shared=0, mode=0, dt=1,
+                       w_router=1 << 20, w13=1 << 21, w2=1 << 22)
+    with pytest.raises(M.MoEError) as e:
+        M.moe_layer_capacity(d, 4, -5, P, P, P, 1 << 30, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:      # workspace too small
+        M.moe_layer_capacity(d, 4, 3, P, P, P, 10, stream=0)
+    assert e.value.status == 3
