@@ -32,7 +32,9 @@ in the design notes of the repository):
   * the EP <-> TP weight reshard cuts the same intermediate range from the
     gate and the up half, as tp_shard does;
   * an expert over capacity keeps its first C (token, slot) pairs in token
-    order.
+    order;
+  * in the padded layout expert i owns rows [i*C, (i+1)*C), its kept pairs
+    first; a padding row has source -1 and a zero input row.
 
 Parity status: every function below is pinned by the `-m "not gpu"` tests in
 tests/test_oracle_pins.py (worked examples printed on the pages, closed forms,
@@ -226,7 +228,7 @@ def expert_capacity(capacity_factor, n_assign, E):
     return int(np.ceil(capacity_factor * n_assign / E))
 
 
-def permute_capacity(ids, e_begin, e_end, C):
+def permute_capacity(ids, e_begin, e_end, C, padded=False):
     """The permutation with a capacity of C (token, slot) pairs per expert.
 
     [MoE guide] section "Capacity、padding 与 token dropping" and [CS349D L8]
@@ -235,16 +237,24 @@ def permute_capacity(ids, e_begin, e_end, C):
     expert keeps): the first C in the stable order of permute(), i.e. token
     order.
 
+    padded: the same section lets an expert with fewer than C pairs be padded
+    to C, so that every expert owns a fixed block of C rows: expert i's rows
+    start at i * C, and a padding row has source -1.  Otherwise the kept rows
+    are packed as in permute().
+
     Returns counts [E_loc] (kept pairs), offsets [E_loc + 1], src_token
-    [kept], dst_row [T, k] (-1 for a pair that is dropped or not local) and
-    the number of dropped local pairs.
+    [offsets[-1]], dst_row [T, k] (-1 for a pair that is dropped or not
+    local) and the number of dropped local pairs.
     """
     ids = np.asarray(ids)
     T, k = ids.shape
     full, _, _, _ = permute(ids, e_begin, e_end)
     counts = np.minimum(full, C)
-    offsets = exclusive_offsets(counts)
-    src_token = np.empty(int(offsets[-1]), dtype=np.int64)
+    if padded:
+        offsets = np.arange(e_end - e_begin + 1, dtype=np.int64) * C
+    else:
+        offsets = exclusive_offsets(counts)
+    src_token = np.full(int(offsets[-1]), -1, dtype=np.int64)
     dst_row = np.full((T, k), -1, dtype=np.int64)
     seen = np.zeros(e_end - e_begin, dtype=np.int64)
     for t in range(T):
@@ -375,6 +385,9 @@ def grouped_ffn(x, src_token, offsets, w13, w2, dtype=np.float64):
     x: [T, H]; src_token: [rows]; offsets: [E_loc + 1];
     w13: indexable by local expert -> [2I, H]; w2: -> [H, I]
     ->  y_perm [rows, H]
+
+    A row whose source is -1 is padding (permute_capacity with padded=True):
+    its input row is zero.
     """
     x = np.asarray(x)
     H = x.shape[1]
@@ -383,7 +396,11 @@ def grouped_ffn(x, src_token, offsets, w13, w2, dtype=np.float64):
     for e in range(len(offsets) - 1):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 > r0:
-            y_perm[r0:r1] = swiglu_expert(x[np.asarray(src_token[r0:r1])], w13[e], w2[e], dtype)
+            src = np.asarray(src_token[r0:r1])
+            xin = np.zeros((r1 - r0, H), dtype=x.dtype)
+            live = src >= 0
+            xin[live] = x[src[live]]
+            y_perm[r0:r1] = swiglu_expert(xin, w13[e], w2[e], dtype)
     return y_perm
 
 
@@ -418,7 +435,7 @@ def combine(y_perm, dst_row, w, y_shared=None, dtype=np.float64):
 
 def moe_layer(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
               e_begin=0, e_end=None, w13_shared=None, w2_shared=None,
-              logits=None, dtype=np.float64, capacity=None):
+              logits=None, dtype=np.float64, capacity=None, padded=False):
     """One GPU's share of the MoE layer forward through the permuted data path.
 
     [MoE guide] section "一个 token 为什么要跨 GPU": router -> top-k ids and
@@ -434,6 +451,7 @@ def moe_layer(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
     route on exactly those values; otherwise they are computed here.
 
     `capacity`: C pairs per local expert (permute_capacity); None = dropless.
+    `padded`: with a capacity, every expert owns a block of C rows.
 
     Returns (y [T, H], aux dict with logits, ids, w, counts, offsets,
     src_token, dst_row, dropped).
@@ -450,7 +468,7 @@ def moe_layer(x, w_r, w13, w2, k, mode, logit_bias=None, sel_bias=None,
         counts, offsets, src_token, dst_row = permute(ids, e_begin, e_end)
     else:
         counts, offsets, src_token, dst_row, dropped = permute_capacity(ids, e_begin, e_end,
-                                                                         capacity)
+                                                                         capacity, padded)
     y_perm = grouped_ffn(x, src_token, offsets, w13, w2, dtype)
     y_shared = None
     if w13_shared is not None:

@@ -230,6 +230,61 @@ def test_capacity_keeps_first_pairs_in_token_order_brute_force():
                 assert dst[t, j] == -1
 
 
+def test_padded_layout_brute_force():
+    """[MoE guide] "Capacity、padding 与 token dropping": an expert with fewer
+    than C pairs is padded to C.  Expert i's block is rows [i*C, (i+1)*C),
+    its kept pairs first in token order, then padding (source -1)."""
+    r = rng(54)
+    T, k, E, C = 90, 3, 8, 30
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)])
+    for eb, ee in ((0, E), (2, 7)):
+        counts, offsets, src, dst, dropped = O.permute_capacity(ids, eb, ee, C, padded=True)
+        E_loc = ee - eb
+        assert offsets.tolist() == [i * C for i in range(E_loc + 1)]
+        assert len(src) == E_loc * C
+        ref_src = -np.ones(E_loc * C, dtype=int)
+        ref_dst = -np.ones((T, k), dtype=int)
+        n_drop = 0
+        for i in range(E_loc):                       # walk each expert's pairs
+            pairs = [(t, j) for t in range(T) for j in range(k) if ids[t, j] == eb + i]
+            for q, (t, j) in enumerate(pairs):
+                if q < C:
+                    ref_src[i * C + q] = t
+                    ref_dst[t, j] = i * C + q
+                else:
+                    n_drop += 1
+            assert counts[i] == min(len(pairs), C)
+        assert np.array_equal(src, ref_src) and np.array_equal(dst, ref_dst)
+        assert dropped == n_drop
+        # the packed layout holds the same rows, moved to its own offsets
+        pc, po, ps, pd, pdrop = O.permute_capacity(ids, eb, ee, C)
+        assert np.array_equal(pc, counts) and pdrop == dropped
+        for i in range(E_loc):
+            assert np.array_equal(src[i * C:i * C + counts[i]], ps[po[i]:po[i + 1]])
+        live = pd >= 0
+        assert np.array_equal(live, dst >= 0)
+
+
+def test_padded_rows_are_zero_and_the_layer_is_unchanged():
+    """A padding row is a zero input row, so its expert output is exactly
+    zero (SwiGLU has no bias: SiLU(0) * 0 = 0); padding changes where rows
+    live, not the layer's result."""
+    L = tiny_layer(55, T=30)
+    k, mode = 2, 2
+    for C in (3, 9, 40):
+        y0, a0 = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode, capacity=C)
+        y1, a1 = O.moe_layer(L["x"], L["w_r"], L["w13"], L["w2"], k, mode, capacity=C,
+                             padded=True)
+        assert a1["dropped"] == a0["dropped"]
+        assert np.array_equal(y0, y1)
+        src = a1["src_token"]
+        y_perm = O.grouped_ffn(L["x"], src, a1["offsets"], L["w13"], L["w2"])
+        assert np.all(y_perm[src < 0] == 0.0)
+        # payload of the fixed-shape buffer: kept pairs over E * C rows
+        kept = int((src >= 0).sum())
+        assert kept == 30 * k - a1["dropped"] == int(a1["counts"].sum())
+
+
 def test_large_capacity_is_dropless():
     L = tiny_layer(51, T=20)
     k, mode = 2, 2
