@@ -325,8 +325,10 @@ def dispatch_bench(steps, warmup, P=8, Ts=(64, 4096)):
 def capacity_bench(bench, steps, warmup, factors=(1.0, 1.25)):
     """moe_layer_capacity on the bench's own layer and batch: C =
     ceil(cf * T * k / E) pairs per expert; the hottest expert is capped, at
-    the price of the dropped (token, expert) pairs.  Graph-replayed time
-    beside the dropless time of the same batch."""
+    the price of the dropped (token, expert) pairs.  Each factor in the packed
+    layout and in the padded one (fixed blocks of C rows per expert; payload =
+    kept pairs over those rows).  Graph-replayed times beside the dropless
+    time of the same batch."""
     import torch
     M, cfg, T = bench.M, bench.cfg, bench.T
     if cfg.dtype != "bf16":
@@ -337,20 +339,32 @@ def capacity_bench(bench, steps, warmup, factors=(1.0, 1.25)):
     try:
         for cf in factors:
             C = int(math.ceil(cf * T * cfg.k / cfg.E))
+            for padded in (0, 1):
+                ws_p = M.layer_workspace(bench.layers[0][0], T, capacity=C, padded=1) \
+                    if padded else None
 
-            def fn(d, T_, x, y, ws, nb, dbg=None, C=C):
-                M.moe_layer_capacity(d, T_, C, x, y, ws, nb, dbg, dropped)
+                def fn(d, T_, x, y, ws, nb, dbg=None, C=C, padded=padded, ws_p=ws_p):
+                    if ws_p is not None:
+                        ws, nb = ws_p, ws_p.numel()
+                    M.moe_layer_capacity(d, T_, C, padded, x, y, ws, nb, dbg, dropped)
 
-            bench.layer_fn = fn
-            bench.step(0)
-            torch.cuda.synchronize()
-            n_drop = int(dropped[0].item())
-            ms = bench.timed_graph(steps, warmup)
-            out.append(dict(capacity_factor=cf, capacity=C, dropped_pairs=n_drop,
-                            dropped_frac=round(n_drop / (T * cfg.k), 4), ms=round(ms, 4),
-                            tokens_per_s=round(T / (ms * 1e-3), 1)))
-            print(f"# capacity cf={cf}: C={C}, dropped {n_drop / (T * cfg.k):.3f} of the pairs, "
-                  f"{ms:.4f} ms", file=sys.stderr, flush=True)
+                bench.layer_fn = fn
+                bench.step(0)
+                torch.cuda.synchronize()
+                n_drop = int(dropped[0].item())
+                ms = bench.timed_graph(steps, warmup)
+                kept = T * cfg.k - n_drop
+                rec = dict(capacity_factor=cf, capacity=C,
+                           layout="padded" if padded else "packed", dropped_pairs=n_drop,
+                           dropped_frac=round(n_drop / (T * cfg.k), 4), ms=round(ms, 4),
+                           tokens_per_s=round(T / (ms * 1e-3), 1))
+                if padded:
+                    rec["payload_frac"] = round(kept / (cfg.E_loc * C), 4)
+                out.append(rec)
+                print(f"# capacity cf={cf} {rec['layout']}: C={C}, dropped "
+                      f"{n_drop / (T * cfg.k):.3f} of the pairs, {ms:.4f} ms", file=sys.stderr,
+                      flush=True)
+                del ws_p
     finally:
         bench.layer_fn = saved
     return out

@@ -142,14 +142,23 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e
  *   default path here is dropless).
  *
  *   An expert keeps its first `capacity` pairs in token order; the others get
- *   dst_row -1 and no row.  counts[i] = kept pairs (<= capacity), offsets and
- *   src_token as in moe_permute over the kept pairs, so at most
- *   E_loc * capacity rows exist.  dropped[0] (int32, may be NULL) = the number
- *   of local pairs dropped.  capacity >= 0 (INT_MAX: moe_permute itself).
- *   Other arguments and the workspace as for moe_permute.
+ *   dst_row -1 and no row.  counts[i] = kept pairs (<= capacity).  dropped[0]
+ *   (int32, may be NULL) = the number of local pairs dropped.  capacity >= 0
+ *   (INT_MAX with padded = 0: moe_permute itself).
+ *
+ *   padded = 0: offsets and src_token as in moe_permute over the kept pairs
+ *   (at most min(T*k, E_loc*capacity) rows).
+ *   padded = 1: the fixed-shape layout of the same section, every expert
+ *   padded to `capacity` rows: offsets[i] = i * capacity, expert i's kept
+ *   pairs fill rows i*capacity .. i*capacity + counts[i] - 1 in token order,
+ *   and src_token = -1 on the rest of its block.  src_token (and x_perm, whose
+ *   padding rows are zero) then hold E_loc * capacity rows, which must fit an
+ *   int (else MOE_ERR_INVALID_ARG), and ws is needed for every T > 0.
+ *   padded must be 0 or 1.  Other arguments and the workspace as for
+ *   moe_permute.
  */
 int moe_permute_capacity(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
-                         int capacity, const void* x, int H, int dt,
+                         int capacity, int padded, const void* x, int H, int dt,
                          int32_t* counts, int32_t* offsets, int32_t* src_token, int32_t* dst_row,
                          void* x_perm, int32_t* dropped, void* ws, size_t ws_bytes, void* stream);
 
@@ -170,6 +179,10 @@ int moe_permute_capacity(const int32_t* topk_ids, int T, int k, int E, int e_beg
  *
  *   max_rows bounds offsets[E_loc] (grid sizing; T*k for a full layer).
  *   x_perm[max_rows][H] or x[*][H] + src_token[max_rows]; w13, w2: dtype dt;
+ *   every row in an expert's range is computed, so for the padded layout of
+ *   moe_permute_capacity pass its x_perm (padding rows zero, hence outputs
+ *   zero); gathering from x, a source of -1 reads row 0 of x and that row's
+ *   output is meaningless;
  *   y_perm[max_rows][H] of dtype y_dt.  ws: at least
  *   moe_grouped_ffn_workspace_size(...) bytes.
  */
@@ -366,10 +379,24 @@ int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y,
  * [MoE guide] section "Capacity、padding 与 token dropping"; not the default,
  * see [CS349D L8] section 1.4).  dropped[0] (int32, may be NULL) receives the
  * number of local pairs dropped; debug copies show the kept counts and -1 for
- * dropped pairs.  capacity >= 0; INT_MAX gives moe_layer_staged exactly. */
-int moe_layer_capacity(const moe_layer_desc* d, int T, int capacity, const void* x, void* y,
-                       void* ws, size_t ws_bytes, moe_debug_out* dbg, int32_t* dropped,
+ * dropped pairs.  capacity >= 0; INT_MAX with padded = 0 gives
+ * moe_layer_staged exactly.
+ *   padded = 1 lays the expert rows out in fixed blocks of `capacity` rows
+ * (moe_permute_capacity's padded layout, debug offsets i * capacity, debug
+ * src_token of E_loc * capacity entries with -1 on padding rows); the GEMMs
+ * compute the kept rows only, so the output equals that of padded = 0.  The
+ * workspace must then be moe_layer_capacity_workspace_size(d, T, capacity, 1)
+ * bytes (else MOE_ERR_WORKSPACE), and E_loc * capacity must fit an int (else
+ * MOE_ERR_INVALID_ARG). */
+int moe_layer_capacity(const moe_layer_desc* d, int T, int capacity, int padded, const void* x,
+                       void* y, void* ws, size_t ws_bytes, moe_debug_out* dbg, int32_t* dropped,
                        void* stream);
+
+/* Workspace for moe_layer_capacity with T <= T_max: moe_layer_workspace_size
+ * for padded = 0; for padded = 1, h and the expert outputs hold
+ * E_loc * capacity rows.  0 for invalid arguments. */
+size_t moe_layer_capacity_workspace_size(const moe_layer_desc* d, int T_max, int capacity,
+                                         int padded);
 
 /* Single-launch decode path: router, gating, dispatch metadata, both expert
  * GEMMs, the shared expert and the combine in ONE kernel launch whose

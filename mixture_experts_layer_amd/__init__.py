@@ -19,7 +19,7 @@ from ._abi import (MOE_F32, MOE_BF16, MOE_OK, GATE_TOPK_SOFTMAX, GATE_SOFTMAX_TO
 __all__ = [
     "MoEError", "lib", "get_lib", "moe_abi_version", "moe_status_str", "moe_route", "moe_permute",
     "moe_permute_workspace_size", "moe_permute_capacity", "moe_grouped_ffn",
-    "moe_grouped_ffn_workspace_size", "moe_layer_capacity",
+    "moe_grouped_ffn_workspace_size", "moe_layer_capacity", "moe_layer_capacity_workspace_size",
     "moe_combine", "moe_pack_by_rank", "moe_pack_workspace_size", "moe_unpack_sum",
     "moe_reshard_ep_to_tp_pack", "moe_reshard_tp_to_ep_interleave", "moe_layer",
     "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
@@ -105,10 +105,11 @@ def moe_permute(topk_ids, T, k, E, e_begin, e_end, x, H, dt, counts, offsets, sr
                                           _p(x_perm), _p(ws), ws_bytes, _stream(stream)))
 
 
-def moe_permute_capacity(topk_ids, T, k, E, e_begin, e_end, capacity, x, H, dt, counts, offsets,
-                         src_token, dst_row, x_perm, dropped, ws, ws_bytes, stream=None):
+def moe_permute_capacity(topk_ids, T, k, E, e_begin, e_end, capacity, padded, x, H, dt, counts,
+                         offsets, src_token, dst_row, x_perm, dropped, ws, ws_bytes, stream=None):
     _check("moe_permute_capacity",
-           lib.moe_permute_capacity(_p(topk_ids), T, k, E, e_begin, e_end, capacity, _p(x), H, dt,
+           lib.moe_permute_capacity(_p(topk_ids), T, k, E, e_begin, e_end, capacity, int(padded),
+                                    _p(x), H, dt,
                                     _p(counts), _p(offsets), _p(src_token), _p(dst_row),
                                     _p(x_perm), _p(dropped), _p(ws), ws_bytes, _stream(stream)))
 
@@ -203,12 +204,17 @@ def moe_layer_staged(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut
                                 None if dbg is None else ctypes.byref(dbg), _stream(stream)))
 
 
-def moe_layer_capacity(desc: MoELayerDesc, T, capacity, x, y, ws, ws_bytes,
+def moe_layer_capacity(desc: MoELayerDesc, T, capacity, padded, x, y, ws, ws_bytes,
                        dbg: MoEDebugOut | None = None, dropped=None, stream=None):
     _check("moe_layer_capacity",
-           lib.moe_layer_capacity(ctypes.byref(desc), T, capacity, _p(x), _p(y), _p(ws), ws_bytes,
-                                  None if dbg is None else ctypes.byref(dbg), _p(dropped),
-                                  _stream(stream)))
+           lib.moe_layer_capacity(ctypes.byref(desc), T, capacity, int(padded), _p(x), _p(y),
+                                  _p(ws), ws_bytes, None if dbg is None else ctypes.byref(dbg),
+                                  _p(dropped), _stream(stream)))
+
+
+def moe_layer_capacity_workspace_size(desc: MoELayerDesc, T_max: int, capacity: int,
+                                      padded: int) -> int:
+    return lib.moe_layer_capacity_workspace_size(ctypes.byref(desc), T_max, capacity, int(padded))
 
 
 def moe_layer_decode(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut | None = None,
@@ -218,11 +224,15 @@ def moe_layer_decode(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut
                                 None if dbg is None else ctypes.byref(dbg), _stream(stream)))
 
 
-def layer_workspace(desc: MoELayerDesc, T_max: int, device="cuda"):
+def layer_workspace(desc: MoELayerDesc, T_max: int, device="cuda", capacity=None, padded=0):
     """A zeroed workspace tensor for the layer entry points (the decode path's
-    synchronisation block must start zeroed)."""
+    synchronisation block must start zeroed); with capacity and padded = 1,
+    sized for moe_layer_capacity's padded layout."""
     import torch
-    n = moe_layer_workspace_size(desc, T_max)
+    if capacity is None:
+        n = moe_layer_workspace_size(desc, T_max)
+    else:
+        n = moe_layer_capacity_workspace_size(desc, T_max, capacity, padded)
     if n == 0:
         raise ValueError("invalid layer description")
     return torch.zeros(n, dtype=torch.uint8, device=device)

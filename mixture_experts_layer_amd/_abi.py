@@ -41,9 +41,9 @@ _SIGS = {
     "moe_permute": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_int, c_int,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                             c_void_p]),
-    "moe_permute_capacity": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
-                                     c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_permute_capacity": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                     c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_grouped_ffn_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "moe_grouped_ffn": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_size_t,
@@ -66,9 +66,11 @@ _SIGS = {
     "moe_layer_path": (c_int, [ctypes.POINTER(MoELayerDesc), c_int]),
     "moe_layer_staged": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p,
                                  c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
-    "moe_layer_capacity": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_int, c_void_p, c_void_p,
-                                   c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p,
-                                   c_void_p]),
+    "moe_layer_capacity": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_int, c_int, c_void_p,
+                                   c_void_p, c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut),
+                                   c_void_p, c_void_p]),
+    "moe_layer_capacity_workspace_size": (c_size_t, [ctypes.POINTER(MoELayerDesc), c_int, c_int,
+                                                     c_int]),
     "moe_layer_decode": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p,
                                  c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
 }

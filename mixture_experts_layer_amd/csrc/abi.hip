@@ -92,14 +92,17 @@ int check_desc(const moe_layer_desc* d) {
   return MOE_OK;
 }
 
-size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w) {
+// pad_rows >= 0: the padded capacity layout, whose h and y_perm hold pad_rows
+// (E_loc * capacity) rows; the GEMM tiles still cover only kept rows.
+size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w, int pad_rows = -1) {
   const int E_loc = d->e_end - d->e_begin;
   const int eb = elt_bytes(d->dt);
-  const int max_rows = T * (d->k < E_loc ? d->k : E_loc);
+  const int real_rows = T * (d->k < E_loc ? d->k : E_loc);
+  const int max_rows = pad_rows >= 0 ? pad_rows : real_rows;
   const int n_tt = cdiv(T, TOK_TILE);
   const int BM = ffn_row_tile(d->dt, mean_rows(T, d->k, d->E), d->H, d->I_loc,
                               T * d->k < E_loc ? T * d->k : E_loc);
-  const int max_tiles = max_tiles_for(max_rows, E_loc, BM);
+  const int max_tiles = max_tiles_for(real_rows < max_rows ? real_rows : max_rows, E_loc, BM);
   Carver c(base);
   LayerWs l;
   // the single-launch decode path keeps its counters here, ahead of
@@ -113,7 +116,7 @@ size_t layer_layout(const moe_layer_desc* d, int T, void* base, LayerWs* w) {
   l.rank = c.take<int32_t>((size_t)T * d->k * 4);
   l.counts = c.take<int32_t>((size_t)E_loc * 4);
   l.offsets = c.take<int32_t>((size_t)(E_loc + 1) * 4);
-  l.src_token = c.take<int32_t>((size_t)T * d->k * 4);
+  l.src_token = c.take<int32_t>((size_t)(pad_rows >= 0 ? pad_rows : T * d->k) * 4);
   l.dst_row = c.take<int32_t>((size_t)T * d->k * 4);
   l.tile_map = c.take<int4>((size_t)max_tiles * sizeof(int4));
   l.n_tiles = c.take<int32_t>(4);
@@ -161,13 +164,13 @@ bool decode_preferred(const moe_layer_desc* d, int T) {
 }
 
 int check_layer_call(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
-                     size_t ws_bytes, const moe_debug_out* dbg) {
+                     size_t ws_bytes, const moe_debug_out* dbg, int pad_rows = -1) {
   int st = check_desc(d);
   if (st) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
-  const size_t need = layer_layout(d, T, nullptr, nullptr);
+  const size_t need = layer_layout(d, T, nullptr, nullptr, pad_rows);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_INVALID_ARG;
   if (dbg) {
@@ -261,18 +264,28 @@ size_t moe_permute_workspace_size(int T, int k, int E_loc) {
   return align_up((size_t)n_tt * E_loc * 4) * 2 + align_up((size_t)T * k * 4);
 }
 
+// Rows of the padded capacity layout (E_loc * capacity), or -1 if that does
+// not fit an int.
+static int padded_rows(int E_loc, int capacity) {
+  const long long n = (long long)E_loc * capacity;
+  return n > INT_MAX ? -1 : (int)n;
+}
+
 static int permute_impl(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
-                        int capacity, const void* x, int H, int dt, int32_t* counts,
+                        int capacity, int padded, const void* x, int H, int dt, int32_t* counts,
                         int32_t* offsets, int32_t* src_token, int32_t* dst_row, void* x_perm,
                         int32_t* dropped, void* ws, size_t ws_bytes, void* stream) {
-  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (capacity < 0 || (padded != 0 && padded != 1)) return MOE_ERR_INVALID_ARG;
   if (dropped && !aligned16(dropped)) return MOE_ERR_INVALID_ARG;
   int st = check_route_shape(T, E, k, 0);
   if (st) return st;
   if (e_begin < 0 || e_end > E || e_begin >= e_end) return MOE_ERR_INVALID_ARG;
   const int E_loc = e_end - e_begin;
+  const int pad_rows = padded ? padded_rows(E_loc, capacity) : 0;
+  if (pad_rows < 0) return MOE_ERR_INVALID_ARG;
   if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !src_token || !dst_row)) return MOE_ERR_INVALID_ARG;
+  if (pad_rows > 0 && !src_token) return MOE_ERR_INVALID_ARG;
   {
     const void* ptrs[] = {topk_ids, counts, offsets, src_token, dst_row};
     for (const void* p : ptrs)
@@ -284,8 +297,9 @@ static int permute_impl(const int32_t* topk_ids, int T, int k, int E, int e_begi
     if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
   }
   const size_t need = moe_permute_workspace_size(T, k, E_loc);
-  const bool single = T <= TOK_TILE;
-  if (!single && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  // the padded layout's offsets come from the scan kernel
+  const bool single = T <= TOK_TILE && !padded;
+  if (!single && need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n_tt = cdiv(T, TOK_TILE);
@@ -304,16 +318,20 @@ static int permute_impl(const int32_t* topk_ids, int T, int k, int E, int e_begi
   a.counts = counts; a.offsets = offsets; a.src_token = src_token; a.dst_row = dst_row;
   a.BM = 16; a.tile_map = nullptr; a.n_tiles = nullptr;
   a.capacity = capacity; a.dropped = dropped;
-  MOE_TRY(launch_gate_tiles(a, n_tt, s));
+  // with no tokens the multi-tile path has no tile to count (its workspace
+  // is empty); the scan still writes counts, offsets and the dropped word
+  if (single || T > 0) MOE_TRY(launch_gate_tiles(a, n_tt, s));
   if (!single) {
     MOE_TRY(launch_permute_scan(tile_counts, n_tt, E_loc, tile_base, counts, offsets, 16, 0, 0,
-                                nullptr, nullptr, capacity, dropped, s));
+                                nullptr, nullptr, capacity, padded, dropped, s));
     MOE_TRY(launch_permute_scatter(topk_ids, rank, tile_base, offsets, T, k, e_begin, e_end,
                                    capacity, dst_row, src_token, s));
+    if (padded) MOE_TRY(launch_pad_rows(counts, E_loc, capacity, src_token, s));
   }
-  if (x && T > 0)
-    MOE_TRY(launch_gather_rows(x, src_token, offsets, E_loc, T * (k < E_loc ? k : E_loc), H,
-                               elt_bytes(dt), x_perm, s));
+  const int gather_rows = padded ? pad_rows : T * (k < E_loc ? k : E_loc);
+  if (x && gather_rows > 0)
+    MOE_TRY(launch_gather_rows(x, src_token, offsets, E_loc, gather_rows, H, elt_bytes(dt), x_perm,
+                               s));
   return MOE_OK;
 }
 
@@ -321,16 +339,16 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e
                 const void* x, int H, int dt, int32_t* counts, int32_t* offsets,
                 int32_t* src_token, int32_t* dst_row, void* x_perm, void* ws, size_t ws_bytes,
                 void* stream) {
-  return permute_impl(topk_ids, T, k, E, e_begin, e_end, INT_MAX, x, H, dt, counts, offsets,
+  return permute_impl(topk_ids, T, k, E, e_begin, e_end, INT_MAX, 0, x, H, dt, counts, offsets,
                       src_token, dst_row, x_perm, nullptr, ws, ws_bytes, stream);
 }
 
 int moe_permute_capacity(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
-                         int capacity, const void* x, int H, int dt, int32_t* counts,
+                         int capacity, int padded, const void* x, int H, int dt, int32_t* counts,
                          int32_t* offsets, int32_t* src_token, int32_t* dst_row, void* x_perm,
                          int32_t* dropped, void* ws, size_t ws_bytes, void* stream) {
-  return permute_impl(topk_ids, T, k, E, e_begin, e_end, capacity, x, H, dt, counts, offsets,
-                      src_token, dst_row, x_perm, dropped, ws, ws_bytes, stream);
+  return permute_impl(topk_ids, T, k, E, e_begin, e_end, capacity, padded, x, H, dt, counts,
+                      offsets, src_token, dst_row, x_perm, dropped, ws, ws_bytes, stream);
 }
 
 size_t moe_grouped_ffn_workspace_size(int max_rows, int E_loc, int H, int I_loc, int dt) {
@@ -520,12 +538,14 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
 }
 
 static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
-                             size_t ws_bytes, moe_debug_out* dbg, int capacity, int32_t* dropped,
-                             void* stream) {
-  int st = check_layer_call(d, T, x, y, ws, ws_bytes, dbg);
+                             size_t ws_bytes, moe_debug_out* dbg, int capacity, int padded,
+                             int32_t* dropped, void* stream) {
+  // padded: expert blocks of `capacity` rows in h and y_perm (pad_rows >= 0)
+  const int pad_rows = padded ? padded_rows(d->e_end - d->e_begin, capacity) : -1;
+  int st = check_layer_call(d, T, x, y, ws, ws_bytes, dbg, pad_rows);
   if (st || T == 0) return st;
   LayerWs l;
-  layer_layout(d, T, ws, &l);
+  layer_layout(d, T, ws, &l, pad_rows);
   if (dbg) {
     if (dbg->logits) l.logits = dbg->logits;
     if (dbg->topk_ids) l.ids = dbg->topk_ids;
@@ -547,7 +567,7 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   // a1: router logits
   MOE_TRY(launch_router_logits(x, d->w_router, d->dt, T, d->H, d->E, d->logit_bias, l.logits, s));
   // a2-a5: gating, histogram, prefix sum, permutation, GEMM tile map
-  const bool single = T <= TOK_TILE;
+  const bool single = T <= TOK_TILE && !padded;
   GateTileArgs a{};
   a.logits = l.logits; a.sel_bias = d->sel_bias;
   a.ids_out = l.ids; a.w_out = l.w;
@@ -564,9 +584,12 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   if (!single) {
     MOE_TRY(launch_permute_scan(l.tile_counts, l.n_tt, E_loc, l.tile_base, l.counts, l.offsets,
                                 l.BM, l.max_rows, l.max_tiles, l.tile_map, l.n_tiles, capacity,
-                                dropped, s));
+                                padded, dropped, s));
     MOE_TRY(launch_permute_scatter(l.ids, l.rank, l.tile_base, l.offsets, T, d->k, d->e_begin,
                                    d->e_end, capacity, l.dst_row, l.src_token, s));
+    // the GEMMs never read padding rows; mark them only for a caller who asks
+    if (padded && dbg && dbg->src_token)
+      MOE_TRY(launch_pad_rows(l.counts, E_loc, capacity, l.src_token, s));
   }
   MOE_TRY(mark(1));
   // a6-a7: grouped SwiGLU GEMMs, gather fused into the first
@@ -601,15 +624,27 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
 
 int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
                      size_t ws_bytes, moe_debug_out* dbg, void* stream) {
-  return layer_staged_impl(d, T, x, y, ws, ws_bytes, dbg, INT_MAX, nullptr, stream);
+  return layer_staged_impl(d, T, x, y, ws, ws_bytes, dbg, INT_MAX, 0, nullptr, stream);
 }
 
-int moe_layer_capacity(const moe_layer_desc* d, int T, int capacity, const void* x, void* y,
-                       void* ws, size_t ws_bytes, moe_debug_out* dbg, int32_t* dropped,
+size_t moe_layer_capacity_workspace_size(const moe_layer_desc* d, int T_max, int capacity,
+                                         int padded) {
+  if (check_desc(d) != MOE_OK || T_max < 0 || capacity < 0 || (padded != 0 && padded != 1))
+    return 0;
+  if (!padded) return layer_layout(d, T_max, nullptr, nullptr);
+  const int pad_rows = padded_rows(d->e_end - d->e_begin, capacity);
+  if (pad_rows < 0) return 0;
+  return layer_layout(d, T_max, nullptr, nullptr, pad_rows);
+}
+
+int moe_layer_capacity(const moe_layer_desc* d, int T, int capacity, int padded, const void* x,
+                       void* y, void* ws, size_t ws_bytes, moe_debug_out* dbg, int32_t* dropped,
                        void* stream) {
-  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (capacity < 0 || (padded != 0 && padded != 1)) return MOE_ERR_INVALID_ARG;
   if (dropped && !aligned16(dropped)) return MOE_ERR_INVALID_ARG;
-  return layer_staged_impl(d, T, x, y, ws, ws_bytes, dbg, capacity, dropped, stream);
+  if (padded && d && d->e_end > d->e_begin && padded_rows(d->e_end - d->e_begin, capacity) < 0)
+    return MOE_ERR_INVALID_ARG;
+  return layer_staged_impl(d, T, x, y, ws, ws_bytes, dbg, capacity, padded, dropped, stream);
 }
 
 }  // extern "C"

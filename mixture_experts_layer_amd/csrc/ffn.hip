@@ -79,7 +79,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
   for (int mt = 0; mt < MT; ++mt) {
     const int row = r0 + 16 * mt + (lane & 15);
     xv[mt] = row < r1;
-    const int src = xv[mt] ? (a.src_token ? a.src_token[row] : row) : 0;
+    // a source of -1 (a padding row) reads row 0 instead of memory before X
+    const int src = xv[mt] ? (a.src_token ? max(a.src_token[row], 0) : row) : 0;
     xp[mt] = a.X + (size_t)src * a.K + kg;
   }
   const bf16_t* We = a.W + (size_t)e * a.w_stride;
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
     const int rt = (wid + C::NWAVE * j) * C::RPI + prow;
     int row = r0 + rt;
     if (row >= r1) row = r0;                          // padding rows read a valid row
-    const int src = a.src_token ? a.src_token[row] : row;
+    const int src = a.src_token ? max(a.src_token[row], 0) : row;
     xsrc[j] = a.X + (size_t)src * a.K + (pchunk ^ tile_swz<C>(rt)) * 8;
   }
   const bf16_t* We = a.W + (size_t)e * a.w_stride;
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(F32Args a) {
   const int row = r0 + (threadIdx.x >> 4);
   const int n = ntile * 16 + (threadIdx.x & 15);
   if (row >= r1) return;
-  const int src = a.src_token ? a.src_token[row] : row;
+  const int src = a.src_token ? max(a.src_token[row], 0) : row;
   const float4* xr = reinterpret_cast<const float4*>(a.X + (size_t)src * a.K);
   const float* We = a.W + (size_t)e * a.w_stride;
   const float4* wg = reinterpret_cast<const float4*>(We + (size_t)n * a.K);

@@ -64,7 +64,11 @@ hipError_t launch_gate_tiles(const GateTileArgs& a, int n_tiles_tok, hipStream_t
 hipError_t launch_permute_scan(const int32_t* tile_counts, int n_tiles_tok, int E_loc,
                                int32_t* tile_base, int32_t* counts, int32_t* offsets, int BM,
                                int max_rows, int max_tiles, int4* tile_map, int32_t* n_tiles,
-                               int capacity, int32_t* dropped, hipStream_t st);
+                               int capacity, int padded, int32_t* dropped, hipStream_t st);
+// Padded capacity layout: src_token = -1 on every expert block's rows past its
+// kept pairs (E_loc * capacity rows).
+hipError_t launch_pad_rows(const int32_t* counts, int E_loc, int capacity, int32_t* src_token,
+                           hipStream_t st);
 hipError_t launch_permute_scatter(const int32_t* ids, const int32_t* rank, const int32_t* tile_base,
                                   const int32_t* offsets, int T, int k, int e_begin, int e_end,
                                   int capacity, int32_t* dst_row, int32_t* src_token,

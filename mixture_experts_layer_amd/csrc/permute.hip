@@ -7,7 +7,9 @@
 // wide kernel writes dst_row / src_token.  No atomics anywhere, so the
 // permutation is the same on every run.  An optional capacity keeps each
 // expert's first pairs in token order and drops the rest ("MoE 推理优化全景
-// 指南", section Capacity、padding 与 token dropping).
+// 指南", section Capacity、padding 与 token dropping); in the padded layout of
+// that section every expert owns a fixed block of `capacity` rows, its kept
+// pairs first, then padding rows whose source is -1.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -15,7 +17,7 @@ namespace moe {
 
 // One block: for every local expert, an exclusive scan of its counts over the
 // token tiles (tile_base), its total (counts), then the exclusive scan over
-// experts (offsets) and the GEMM tile map.
+// experts (offsets; el * capacity in the padded layout) and the GEMM tile map.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __restrict__ tile_counts,
                                                             int n_tt, int E_loc,
                                                             int32_t* __restrict__ tile_base,
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __res
                                                             int max_rows, int max_tiles,
                                                             int4* __restrict__ tile_map,
                                                             int32_t* __restrict__ n_tiles,
-                                                            int capacity,
+                                                            int capacity, int padded,
                                                             int32_t* __restrict__ dropped) {
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1025];
@@ -59,7 +61,12 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(const int32_t* __res
   const int n_dropped = block_exclusive_scan(s_scr, E_loc, s_tmp);
   if (dropped && threadIdx.x == 0) dropped[0] = n_dropped;
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
-  if (threadIdx.x == 0) s_off[E_loc] = total;
+  if (padded) {
+    // the host has checked that E_loc * capacity fits an int
+    for (int el = threadIdx.x; el <= E_loc; el += blockDim.x) s_off[el] = el * capacity;
+  } else if (threadIdx.x == 0) {
+    s_off[E_loc] = total;
+  }
   lds_barrier();
   for (int el = threadIdx.x; el < E_loc; el += blockDim.x) counts[el] = s_cnt[el];
   for (int el = threadIdx.x; el <= E_loc; el += blockDim.x) offsets[el] = s_off[el];
@@ -93,7 +100,20 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   dst_row[p] = row;
 }
 
-// x_perm[row] = x[src_token[row]] for rows < offsets[E_loc]; 16-byte copies.
+// Padded layout: src_token = -1 on the rows of every expert block past its
+// kept pairs (row r is row r % capacity of expert r / capacity).  The kept
+// rows are the scatter kernel's, so the two write disjoint rows.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict__ counts,
+                                                       int n_rows, int capacity,
+                                                       int32_t* __restrict__ src_token) {
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < n_rows; r += gridDim.x * blockDim.x) {
+    const int el = r / capacity;
+    if (r - el * capacity >= counts[el]) src_token[r] = -1;
+  }
+}
+
+// x_perm[row] = x[src_token[row]] for rows < offsets[E_loc], a zero row where
+// the source is -1 (padding); 16-byte copies.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
                                                           const int32_t* __restrict__ src_token,
                                                           const int32_t* __restrict__ offsets,
@@ -102,6 +122,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   const int row = blockIdx.x;
   if (row >= offsets[E_loc]) return;
   const int t = src_token[row];
+  if (t < 0) {
+    for (int c = threadIdx.x; c < row_vecs; c += blockDim.x)
+      x_perm[(size_t)row * row_vecs + c] = make_uint4(0, 0, 0, 0);
+    return;
+  }
   for (int c = threadIdx.x; c < row_vecs; c += blockDim.x)
     x_perm[(size_t)row * row_vecs + c] = x[(size_t)t * row_vecs + c];
 }
@@ -127,11 +152,21 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
 hipError_t launch_permute_scan(const int32_t* tile_counts, int n_tt, int E_loc,
                                int32_t* tile_base, int32_t* counts, int32_t* offsets, int BM,
                                int max_rows, int max_tiles, int4* tile_map, int32_t* n_tiles,
-                               int capacity, int32_t* dropped, hipStream_t st) {
+                               int capacity, int padded, int32_t* dropped, hipStream_t st) {
   const int threads = E_loc > 512 ? 1024 : (E_loc > 256 ? 512 : 256);
   permute_scan_kernel<<<1, threads, 0, st>>>(tile_counts, n_tt, E_loc, tile_base, counts, offsets,
                                              BM, max_rows, max_tiles, tile_map, n_tiles, capacity,
-                                             dropped);
+                                             padded, dropped);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(const int32_t* counts, int E_loc, int capacity, int32_t* src_token,
+                           hipStream_t st) {
+  const long long n = (long long)E_loc * capacity;
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  pad_rows_kernel<<<(int)(blocks < 2048 ? blocks : 2048), 256, 0, st>>>(counts, (int)n, capacity,
+                                                                         src_token);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(moe_\w+)", out))
@@ -222,19 +222,47 @@ def test_reshard_rejects_before_launch():
 
 
 def test_capacity_entries_reject_before_launch():
-    with pytest.raises(M.MoEError) as e:      # negative capacity
-        M.moe_permute_capacity(P, 4, 2, 8, 0, 8, -1, None, 0, 0, P, P, P, P, None, None, None, 0,
-                               stream=0)
-    assert e.value.status == 1
-    with pytest.raises(M.MoEError) as e:      # misaligned dropped counter
-        M.moe_permute_capacity(P, 4, 2, 8, 0, 8, 3, None, 0, 0, P, P, P, P, None, MIS, None, 0,
-                               stream=0)
-    assert e.value.status == 1
+    for cap, padded, dropped, ws, status in [
+            (-1, 0, None, None, 1),            # negative capacity
+            (3, 0, MIS, None, 1),              # misaligned dropped counter
+            (3, 2, None, None, 1),             # padded is 0 or 1
+            (2 ** 31 - 1, 1, None, P, 1),      # E_loc * capacity does not fit an int
+            (3, 1, None, None, 3)]:            # the padded layout needs a workspace at any T
+        with pytest.raises(M.MoEError) as e:
+            M.moe_permute_capacity(P, 4, 2, 8, 0, 8, cap, padded, None, 0, 0, P, P, P, P, None,
+                                   dropped, ws, 0 if ws is None else 1 << 20, stream=0)
+        assert e.value.status == status, (cap, padded)
     d = M.MoELayerDesc(H=256, E=8, k=2, I_loc=128, e_begin=0, e_end=8, I_shared=0, mode=0, dt=1,
                        w_router=1 << 20, w13=1 << 21, w2=1 << 22)
     with pytest.raises(M.MoEError) as e:
-        M.moe_layer_capacity(d, 4, -5, P, P, P, 1 << 30, stream=0)
+        M.moe_layer_capacity(d, 4, -5, 0, P, P, P, 1 << 30, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:
+        M.moe_layer_capacity(d, 4, 3, 3, P, P, P, 1 << 30, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(M.MoEError) as e:
+        M.moe_layer_capacity(d, 4, 2 ** 31 - 1, 1, P, P, P, 1 << 40, stream=0)
     assert e.value.status == 1
     with pytest.raises(M.MoEError) as e:      # workspace too small
-        M.moe_layer_capacity(d, 4, 3, P, P, P, 10, stream=0)
+        M.moe_layer_capacity(d, 4, 3, 0, P, P, P, 10, stream=0)
     assert e.value.status == 3
+    # the padded layout needs E_loc * capacity rows of h and y_perm: the
+    # dropless workspace is too small for a large capacity
+    n = M.moe_layer_workspace_size(d, 4)
+    with pytest.raises(M.MoEError) as e:
+        M.moe_layer_capacity(d, 4, 1000, 1, P, P, P, n, stream=0)
+    assert e.value.status == 3
+
+
+def test_capacity_workspace_sizes():
+    d = M.MoELayerDesc(H=256, E=8, k=2, I_loc=128, e_begin=0, e_end=8, I_shared=0, mode=0, dt=1,
+                       w_router=1 << 20, w13=1 << 21, w2=1 << 22)
+    T = 100
+    assert M.moe_layer_capacity_workspace_size(d, T, 7, 0) == M.moe_layer_workspace_size(d, T)
+    small = M.moe_layer_capacity_workspace_size(d, T, 0, 1)
+    big = M.moe_layer_capacity_workspace_size(d, T, 1000, 1)
+    # 8 experts x 1000 rows of h (128) and y_perm (256) in bf16, and src_token
+    assert big - small >= 8 * 1000 * (128 + 256) * 2
+    assert M.moe_layer_capacity_workspace_size(d, T, -1, 1) == 0
+    assert M.moe_layer_capacity_workspace_size(d, T, 3, 2) == 0
+    assert M.moe_layer_capacity_workspace_size(d, T, 2 ** 31 - 1, 1) == 0
