@@ -22,9 +22,9 @@
 //      units it finished to a counter once, after its last unit.
 //   4. Down units (16 rows of H, all slots): the block's waves form groups of
 //      KS that split each slot's K range (KS from the host: 1 when I is
-//      short, up to 8 for a long I with few experts); a wave touches its
-//      first W2 loads (into L2), the block waits until every gate/up unit is
-//      counted, then streams.  Results stay in LDS, where the block combines
+//      short, up to 8 for a long I with few experts); a wave issues its first
+//      batch of W2 loads, waits until every gate/up unit is counted, then
+//      loads h and streams.  Results stay in LDS, where the block combines
 //      them per token in slot order (plus the shared expert, weight 1) and
 //      writes 16 columns of y.
 // Units are dealt statically (every block derives the same lists from the
@@ -417,23 +417,13 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
     int max_n = 0;
     for (int sl = 0; sl < nslot; ++sl) max_n = max(max_n, s_slot_n[sl]);
     const int v0 = NB - 1 - b;
-    if (v0 < nhb && U1 > 0 && !g1_last) {
-      // bring this wave's first W2 loads into L2 while the block waits for
-      // every h row
-      if (grp < nslot) {
-        const int el = s_slot_e[grp];
-        const int Ia = el < 0 ? a.Is : a.I;
-        const bf16_t* wp =
-            (el < 0 ? a.w2s : a.w2 + (size_t)el * H * a.I) + (size_t)(16 * v0 + r16) * Ia + kg;
-        const int S2 = Ia / 32;
-        const int kb = (S2 * kq) / KS, ke = (S2 * (kq + 1)) / KS;
-        uint32_t touch = 0;
-        for (int q = 0; q < DEC_U && kb + q < ke; ++q) touch ^= ld16(wp + (kb + q) * 32).x;
-        asm volatile("" ::"v"(touch));
-      }
-      if (tid == 0 && !wait_flag(my_flag, 2u * ep + 2u, false)) set_error(sync, 2);
-      __syncthreads();
-    }
+    // Each wave waits for the gate/up units inside its first batch, between
+    // that batch's W2 loads (which do not depend on h) and its h loads, so
+    // the weights are in flight during the wait; a wave that reads no h does
+    // not wait.  (Touching the first W2 loads into L2 before a block-wide
+    // wait instead left the first batches of a workgroup's 16 waves to
+    // complete one SIMD slot after another, about a memory round trip apart.)
+    bool waiting = v0 < nhb && U1 > 0 && !g1_last;
     for (int v = v0; v < nhb; v += NB) {
       const int hr0 = 16 * v;
       for (int r = 0; r < rounds; ++r) {
@@ -455,9 +445,16 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
             for (int s = kb; s < ke; s += DEC_U) {
               uint4 wv[DEC_U], hv[DEC_U];
 #pragma unroll
+              for (int q = 0; q < DEC_U; ++q) wv[q] = ld16(wp + min(s + q, ke - 1) * 32);
+              if (waiting) {
+                if (lane == 0 && !wait_flag(my_flag, 2u * ep + 2u, false)) set_error(sync, 2);
+                waiting = false;
+                // no h load may be moved above the wait
+                asm volatile("" ::: "memory");
+              }
+#pragma unroll
               for (int q = 0; q < DEC_U; ++q) {
                 const int ko = min(s + q, ke - 1) * 32;
-                wv[q] = ld16(wp + ko);
                 hv[q] = mv ? load_coherent16(hq + ko) : make_uint4(0, 0, 0, 0);
               }
 #pragma unroll
