@@ -30,7 +30,8 @@
  *     y = W2 * (SiLU(W_gate x) * (W_up x)),  SiLU(z) = z / (1 + exp(-z)).
  * - `stream` is a hipStream_t (NULL = the null stream).  Calls are enqueued
  *   on it asynchronously; no call copies between host and device or
- *   synchronises, so every call may be captured in a HIP graph.
+ *   synchronises (except in the MOE_VALIDATE=1 mode below), so every call
+ *   may be captured in a HIP graph.
  * - Arguments are checked on the host before anything is enqueued; a failed
  *   check returns an error and enqueues nothing.  A kernel launch failure
  *   returns MOE_ERR_HIP.  T = 0 is a successful no-op (moe_permute still
@@ -41,7 +42,21 @@
  *   floating-point values or to order rows (the decode path's atomics only
  *   count finished work).
  * - Inference is dropless: every (token, slot) pair routed to a local expert
- *   is computed ([CS349D L8] section 1.4).
+ *   is computed ([CS349D L8] section 1.4), except through the explicit
+ *   capacity entry points.
+ * - Metadata checks ([MoE guide] section "Dispatch 并不是一次普通 all-to-all":
+ *   counts and offsets must be exact, or rows are misrouted silently).  With
+ *   MOE_VALIDATE=1 in the environment (read at every call), moe_permute,
+ *   moe_permute_capacity and the layer entry points check on the device, after
+ *   the metadata is built, that every id is in [0, E), that the offsets start
+ *   at 0 and step by the counts (padded layout: i * capacity), that the counts
+ *   add up to the local pairs (less the dropped ones) and stay within the
+ *   capacity.  The result word is copied to the host and the call waits for
+ *   its stream, then returns MOE_ERR_METADATA if a check failed (the call's
+ *   outputs are written either way).  Such calls synchronise and cannot be
+ *   captured in a graph.  The word lives in the caller's workspace: the
+ *   permute workspace grows by 256 bytes in this mode (and is then needed at
+ *   every T), the layer uses bytes 32..35 of its synchronisation block.
  * - Non-finite inputs are outside the contract.
  */
 #ifndef MOE_MI355X_H
@@ -62,7 +77,7 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 2,   /* valid but outside the shape / dtype / mode limits above */
   MOE_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than the size query */
   MOE_ERR_HIP = 4,           /* a HIP launch returned an error */
-  MOE_ERR_METADATA = 5       /* reserved: device-side metadata check failed */
+  MOE_ERR_METADATA = 5       /* the metadata check of MOE_VALIDATE=1 failed (below) */
 } moe_status;
 
 typedef enum {
@@ -124,7 +139,8 @@ int moe_route(const void* x, const void* w_router, int dt, int T, int H, int E, 
  *   src_token[T*k] (first offsets[E_loc] entries written), dst_row[T][k]: int32
  *   (topk_ids, src_token and dst_row may be NULL when T = 0).
  *   ws: at least moe_permute_workspace_size(T, k, E_loc) bytes (may be NULL
- *   when T <= 64: a single tile needs no workspace).
+ *   when T <= 64: a single tile needs no workspace; not with MOE_VALIDATE=1,
+ *   whose result word is kept there).
  */
 size_t moe_permute_workspace_size(int T, int k, int E_loc);
 int moe_permute(const int32_t* topk_ids, int T, int k, int E, int e_begin, int e_end,
@@ -348,7 +364,8 @@ typedef struct {
  * workspace) before the first call that uses the workspace.  Every call
  * leaves it valid for the next; the staged path never touches it.  Calls that
  * share a workspace must be ordered (one stream, or events), as for any
- * scratch buffer.  Bytes 4..7 hold an int32 error word that the decode path
+ * scratch buffer.  Bytes 32..35 receive the result of the MOE_VALIDATE=1
+ * metadata check.  Bytes 4..7 hold an int32 error word that the decode path
  * sets (bit 0: the router wait, bit 1: an expert wait) if a wait for another
  * workgroup exceeds its bound -- a grid that could not be resident at once;
  * that call's outputs are then undefined.  It stays set until the caller

@@ -2,6 +2,7 @@
 // Declarations and the full contract are in include/moe.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <climits>
@@ -182,6 +183,28 @@ int check_layer_call(const moe_layer_desc* d, int T, const void* x, void* y, voi
   return MOE_OK;
 }
 
+// MOE_VALIDATE=1 in the environment (read at every call): after the routing
+// metadata is built, check it on the device and return MOE_ERR_METADATA if it
+// is inconsistent.  The check copies its result word to the host and waits
+// for the stream, so such calls cannot be captured in a graph.
+bool validate_on() {
+  const char* v = getenv("MOE_VALIDATE");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+constexpr size_t VALIDATE_BYTES = 256;   // the result word, at a 256-byte boundary
+constexpr int LAYER_VALIDATE_INT = 8;    // its int index in the layer's sync block
+
+int check_meta(const int32_t* ids, int npair, int E, int e_begin, int e_end, const int32_t* counts,
+               const int32_t* offsets, int capacity, int padded, const int32_t* dropped,
+               int32_t* err, hipStream_t s) {
+  MOE_TRY(launch_validate_meta(ids, npair, E, e_begin, e_end, counts, offsets, capacity, padded,
+                               dropped, err, s));
+  int32_t word = 0;
+  MOE_TRY(hipMemcpyAsync(&word, err, sizeof(word), hipMemcpyDeviceToHost, s));
+  MOE_TRY(hipStreamSynchronize(s));
+  return word ? MOE_ERR_METADATA : MOE_OK;
+}
+
 int run_decode(const moe_layer_desc* d, int T, const void* x, void* y, const LayerWs& l,
                moe_debug_out* dbg, hipStream_t s) {
   auto mark = [&](int i) -> hipError_t {
@@ -203,9 +226,19 @@ int run_decode(const moe_layer_desc* d, int T, const void* x, void* y, const Lay
   }
   a.T = T; a.H = d->H; a.E = d->E; a.k = d->k; a.mode = d->mode;
   a.I_loc = d->I_loc; a.I_shared = d->I_shared; a.e_begin = d->e_begin; a.e_end = d->e_end;
+  const bool check = validate_on();
+  if (check) {
+    // the kernel's metadata lives in LDS; have it written out to be checked
+    if (!a.ids_out) a.ids_out = l.ids;
+    if (!a.counts_out) a.counts_out = l.counts;
+    if (!a.offsets_out) a.offsets_out = l.offsets;
+  }
   MOE_TRY(mark(0));
   MOE_TRY(launch_decode(a, s));
   for (int i = 1; i < MOE_STAGE_EVENTS; ++i) MOE_TRY(mark(i));
+  if (check)
+    return check_meta(a.ids_out, T * d->k, d->E, d->e_begin, d->e_end, a.counts_out,
+                      a.offsets_out, INT_MAX, 0, nullptr, l.sync + LAYER_VALIDATE_INT, s);
   return MOE_OK;
 }
 
@@ -258,10 +291,14 @@ int moe_route(const void* x, const void* w_router, int dt, int T, int H, int E, 
   return hip_status(launch_gate_tiles(a, cdiv(T, TOK_TILE), s));
 }
 
-size_t moe_permute_workspace_size(int T, int k, int E_loc) {
-  if (T < 0 || k < 1 || E_loc < 1) return 0;
+static size_t permute_ws_base(int T, int k, int E_loc) {
   const int n_tt = cdiv(T, TOK_TILE);
   return align_up((size_t)n_tt * E_loc * 4) * 2 + align_up((size_t)T * k * 4);
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E_loc) {
+  if (T < 0 || k < 1 || E_loc < 1) return 0;
+  return permute_ws_base(T, k, E_loc) + (validate_on() ? VALIDATE_BYTES : 0);
 }
 
 // Rows of the padded capacity layout (E_loc * capacity), or -1 if that does
@@ -297,9 +334,10 @@ static int permute_impl(const int32_t* topk_ids, int T, int k, int E, int e_begi
     if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
   }
   const size_t need = moe_permute_workspace_size(T, k, E_loc);
+  const bool check = validate_on();      // the result word needs the workspace
   // the padded layout's offsets come from the scan kernel
   const bool single = T <= TOK_TILE && !padded;
-  if (!single && need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if ((!single || check) && need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n_tt = cdiv(T, TOK_TILE);
@@ -332,6 +370,12 @@ static int permute_impl(const int32_t* topk_ids, int T, int k, int E, int e_begi
   if (x && gather_rows > 0)
     MOE_TRY(launch_gather_rows(x, src_token, offsets, E_loc, gather_rows, H, elt_bytes(dt), x_perm,
                                s));
+  if (check)
+    return check_meta(topk_ids, T * k, E, e_begin, e_end, counts, offsets, capacity, padded,
+                      dropped,
+                      reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                                 permute_ws_base(T, k, E_loc)),
+                      s);
   return MOE_OK;
 }
 
@@ -619,6 +663,9 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   MOE_TRY(launch_combine(l.y_perm, d->dt, l.dst_row, l.w, T, d->k, d->H,
                          d->I_shared > 0 ? l.y_s : nullptr, y, d->dt, s));
   MOE_TRY(mark(5));
+  if (validate_on())
+    return check_meta(l.ids, T * d->k, d->E, d->e_begin, d->e_end, l.counts, l.offsets, capacity,
+                      padded, dropped, l.sync + LAYER_VALIDATE_INT, s);
   return MOE_OK;
 }
 

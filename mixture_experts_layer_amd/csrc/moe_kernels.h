@@ -76,6 +76,10 @@ hipError_t launch_permute_scatter(const int32_t* ids, const int32_t* rank, const
 hipError_t launch_gather_rows(const void* x, const int32_t* src_token, const int32_t* offsets,
                               int E_loc, int max_rows, int H, int elt_bytes, void* x_perm,
                               hipStream_t st);
+// Routing-metadata checks into err[0] (0: consistent); see permute.hip.
+hipError_t launch_validate_meta(const int32_t* ids, int npair, int E, int e_begin, int e_end,
+                                const int32_t* counts, const int32_t* offsets, int capacity,
+                                int padded, const int32_t* dropped, int32_t* err, hipStream_t st);
 hipError_t launch_tile_map_from_offsets(const int32_t* offsets, int E_loc, int BM, int max_rows,
                                         int max_tiles, int4* tile_map, int32_t* n_tiles,
                                         hipStream_t st);

@@ -10,6 +10,8 @@
 // 指南", section Capacity、padding 与 token dropping); in the padded layout of
 // that section every expert owns a fixed block of `capacity` rows, its kept
 // pairs first, then padding rows whose source is -1.
+#include <climits>
+
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -131,6 +133,60 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
     x_perm[(size_t)row * row_vecs + c] = x[(size_t)t * row_vecs + c];
 }
 
+// Checks of the routing metadata, for callers that ask for them ("MoE 推理优化
+// 全景指南", section Dispatch 并不是一次普通 all-to-all: wrong counts or
+// offsets misroute rows without any error).  One block; err[0] receives
+//   bit 0  an id outside [0, E)
+//   bit 1  offsets that do not start at 0 or disagree with counts (padded
+//          layout: offsets[i] != i * capacity)
+//   bit 2  counts that do not add up to the local pairs less the dropped
+//          ones (without a dropped word and with a capacity: more than them)
+//   bit 3  a count below 0 or above the capacity
+// or 0.  Integer sums only; the result does not depend on thread timing.
+__global__ __launch_bounds__(256) void validate_meta_kernel(
+    const int32_t* __restrict__ ids, int npair, int E, int e_begin, int e_end,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int capacity,
+    int padded, const int32_t* __restrict__ dropped, int32_t* __restrict__ err) {
+  __shared__ int s_bits, s_local, s_sum;
+  if (threadIdx.x == 0) {
+    s_bits = 0;
+    s_local = 0;
+    s_sum = 0;
+  }
+  __syncthreads();
+  int bits = 0, local = 0, sum = 0;
+  for (int p = threadIdx.x; p < npair; p += blockDim.x) {
+    const int e = ids[p];
+    if (e < 0 || e >= E) bits |= 1;
+    if (e >= e_begin && e < e_end) ++local;
+  }
+  const int E_loc = e_end - e_begin;
+  for (int el = threadIdx.x; el < E_loc; el += blockDim.x) {
+    const int c = counts[el], o0 = offsets[el], o1 = offsets[el + 1];
+    sum += c;
+    if (c < 0 || c > capacity) bits |= 8;
+    if (padded) {
+      // the host has checked that E_loc * capacity fits an int
+      if (o0 != el * capacity || o1 != (el + 1) * capacity) bits |= 2;
+    } else if (o1 - o0 != c) {
+      bits |= 2;
+    }
+  }
+  if (threadIdx.x == 0 && offsets[0] != 0) bits |= 2;
+  atomicOr(&s_bits, bits);
+  atomicAdd(&s_local, local);
+  atomicAdd(&s_sum, sum);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int b = s_bits;
+    const int d = dropped ? dropped[0] : -1;
+    const bool bad = d >= 0 ? s_sum + d != s_local
+                            : (capacity == INT_MAX ? s_sum != s_local : s_sum > s_local);
+    if (bad) b |= 4;
+    err[0] = b;
+  }
+}
+
 // Tile map for a standalone grouped-FFN call, from device offsets.
 __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets,
                                                        int E_loc, int BM, int max_rows,
@@ -189,6 +245,14 @@ hipError_t launch_gather_rows(const void* x, const int32_t* src_token, const int
   const int row_vecs = H * elt_bytes / 16;
   gather_rows_kernel<<<max_rows, 256, 0, st>>>((const uint4*)x, src_token, offsets, E_loc,
                                                row_vecs, (uint4*)x_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate_meta(const int32_t* ids, int npair, int E, int e_begin, int e_end,
+                                const int32_t* counts, const int32_t* offsets, int capacity,
+                                int padded, const int32_t* dropped, int32_t* err, hipStream_t st) {
+  validate_meta_kernel<<<1, 256, 0, st>>>(ids, npair, E, e_begin, e_end, counts, offsets, capacity,
+                                          padded, dropped, err);
   return hipGetLastError();
 }
 

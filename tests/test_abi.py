@@ -266,3 +266,15 @@ def test_capacity_workspace_sizes():
     assert M.moe_layer_capacity_workspace_size(d, T, -1, 1) == 0
     assert M.moe_layer_capacity_workspace_size(d, T, 3, 2) == 0
     assert M.moe_layer_capacity_workspace_size(d, T, 2 ** 31 - 1, 1) == 0
+
+
+def test_validate_mode_keeps_its_result_word_in_the_workspace(monkeypatch):
+    monkeypatch.delenv("MOE_VALIDATE", raising=False)
+    base = M.moe_permute_workspace_size(100, 4, 16)
+    monkeypatch.setenv("MOE_VALIDATE", "1")
+    assert M.moe_permute_workspace_size(100, 4, 16) == base + 256
+    # a single-tile batch needs a workspace in this mode
+    with pytest.raises(M.MoEError) as e:
+        M.moe_permute(P, 4, 2, 8, 0, 8, None, 0, 0, P, P, P, P, None, None, 0, stream=0)
+    assert e.value.status == 3
+    assert M.moe_status_str(5) == "routing metadata check failed"
