@@ -8,7 +8,7 @@
 //
 // One grid of one 16-wave block per CU, every block resident at once (the
 // host sizes the grid from the occupancy of this kernel).  Phases:
-//   1. Router: wave units (expert, 8 tokens) write float32 logits; every block
+//   1. Router: wave units (expert, 4 tokens) write float32 logits; every block
 //      then arrives at a counter and waits for all blocks.
 //   2. Gating, repeated by every block for all T <= 64 tokens (gate_row), and
 //      the routing metadata in LDS: a 64-bit token mask per local expert gives
@@ -191,14 +191,14 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
   int* flags = sync + SYNC_FLAGS;
   const int* my_flag = flags + b * FLAG_STRIDE;
 
-  // ---- 1. router logits: wave unit (expert e, tokens t0 .. t0 + 7), dealt
+  // ---- 1. router logits: wave unit (expert e, tokens t0 .. t0 + 3), dealt
   // over the blocks first so that as many CUs as possible stream W_r --------
   {
-    const int ntg = (T + 7) >> 3;
+    const int ntg = (T + 3) >> 2;
     for (int u = b + wid * NB; u < E * ntg; u += NB * DEC_WAVES) {
-      const int e = u / ntg, t0 = (u - e * ntg) * 8;
-      router_dot_wave<bf16_t, true>(a.x, a.wr, H, E, e, t0, min(8, T - t0), a.logit_bias,
-                                    a.logits);
+      const int e = u / ntg, t0 = (u - e * ntg) * 4;
+      router_dot_wave<bf16_t, true, 2, 4>(a.x, a.wr, H, E, e, t0, min(4, T - t0), a.logit_bias,
+                                          a.logits);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's logit stores completed

@@ -8,67 +8,82 @@
 
 namespace moe {
 
-// Logits of tokens t0 .. t0 + nt - 1 (nt <= 8) against expert e, computed by
+// Logits of tokens t0 .. t0 + nt - 1 (nt <= NTM <= 8) against expert e, computed by
 // the calling wave (all 64 lanes): lane l takes the 16-byte chunks l, l + 64,
 // ... of the H axis and accumulates them in H order with fmaf; a fixed xor
 // butterfly then sums the 64 lanes.  Lane 0 stores logits[t][e] (+ bias[e]).
-// The chunks are taken 8 at a time, the weight row's loads and then every
-// token's loads issued before the first multiply, so a group costs one
-// memory round trip rather than one per chunk.
+// The chunks are taken in groups, and a group's weight loads and every
+// token's loads are issued before the first multiply, so a group costs one
+// memory round trip: 8 chunks per group for a single token, GM for several
+// (GM * (nt + 1) loads in flight per lane).  Every lane visits its chunks in
+// the same order whatever the grouping, so the logits are bit-identical.
 // COHERENT: store with a device-scope atomic (visible to other workgroups of
 // the running kernel once the store has completed); same value either way.
-template <typename Tin, bool COHERENT = false>
+template <typename Tin>
+__device__ __forceinline__ void router_fma_chunk(const uint4& wraw, const uint4& xraw, float& a) {
+  constexpr int VEC = 16 / sizeof(Tin);
+  float wv[8], xv[8];
+  if constexpr (VEC == 8) {
+    unpack_bf16x8(wraw, wv);
+    unpack_bf16x8(xraw, xv);
+  } else {
+    wv[0] = __uint_as_float(wraw.x); wv[1] = __uint_as_float(wraw.y);
+    wv[2] = __uint_as_float(wraw.z); wv[3] = __uint_as_float(wraw.w);
+    xv[0] = __uint_as_float(xraw.x); xv[1] = __uint_as_float(xraw.y);
+    xv[2] = __uint_as_float(xraw.z); xv[3] = __uint_as_float(xraw.w);
+  }
+#pragma unroll
+  for (int q = 0; q < VEC; ++q) a = fmaf(xv[q], wv[q], a);
+}
+
+template <typename Tin, bool COHERENT = false, int GM = 2, int NTM = 8>
 __device__ __forceinline__ void router_dot_wave(const Tin* __restrict__ x, const Tin* __restrict__ wr,
                                        int H, int E, int e, int t0, int nt,
                                        const float* __restrict__ bias, float* __restrict__ logits) {
   constexpr int VEC = 16 / sizeof(Tin);  // elements per 16-byte load
-  constexpr int G = 8;                   // chunks per group
   const int lane = threadIdx.x & 63;
   const Tin* wrow = wr + (size_t)e * H;
-  float acc[8];
+  float acc[NTM];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int h0 = VEC * lane; h0 < H; h0 += G * 64 * VEC) {
-    uint4 wraw[G];
+  for (int i = 0; i < NTM; ++i) acc[i] = 0.f;
+  auto ld = [&](const Tin* p, int h) {
+    return h < H ? *reinterpret_cast<const uint4*>(p + h) : make_uint4(0, 0, 0, 0);
+  };
+  if (nt == 1) {
+    constexpr int G = 8;
+    const Tin* xr = x + (size_t)t0 * H;
+    for (int h0 = VEC * lane; h0 < H; h0 += G * 64 * VEC) {
+      uint4 wraw[G], xraw[G];
 #pragma unroll
-    for (int c = 0; c < G; ++c) {
-      const int h = h0 + c * 64 * VEC;
-      wraw[c] = h < H ? *reinterpret_cast<const uint4*>(wrow + h) : make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < G; ++c) wraw[c] = ld(wrow, h0 + c * 64 * VEC);
+#pragma unroll
+      for (int c = 0; c < G; ++c) xraw[c] = ld(xr, h0 + c * 64 * VEC);
+#pragma unroll
+      for (int c = 0; c < G; ++c)
+        if (h0 + c * 64 * VEC < H) router_fma_chunk<Tin>(wraw[c], xraw[c], acc[0]);
     }
+  } else {
+    for (int h0 = VEC * lane; h0 < H; h0 += GM * 64 * VEC) {
+      uint4 wraw[GM], xraw[NTM][GM];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < nt) {
-        uint4 xraw[G];
+      for (int c = 0; c < GM; ++c) wraw[c] = ld(wrow, h0 + c * 64 * VEC);
 #pragma unroll
-        for (int c = 0; c < G; ++c) {
-          const int h = h0 + c * 64 * VEC;
-          xraw[c] = h < H ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + i) * H + h)
-                          : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NTM; ++i)
+#pragma unroll
+        for (int c = 0; c < GM; ++c)
+          xraw[i][c] = i < nt ? ld(x + (size_t)(t0 + i) * H, h0 + c * 64 * VEC)
+                              : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NTM; ++i)
+        if (i < nt) {
+#pragma unroll
+          for (int c = 0; c < GM; ++c)
+            if (h0 + c * 64 * VEC < H) router_fma_chunk<Tin>(wraw[c], xraw[i][c], acc[i]);
         }
-        float a = acc[i];
-#pragma unroll
-        for (int c = 0; c < G; ++c) {
-          if (h0 + c * 64 * VEC < H) {
-            float wv[8], xv[8];
-            if constexpr (VEC == 8) {
-              unpack_bf16x8(wraw[c], wv);
-              unpack_bf16x8(xraw[c], xv);
-            } else {
-              wv[0] = __uint_as_float(wraw[c].x); wv[1] = __uint_as_float(wraw[c].y);
-              wv[2] = __uint_as_float(wraw[c].z); wv[3] = __uint_as_float(wraw[c].w);
-              xv[0] = __uint_as_float(xraw[c].x); xv[1] = __uint_as_float(xraw[c].y);
-              xv[2] = __uint_as_float(xraw[c].z); xv[3] = __uint_as_float(xraw[c].w);
-            }
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) a = fmaf(xv[q], wv[q], a);
-          }
-        }
-        acc[i] = a;
-      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NTM; ++i) {
     if (i < nt) {
       float v = acc[i];
 #pragma unroll

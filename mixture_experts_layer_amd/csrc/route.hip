@@ -12,22 +12,28 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router logits, matrix-vector form: one wave per (expert, group of up to 8
-// tokens), four per block (router_dot_wave: lanes split H, a fixed butterfly
-// sums them, so results are bitwise repeatable and equal to the decode
-// kernel's).  Used for float32 inputs and for small token counts, where the
-// whole of W_r must be streamed once by many CUs.
+// Router logits, matrix-vector form: one wave per (expert, pair of tokens),
+// four per block (router_dot_wave: lanes split H, a fixed butterfly sums
+// them, so results are bitwise repeatable and equal to the decode kernel's).
+// Used for float32 inputs and for small token counts, where the whole of W_r
+// must be streamed by many CUs.  Two tokens per wave keep each wave's loads to
+// one round trip (8 chunks of the weight row and of each token per lane) and
+// give the CUs many waves to switch between; W_r is read once per token pair,
+// mostly from L2.
 // ---------------------------------------------------------------------------
+constexpr int RT_GEMV_TOK = 2;
+
 template <typename Tin>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const Tin* __restrict__ x,
                                                           const Tin* __restrict__ wr, int T, int H,
                                                           int E, const float* __restrict__ bias,
                                                           float* __restrict__ logits) {
-  const int ntg = (T + 7) >> 3;
+  const int ntg = (T + RT_GEMV_TOK - 1) / RT_GEMV_TOK;
   const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (u >= E * ntg) return;
-  const int e = u / ntg, t0 = (u - e * ntg) * 8;
-  router_dot_wave<Tin>(x, wr, H, E, e, t0, min(8, T - t0), bias, logits);
+  const int e = u / ntg, t0 = (u - e * ntg) * RT_GEMV_TOK;
+  router_dot_wave<Tin, false, 8, RT_GEMV_TOK>(x, wr, H, E, e, t0, min(RT_GEMV_TOK, T - t0), bias,
+                                              logits);
 }
 
 // ---------------------------------------------------------------------------
@@ -165,12 +171,12 @@ static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, i
 // wave in 64 distinct banks.  The gate weights are finished in the row and
 // written straight out.
 //
-// Histogram and ranks (no atomics): the tile's (token, slot) pairs are cut
-// into C chunks; thread (chunk, e) counts the pairs of its chunk routed to
-// local expert e, and after a barrier walks the chunk again numbering them
-// from the counts of the chunks before it.  The rank of a pair inside its
-// expert's segment of the tile is that number, so rows keep ascending token
-// order.
+// Histogram and ranks: the tile's tokens routed to a local expert form a
+// 64-bit mask (one bit per token of the tile; a token's k ids are distinct),
+// built with one LDS atomic OR per pair -- the result does not depend on
+// their order.  The expert's count is the mask's popcount, and the rank of
+// pair (t, j) inside the expert's segment of the tile is the popcount of the
+// bits below t, so rows keep ascending token order.
 //
 // single != 0 (the whole batch is this one tile): the block also finishes the
 // permutation -- counts, offsets, dst_row, src_token and the GEMM tile map.
@@ -195,7 +201,8 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
   __shared__ int s_rank[TOK_TILE * KMAX];
   __shared__ __attribute__((aligned(16))) float s_logits[STAGE ? TOK_TILE * GATE_PITCH_MAX : 4];
   __shared__ int s_cnt[1024];
-  __shared__ int s_part[1024];
+  __shared__ unsigned long long s_mask[1024];
+  __shared__ int s_drop;
   __shared__ int s_off[1025];
   __shared__ int s_scr[1024];
   __shared__ int s_tmp[NT + 1];
@@ -237,6 +244,7 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
     }
     const int row = lane >> 4, sub = lane & 15;
     for (int pass = 0; pass * NW * 4 < ntok; ++pass) {
+      if (pass * NW * 4 + wid * 4 >= ntok) break;   // no token of this wave left
       const int tt = pass * NW * 4 + wid * 4 + row;
       const bool live = tt < ntok;
       float s[EPR];
@@ -267,43 +275,19 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
   }
   if (!a.do_permute) return;
   const int npair = ntok * k;
-  // pad the id list to a multiple of 16 with an id no expert has
-  for (int p = npair + threadIdx.x; p < ((npair + 15) & ~15); p += NT) s_ids[p] = -1;
-  lds_barrier();
-
-  // atomic-free histogram and in-tile ranks, 16 ids per LDS read
   const int E_loc = a.e_end - a.e_begin;
-  const int C = E_loc >= NT ? 1 : min(16, NT / E_loc);     // chunks of the pair list
-  const int L = ((npair + C - 1) / C + 15) & ~15;          // pairs per chunk
-  for (int job = threadIdx.x; job < C * E_loc; job += NT) {
-    const int ch = job / E_loc, e = a.e_begin + (job - ch * E_loc);
-    const int p1 = min(npair, (ch + 1) * L);
-    int c = 0;
-    for (int p = ch * L; p < p1; p += 16) {
-      const int4* q = reinterpret_cast<const int4*>(s_ids + p);
-      const int4 w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
-      c += (w0.x == e) + (w0.y == e) + (w0.z == e) + (w0.w == e) + (w1.x == e) + (w1.y == e) +
-           (w1.z == e) + (w1.w == e) + (w2.x == e) + (w2.y == e) + (w2.z == e) + (w2.w == e) +
-           (w3.x == e) + (w3.y == e) + (w3.z == e) + (w3.w == e);
-    }
-    s_part[job] = c;
+  for (int el = threadIdx.x; el < E_loc; el += NT) s_mask[el] = 0ull;
+  if (threadIdx.x == 0) s_drop = 0;
+  lds_barrier();
+  for (int p = threadIdx.x; p < npair; p += NT) {
+    const int el = s_ids[p] - a.e_begin;
+    if (el >= 0 && el < E_loc) atomicOr(&s_mask[el], 1ull << (p / k));
   }
   lds_barrier();
-  for (int job = threadIdx.x; job < C * E_loc; job += NT) {
-    const int ch = job / E_loc, el = job - ch * E_loc, e = a.e_begin + el;
-    int c = 0;
-    for (int q = 0; q < ch; ++q) c += s_part[q * E_loc + el];
-    if (ch == C - 1) s_cnt[el] = c + s_part[job];
-    const int p1 = min(npair, (ch + 1) * L);
-    for (int p = ch * L; p < p1; p += 16) {
-      const int4* q = reinterpret_cast<const int4*>(s_ids + p);
-      const int4 w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
-      const int ids16[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
-                             w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (ids16[j] == e) s_rank[p + j] = c++;
-    }
+  for (int el = threadIdx.x; el < E_loc; el += NT) s_cnt[el] = __popcll(s_mask[el]);
+  for (int p = threadIdx.x; p < npair; p += NT) {
+    const int el = s_ids[p] - a.e_begin;
+    if (el >= 0 && el < E_loc) s_rank[p] = __popcll(s_mask[el] & ((1ull << (p / k)) - 1ull));
   }
   lds_barrier();
 
@@ -320,15 +304,16 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 
 // single tile: finish the permutation here (an expert over capacity keeps
 // its first pairs in token order: their ranks are below the capacity)
+  int drop = 0;
   for (int el = threadIdx.x; el < E_loc; el += NT) {
     const int kept = min(s_cnt[el], a.capacity);
-    s_scr[el] = s_cnt[el] - kept;
+    drop += s_cnt[el] - kept;
     s_cnt[el] = kept;
     s_off[el] = kept;
   }
+  if (a.dropped && drop) atomicAdd(&s_drop, drop);   // an integer total
   lds_barrier();
-  const int n_dropped = block_exclusive_scan(s_scr, E_loc, s_tmp);
-  if (a.dropped && threadIdx.x == 0) a.dropped[0] = n_dropped;
+  if (a.dropped && threadIdx.x == 0) a.dropped[0] = s_drop;
   const int total = block_exclusive_scan(s_off, E_loc, s_tmp);
   if (threadIdx.x == 0) s_off[E_loc] = total;
   lds_barrier();
@@ -357,7 +342,7 @@ hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, in
   // bf16 prefill batches with E a multiple of 4 (16-byte logit stores)
   const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 && E % 4 == 0;
   if (!mfma_shape) {
-    const long long units = (long long)E * ((T + 7) / 8);
+    const long long units = (long long)E * ((T + RT_GEMV_TOK - 1) / RT_GEMV_TOK);
     const int grid = (int)((units + 3) / 4);
     if (dt == 0)
       router_gemv_kernel<float><<<grid, 256, 0, st>>>((const float*)x, (const float*)wr, T, H, E,
