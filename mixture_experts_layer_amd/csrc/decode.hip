@@ -8,7 +8,7 @@
 //
 // One grid of one 16-wave block per CU, every block resident at once (the
 // host sizes the grid from the occupancy of this kernel).  Phases:
-//   1. Router: wave units (expert, 4 tokens) write float32 logits; every block
+//   1. Router: wave units (expert, 2 tokens) write float32 logits; every block
 //      then arrives at a counter and waits for all blocks.
 //   2. Gating, repeated by every block for all T <= 64 tokens (gate_row), and
 //      the routing metadata in LDS: a 64-bit token mask per local expert gives
@@ -191,13 +191,13 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
   int* flags = sync + SYNC_FLAGS;
   const int* my_flag = flags + b * FLAG_STRIDE;
 
-  // ---- 1. router logits: wave unit (expert e, tokens t0 .. t0 + 3), dealt
+  // ---- 1. router logits: wave unit (expert e, tokens t0, t0 + 1), dealt
   // over the blocks first so that as many CUs as possible stream W_r --------
   {
-    const int ntg = (T + 3) >> 2;
+    const int ntg = (T + 1) >> 1;
     for (int u = b + wid * NB; u < E * ntg; u += NB * DEC_WAVES) {
-      const int e = u / ntg, t0 = (u - e * ntg) * 4;
-      router_dot_wave<bf16_t, true, 2, 4>(a.x, a.wr, H, E, e, t0, min(4, T - t0), a.logit_bias,
+      const int e = u / ntg, t0 = (u - e * ntg) * 2;
+      router_dot_wave<bf16_t, true, 4, 2>(a.x, a.wr, H, E, e, t0, min(2, T - t0), a.logit_bias,
                                           a.logits);
     }
   }
