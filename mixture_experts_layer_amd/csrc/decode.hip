@@ -10,7 +10,8 @@
 // host sizes the grid from the occupancy of this kernel).  Phases:
 //   1. Router: wave units (expert, 2 tokens) write float32 logits; every block
 //      then arrives at a counter and waits for all blocks.
-//   2. Gating, repeated by every block for all T <= 64 tokens (gate_row), and
+//   2. Gating, repeated by every block for all T <= 64 tokens (a whole wave per
+//      token while T <= 16, gate_select64; else a 16-lane row, gate_row), and
 //      the routing metadata in LDS: a 64-bit token mask per local expert gives
 //      counts = popcount, offsets by a scan, and the row of (t, j) as
 //      offset + popcount of the mask below bit t -- the stable order of the
@@ -209,9 +210,39 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
     __syncthreads();
   }
 
-  // ---- 2. gating of all T tokens, four per wave per pass ------------------
+  // ---- 2. gating of all T tokens: one per wave while T <= 16, else four per
+  // wave per pass ------------------------------------------------------------
   {
     const int row = lane >> 4, sub = lane & 15;
+    if (T <= DEC_WAVES) {
+      // the whole wave makes the choice (gate_select64: a quarter of
+      // gate_row's keys per lane, so shorter rounds), and every row then
+      // finishes the weights exactly as gate_row would; row 0 keeps them
+      constexpr int EPR64 = (EPR + 3) / 4;
+      const int tt = wid;
+      if (tt < T) {
+        float s64[EPR64], s[EPR];
+#pragma unroll
+        for (int i = 0; i < EPR64; ++i) {
+          const int e = lane + 64 * i;
+          s64[i] = e < E ? load_coherent_f32(a.logits + (size_t)tt * E + e) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < EPR; ++i) {
+          const int e = sub + 16 * i;
+          s[i] = e < E ? load_coherent_f32(a.logits + (size_t)tt * E + e) : 0.f;
+        }
+        unsigned long long c0, c1, first;
+        gate_select64<EPR64>(s64, true, E, k, a.mode, a.sel_bias, c0, c1, first);
+        int id0, id1;
+        float g0, g1;
+        gate_weights<EPR>(s, true, sub, E, k, a.mode, c0, c1, first, id0, g0, id1, g1);
+        if (row == 0 && sub < k) {
+          s_ids[tt * k + sub] = id0;
+          s_w[tt * k + sub] = g0;
+        }
+      }
+    } else
     for (int tt0 = wid * 4; tt0 < T; tt0 += DEC_WAVES * 4) {
       const int tt = tt0 + row;
       const bool live = tt < T;

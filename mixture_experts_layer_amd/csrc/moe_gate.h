@@ -81,35 +81,15 @@ __device__ __forceinline__ void max64_step(unsigned long long& v) {
 // taken at the chosen ids; 2 as 1, renormalised over the k chosen; 3
 // sigmoid(logit) of the chosen, renormalised (no bias in the weights).
 // ---------------------------------------------------------------------------
+// The gate weights of one token from its chosen keys, on the 16-lane row
+// layout of gate_row: lane `sub` holds the logits of experts sub, sub + 16,
+// ... in s[], choice sub in c0 and choice sub + 16 in c1 (packed keys), and
+// `first` is the largest key.
 template <int EPR>
-__device__ __forceinline__ void gate_row(const float (&s)[EPR], bool live, int sub, int E, int k, int mode,
-                                const float* __restrict__ sel_bias, int& id0, float& g0, int& id1,
-                                float& g1) {
-  const bool sig = mode == 3;
-  unsigned long long cand[EPR];
-#pragma unroll
-  for (int i = 0; i < EPR; ++i) {
-    const int e = sub + 16 * i;
-    const bool ok = live && e < E;
-    cand[i] = ok ? pack_key((sig && sel_bias) ? s[i] + sel_bias[e] : s[i], e) : 0ull;
-  }
-  unsigned long long c0 = 0ull, c1 = 0ull, first = 0ull;
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = cand[0];
-#pragma unroll
-    for (int i = 1; i < EPR; ++i) best = cand[i] > best ? cand[i] : best;
-    max64_step<DPP_XOR1>(best);
-    max64_step<DPP_XOR2>(best);
-    max64_step<DPP_HALF_MIRROR>(best);
-    max64_step<DPP_MIRROR>(best);
-    if (r == 0) first = best;
-    if (sub == (r & 15)) {
-      if (r < 16) c0 = best;
-      else c1 = best;
-    }
-#pragma unroll
-    for (int i = 0; i < EPR; ++i) cand[i] = cand[i] == best ? 0ull : cand[i];
-  }
+__device__ __forceinline__ void gate_weights(const float (&s)[EPR], bool live, int sub, int E,
+                                             int k, int mode, unsigned long long c0,
+                                             unsigned long long c1, unsigned long long first,
+                                             int& id0, float& g0, int& id1, float& g1) {
   const bool h0 = live && sub < k, h1 = live && sub + 16 < k;
   id0 = h0 ? packed_id(c0) : -1;
   id1 = h1 ? packed_id(c1) : -1;
@@ -154,6 +134,98 @@ __device__ __forceinline__ void gate_row(const float (&s)[EPR], bool live, int s
       g0 = g0 / ps;
       g1 = g1 / ps;
     }
+  }
+}
+
+template <int EPR>
+__device__ __forceinline__ void gate_row(const float (&s)[EPR], bool live, int sub, int E, int k, int mode,
+                                const float* __restrict__ sel_bias, int& id0, float& g0, int& id1,
+                                float& g1) {
+  const bool sig = mode == 3;
+  unsigned long long cand[EPR];
+#pragma unroll
+  for (int i = 0; i < EPR; ++i) {
+    const int e = sub + 16 * i;
+    const bool ok = live && e < E;
+    cand[i] = ok ? pack_key((sig && sel_bias) ? s[i] + sel_bias[e] : s[i], e) : 0ull;
+  }
+  unsigned long long c0 = 0ull, c1 = 0ull, first = 0ull;
+  for (int r = 0; r < k; ++r) {
+    unsigned long long best = cand[0];
+#pragma unroll
+    for (int i = 1; i < EPR; ++i) best = cand[i] > best ? cand[i] : best;
+    max64_step<DPP_XOR1>(best);
+    max64_step<DPP_XOR2>(best);
+    max64_step<DPP_HALF_MIRROR>(best);
+    max64_step<DPP_MIRROR>(best);
+    if (r == 0) first = best;
+    if (sub == (r & 15)) {
+      if (r < 16) c0 = best;
+      else c1 = best;
+    }
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) cand[i] = cand[i] == best ? 0ull : cand[i];
+  }
+  gate_weights<EPR>(s, live, sub, E, k, mode, c0, c1, first, id0, g0, id1, g1);
+}
+
+// ---------------------------------------------------------------------------
+// The same choice for one token made by a whole wave (all 64 lanes, one token
+// per wave): lane l holds the logits of experts l, l + 64, ... in s64[].
+// Each round's arg-max takes four DPP steps inside the rows and two
+// row-exchange steps (v_permlane16_swap, then v_permlane32_swap) across them,
+// with a quarter of gate_row's keys per lane.  Every lane leaves with the
+// row layout's (c0, c1, first): choice (lane % 16) and (lane % 16) + 16, and
+// the largest key -- the same keys gate_row finds, since they are distinct.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned long long max64_across_rows(unsigned long long v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const unsigned long long a = ((unsigned long long)h[0] << 32) | l[0];
+    const unsigned long long b = ((unsigned long long)h[1] << 32) | l[1];
+    v = a > b ? a : b;                 // the row pair's largest
+  }
+  const uint32_t lo2 = (uint32_t)v, hi2 = (uint32_t)(v >> 32);
+  const auto l = __builtin_amdgcn_permlane32_swap(lo2, lo2, false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi2, hi2, false, false);
+  const unsigned long long a = ((unsigned long long)h[0] << 32) | l[0];
+  const unsigned long long b = ((unsigned long long)h[1] << 32) | l[1];
+  return a > b ? a : b;                // the two halves' largest
+}
+
+template <int EPR64>
+__device__ __forceinline__ void gate_select64(const float (&s64)[EPR64], bool live, int E, int k,
+                                              int mode, const float* __restrict__ sel_bias,
+                                              unsigned long long& c0, unsigned long long& c1,
+                                              unsigned long long& first) {
+  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const bool sig = mode == 3;
+  unsigned long long cand[EPR64];
+#pragma unroll
+  for (int i = 0; i < EPR64; ++i) {
+    const int e = lane + 64 * i;
+    const bool ok = live && e < E;
+    cand[i] = ok ? pack_key((sig && sel_bias) ? s64[i] + sel_bias[e] : s64[i], e) : 0ull;
+  }
+  c0 = c1 = first = 0ull;
+  for (int r = 0; r < k; ++r) {
+    unsigned long long best = cand[0];
+#pragma unroll
+    for (int i = 1; i < EPR64; ++i) best = cand[i] > best ? cand[i] : best;
+    max64_step<DPP_XOR1>(best);
+    max64_step<DPP_XOR2>(best);
+    max64_step<DPP_HALF_MIRROR>(best);
+    max64_step<DPP_MIRROR>(best);
+    best = max64_across_rows(best);
+    if (r == 0) first = best;
+    if (sub == (r & 15)) {
+      if (r < 16) c0 = best;
+      else c1 = best;
+    }
+#pragma unroll
+    for (int i = 0; i < EPR64; ++i) cand[i] = cand[i] == best ? 0ull : cand[i];
   }
 }
 
