@@ -141,6 +141,20 @@ __device__ bool arrive(int* ctr, int inc, int target, int* flags, int nb, uint32
 
 __device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Inclusive prefix sum over the 64 lanes of a wave: a Hillis-Steele scan
+// inside each 16-lane row by DPP row shifts (a lane with no source lane in
+// its row adds 0), then the totals of the rows below, read with readlane.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+            t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
 }  // namespace
 
 struct DecodeArgs {
@@ -285,13 +299,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
       rows += c[j];
       act += c[j] > 0 ? 1 : 0;
     }
-    int rs = rows, as = act;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int ru = __shfl_up(rs, o), au = __shfl_up(as, o);
-      if (lane >= o) { rs += ru; as += au; }
-    }
-    const int R_all = __shfl(rs, 63), n_all = __shfl(as, 63);
+    const int rs = wave_inclusive_scan(rows), as = wave_inclusive_scan(act);
+    const int R_all = __builtin_amdgcn_readlane(rs, 63), n_all = __builtin_amdgcn_readlane(as, 63);
     int off = rs - rows, sl = base + as - act;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
