@@ -76,6 +76,23 @@ def test_decode_matches_staged():
     assert (ya - yb).abs().max().item() <= 1e-2 * yb.abs().max().item()
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("E", [8, 100, 256])
+@pytest.mark.parametrize("T", [1, 16])
+def test_whole_wave_gating_matches_the_staged_path_bitwise(mode, E, T):
+    """While T <= 16 the decode kernel gates each token with a whole wave
+    (a quarter of the keys per lane); its ids and weights must equal the
+    staged path's 16-lane gating bit for bit, in every gating mode."""
+    cfg = dataclasses.replace(W.CONFIGS["deepseek_v3"], mode=mode, I_shared=0)
+    L = W.make_layer(cfg, device=DEV, seed=26 + mode, T_max=T, H=256, I=128, E=E)
+    gl = GpuLayer(L)
+    a = gl.run(T, path="decode")
+    b = gl.run(T, path="staged")
+    torch.cuda.synchronize()
+    for key in ("logits", "ids", "w", "counts", "offsets", "dst_row"):
+        assert torch.equal(a[key], b[key]), key
+
+
 def test_decode_repeated_calls_and_sync_block():
     """Many calls in a row on one workspace (the counter sets alternate), with
     changing T: every call matches the first call at its T bit for bit."""
