@@ -534,7 +534,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
-              "supported; this build runs the single-GPU share of the layer only.", flush=True)
+              "supported: the library computes one GPU's share of the layer, and the exchanges "
+              "between GPUs are not part of it.", flush=True)
         sys.exit(2)
     import torch
     import workloads as W
