@@ -63,7 +63,11 @@ def parse():
                     help="skip the EP <-> TP weight reshard measurement")
     ap.add_argument("--no-capacity", action="store_true",
                     help="skip the capacity-factor (token dropping) measurement")
-    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens in the CPU oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens in the CPU oracle sample (default: the whole batch)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the CPU oracle repeats whole passes over its sample until this much "
+                         "time has been spent")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
                          "(calibrates the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -430,7 +434,7 @@ def reshard_bench(steps, warmup, P=8):
 # CPU oracle baseline (bounded sample)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(bench, n_sample):
+def cpu_baseline(bench, n_sample, min_seconds):
     import numpy as np
     import torch
     from oracle import moe_oracle as O
@@ -442,7 +446,7 @@ def cpu_baseline(bench, n_sample):
     L, cfg = bench.L, bench.cfg
     W = bench.W
     T = bench.T
-    n = min(n_sample, T)
+    n = T if n_sample is None else min(n_sample, T)
     idx = W.sample_rows(T, n, seed=1).numpy()
     f = lambda t: None if t is None else t.float().cpu().numpy()
     x = f(L.x[:T])[idx]
@@ -464,12 +468,16 @@ def cpu_baseline(bench, n_sample):
     kw = {}
     if cfg.I_shared:
         kw = dict(w13_shared=f(L.w13_shared), w2_shared=f(L.w2_shared))
-    t0 = time.perf_counter()
-    O.moe_layer(x, w_r, V(w13_h), V(w2_h), cfg.k, cfg.mode, logit_bias=lb, sel_bias=sb,
-                dtype=np.float32, **kw)
-    dt = time.perf_counter() - t0
-    return dict(value=round(n / dt, 2), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{n} of the {T} tokens (seeded subset), float32 numpy oracle, "
+    passes, dt = 0, 0.0
+    while passes == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        O.moe_layer(x, w_r, V(w13_h), V(w2_h), cfg.k, cfg.mode, logit_bias=lb, sel_bias=sb,
+                    dtype=np.float32, **kw)
+        dt += time.perf_counter() - t0
+        passes += 1
+    what = "all" if n == T else f"{n} (seeded subset) of the"
+    return dict(value=round(passes * n / dt, 2), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{passes} pass(es) over {what} {T} tokens, float32 numpy oracle, "
                        f"per-expert bf16->fp32 widening inside the timed region; {dt:.1f} s")
 
 
@@ -613,7 +621,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(bench, args.cpu_sample)
+        cpu = cpu_baseline(bench, args.cpu_sample, args.cpu_seconds)
 
     imb = max(counts) / (sum(counts) / len(counts)) if sum(counts) else 0.0
     line = {
