@@ -362,7 +362,8 @@ typedef struct {
  * counters, then one 128-byte flag line per workgroup) that the single-launch
  * decode path keeps between calls: ZERO IT ONCE (e.g. zero the whole
  * workspace) before the first call that uses the workspace.  Every call
- * leaves it valid for the next; the staged path never touches it.  Calls that
+ * leaves it valid for the next; the staged path touches only the result
+ * word of the MOE_VALIDATE=1 checks (below).  Calls that
  * share a workspace must be ordered (one stream, or events), as for any
  * scratch buffer.  Bytes 32..35 receive the result of the MOE_VALIDATE=1
  * metadata check.  Bytes 4..7 hold an int32 error word that the decode path
