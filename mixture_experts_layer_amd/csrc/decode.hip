@@ -141,20 +141,6 @@ __device__ bool arrive(int* ctr, int inc, int target, int* flags, int nb, uint32
 
 __device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Inclusive prefix sum over the 64 lanes of a wave: a Hillis-Steele scan
-// inside each 16-lane row by DPP row shifts (a lane with no source lane in
-// its row adds 0), then the totals of the rows below, read with readlane.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
-  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
-            t2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return v + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
-}
-
 }  // namespace
 
 struct DecodeArgs {

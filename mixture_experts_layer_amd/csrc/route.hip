@@ -243,7 +243,44 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
       lds_barrier();
     }
     const int row = lane >> 4, sub = lane & 15;
-    for (int pass = 0; pass * NW * 4 < ntok; ++pass) {
+    if (ntok <= NW) {
+      // a whole wave per token (gate_select64: a quarter of gate_row's keys
+      // per lane, so shorter rounds); every row then finishes the weights
+      // exactly as gate_row would, and row 0 keeps them
+      constexpr int EPR64 = (EPR + 3) / 4;
+      const int tt = wid;
+      if (tt < ntok) {
+        float s64[EPR64], s[EPR];
+#pragma unroll
+        for (int i = 0; i < EPR64; ++i) {
+          const int e = lane + 64 * i;
+          s64[i] = e < E ? (STAGE ? s_logits[tt * P + e] : a.logits[(size_t)(t0 + tt) * E + e])
+                         : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < EPR; ++i) {
+          const int e = sub + 16 * i;
+          s[i] = e < E ? (STAGE ? s_logits[tt * P + e] : a.logits[(size_t)(t0 + tt) * E + e])
+                       : 0.f;
+        }
+        unsigned long long c0, c1, first;
+        gate_select64<EPR64>(s64, true, E, k, mode, a.sel_bias, c0, c1, first);
+        int id0, id1;
+        float g0, g1;
+        gate_weights<EPR>(s, true, sub, E, k, mode, c0, c1, first, id0, g0, id1, g1);
+        if (row == 0 && sub < k) {
+          s_ids[tt * k + sub] = id0;
+          a.ids_out[(size_t)(t0 + tt) * k + sub] = id0;
+          a.w_out[(size_t)(t0 + tt) * k + sub] = g0;
+        }
+        if (row == 0 && sub + 16 < k) {
+          s_ids[tt * k + sub + 16] = id1;
+          a.ids_out[(size_t)(t0 + tt) * k + sub + 16] = id1;
+          a.w_out[(size_t)(t0 + tt) * k + sub + 16] = g1;
+        }
+      }
+    }
+    for (int pass = 0; ntok > NW && pass * NW * 4 < ntok; ++pass) {
       if (pass * NW * 4 + wid * 4 >= ntok) break;   // no token of this wave left
       const int tt = pass * NW * 4 + wid * 4 + row;
       const bool live = tt < ntok;
@@ -304,6 +341,69 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 
 // single tile: finish the permutation here (an expert over capacity keeps
 // its first pairs in token order: their ranks are below the capacity)
+  if (E_loc <= 256) {
+    // wave 0 alone: lane l owns local experts [4l, 4l + 4), and DPP scans
+    // give the row offsets and then the GEMM tile map's entry offsets (the
+    // same values block_exclusive_scan and block_build_tile_map produce)
+    if (wid == 0) {
+      int c[4], rows = 0, drop = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int el = 4 * lane + j;
+        const int n = el < E_loc ? s_cnt[el] : 0;
+        c[j] = min(n, a.capacity);
+        drop += n - c[j];
+        rows += c[j];
+      }
+      const int rs = wave_inclusive_scan(rows);
+      const int total = __builtin_amdgcn_readlane(rs, 63);
+      int off = rs - rows, o[4], nt[4], tiles = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int el = 4 * lane + j;
+        o[j] = off;
+        nt[j] = 0;
+        if (el < E_loc) {
+          s_off[el] = off;
+          a.counts[el] = c[j];
+          a.offsets[el] = off;
+          nt[j] = tiles_of(c[j], off, a.BM, a.max_rows);
+        }
+        tiles += nt[j];
+        off += c[j];
+      }
+      if (a.dropped) {
+        const int ds = wave_inclusive_scan(drop);
+        if (lane == 63) a.dropped[0] = ds;
+      }
+      if (lane == 0) {
+        s_off[E_loc] = total;
+        a.offsets[E_loc] = total;
+      }
+      if (a.tile_map) {
+        const int ts = wave_inclusive_scan(tiles);
+        int tb = ts - tiles;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int4 entry = make_int4(4 * lane + j, o[j], o[j] + c[j], tb);
+          for (int q = 0; q < nt[j] && tb + q < a.max_tiles; ++q) a.tile_map[tb + q] = entry;
+          tb += nt[j];
+        }
+        if (lane == 63) a.n_tiles[0] = min(ts, a.max_tiles);
+      }
+    }
+    lds_barrier();
+    for (int p = threadIdx.x; p < npair; p += NT) {
+      const int e = s_ids[p];
+      int row = -1;
+      if (e >= a.e_begin && e < a.e_end && s_rank[p] < a.capacity) {
+        row = s_off[e - a.e_begin] + s_rank[p];
+        a.src_token[row] = p / k;
+      }
+      a.dst_row[p] = row;
+    }
+    return;
+  }
   int drop = 0;
   for (int el = threadIdx.x; el < E_loc; el += NT) {
     const int kept = min(s_cnt[el], a.capacity);

@@ -78,19 +78,24 @@ def test_decode_matches_staged():
 
 @pytest.mark.parametrize("mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("E", [8, 100, 256])
-@pytest.mark.parametrize("T", [1, 16])
-def test_whole_wave_gating_matches_the_staged_path_bitwise(mode, E, T):
-    """While T <= 16 the decode kernel gates each token with a whole wave
-    (a quarter of the keys per lane); its ids and weights must equal the
-    staged path's 16-lane gating bit for bit, in every gating mode."""
+def test_whole_wave_gating_matches_row_gating_bitwise(mode, E):
+    """A batch (or tile) of at most 16 tokens is gated a whole wave per token
+    (a quarter of the keys per lane), a larger one a 16-lane row per token.
+    Gating is per token, so the first 16 tokens of a 17-token batch (row
+    gating) must get the logits, ids and weights of a 16-token batch
+    (whole-wave gating) bit for bit, on both paths and in every gating mode;
+    at 16 tokens the two paths also agree on the routing metadata."""
     cfg = dataclasses.replace(W.CONFIGS["deepseek_v3"], mode=mode, I_shared=0)
-    L = W.make_layer(cfg, device=DEV, seed=26 + mode, T_max=T, H=256, I=128, E=E)
+    L = W.make_layer(cfg, device=DEV, seed=26 + mode, T_max=17, H=256, I=128, E=E)
     gl = GpuLayer(L)
-    a = gl.run(T, path="decode")
-    b = gl.run(T, path="staged")
+    rows = gl.run(17, path="staged")
+    wave = {path: gl.run(16, path=path) for path in ("staged", "decode")}
     torch.cuda.synchronize()
-    for key in ("logits", "ids", "w", "counts", "offsets", "dst_row"):
-        assert torch.equal(a[key], b[key]), key
+    for path, a in wave.items():
+        for key in ("logits", "ids", "w"):
+            assert torch.equal(a[key], rows[key][:16]), (path, key)
+    for key in ("counts", "offsets", "dst_row"):
+        assert torch.equal(wave["staged"][key], wave["decode"][key]), key
 
 
 def test_decode_repeated_calls_and_sync_block():
