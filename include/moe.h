@@ -340,7 +340,9 @@ typedef struct {
  * a hipEvent_t that moe_layer records on `stream` at stage boundary i:
  *   0 before routing, 1 after the routing metadata (route + permute),
  *   2 after the gate/up GEMM, 3 after the down GEMM, 4 after the shared
- *   expert, 5 after the combine.
+ *   expert, 5 after the combine.  At a few tokens the shared expert's GEMMs
+ *   may run inside the routed GEMMs' launches (stages 2 and 3); stage 4 is
+ *   then empty.
  * (Per-stage timing: the time split between router, dispatch metadata,
  * expert GEMMs and combine.) */
 #define MOE_STAGE_EVENTS 6
@@ -388,7 +390,9 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y,
 int moe_layer_path(const moe_layer_desc* d, int T);
 
 /* Staged path: one launch per step (router, gating + metadata, gate/up GEMM,
- * down GEMM, shared expert, combine), any supported shape and T. */
+ * down GEMM, shared expert, combine), any supported shape and T.  When the
+ * shared expert and the routed experts take the same small-batch GEMM tiles,
+ * the shared expert's two GEMMs ride in the routed GEMMs' launches. */
 int moe_layer_staged(const moe_layer_desc* d, int T, const void* x, void* y,
                      void* ws, size_t ws_bytes, moe_debug_out* dbg, void* stream);
 

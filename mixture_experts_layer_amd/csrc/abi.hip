@@ -643,21 +643,25 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   f.H = d->H; f.I_loc = d->I_loc; f.w13 = d->w13; f.w2 = d->w2;
   f.h = l.h; f.y = l.y_perm; f.dt = d->dt; f.y_dt = d->dt;
   f.x_rows = T; f.h_rows = l.max_rows;
-  MOE_TRY(launch_ffn_gate_up(f, l.BM, s));
-  MOE_TRY(mark(2));
-  MOE_TRY(launch_ffn_down(f, l.BM, s));
-  MOE_TRY(mark(3));
-  // a8: shared expert over every token
+  // a8: shared expert over every token -- in the routed GEMMs' launches when
+  // both take the same direct-kernel tiles (a few tokens: its own grid would
+  // leave most CUs idle), else its own two launches after them
+  FfnArgs g{};
+  int BMs = 0;
   if (d->I_shared > 0) {
-    const int BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared, 1);
-    FfnArgs g{};
+    BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared, 1);
     g.x = x; g.src_token = nullptr; g.tile_map = nullptr; g.n_tiles = nullptr;
     g.M_dense = T; g.max_tiles = cdiv(T, BMs); g.mean_rows = T;
     g.H = d->H; g.I_loc = d->I_shared; g.w13 = d->w13_shared; g.w2 = d->w2_shared;
     g.h = l.h_s; g.y = l.y_s; g.dt = d->dt; g.y_dt = d->dt;
     g.x_rows = T; g.h_rows = T;
-    MOE_TRY(launch_grouped_ffn(g, BMs, s));
   }
+  const bool share = d->I_shared > 0 && ffn_can_share_launch(f, l.BM, g, BMs);
+  MOE_TRY(launch_ffn_gate_up(f, l.BM, s, share ? &g : nullptr));
+  MOE_TRY(mark(2));
+  MOE_TRY(launch_ffn_down(f, l.BM, s, share ? &g : nullptr));
+  MOE_TRY(mark(3));
+  if (d->I_shared > 0 && !share) MOE_TRY(launch_grouped_ffn(g, BMs, s));
   MOE_TRY(mark(4));
   // a9: inverse permutation + weighted sum (+ shared expert)
   MOE_TRY(launch_combine(l.y_perm, d->dt, l.dst_row, l.w, T, d->k, d->H,

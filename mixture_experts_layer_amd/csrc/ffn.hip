@@ -44,9 +44,17 @@ struct DirectArgs {
 //
 // SWIGLU: W rows [n] (gate) and [up_off + n] (up) are multiplied together and
 // the epilogue writes SiLU(gate) * up.
+//
+// One launch may carry two problems of the same tile shape: blocks
+// [0, grid0) take a0 and the rest a1 (the shared expert beside the routed
+// experts, so that one grid covers the CUs).
 // ---------------------------------------------------------------------------
 template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
+__global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, DirectArgs a1,
+                                                             int grid0) {
+  const bool second = (int)blockIdx.x >= grid0;
+  const DirectArgs a = second ? a1 : a0;
+  const int bid = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
   constexpr int NS = SWIGLU ? 2 : 1;
   constexpr int BM = 16 * MT;
   constexpr int BN = 16 * NT;
@@ -58,8 +66,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a) {
   __shared__ float red[NW > 1 ? NW * NACC * 4 * PITCH : 1];
 
   const int n_ntiles = a.N_out / BN;
-  const int tile = blockIdx.x / n_ntiles;
-  const int ntile = blockIdx.x - tile * n_ntiles;
+  const int tile = bid / n_ntiles;
+  const int ntile = bid - tile * n_ntiles;
   int e, r0, r1;
   if (a.tile_map) {
     if (tile >= a.n_tiles[0]) return;
@@ -756,19 +764,23 @@ static int pick_nw(int steps, int max_nw, int batch) {
 }
 
 template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
-static hipError_t launch_direct_t(const DirectArgs& a, int max_tiles, hipStream_t st) {
-  const int grid = max_tiles * (a.N_out / (16 * NT));
-  ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16><<<grid, NW * 64, 0, st>>>(a);
+static hipError_t launch_direct_t(const DirectArgs& a, int max_tiles, const DirectArgs* b,
+                                  int b_tiles, hipStream_t st) {
+  const int grid0 = max_tiles * (a.N_out / (16 * NT));
+  const int grid1 = b ? b_tiles * (b->N_out / (16 * NT)) : 0;
+  ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16><<<grid0 + grid1, NW * 64, 0, st>>>(
+      a, b ? *b : a, grid0);
   return hipGetLastError();
 }
 
 template <int MT, int NT, bool SWIGLU, bool OUT_BF16>
-static hipError_t launch_direct_nw(const DirectArgs& a, int nw, int max_tiles, hipStream_t st) {
+static hipError_t launch_direct_nw(const DirectArgs& a, int nw, int max_tiles, const DirectArgs* b,
+                                   int b_tiles, hipStream_t st) {
   switch (nw) {
-    case 1: return launch_direct_t<MT, NT, 1, SWIGLU, OUT_BF16>(a, max_tiles, st);
-    case 2: return launch_direct_t<MT, NT, 2, SWIGLU, OUT_BF16>(a, max_tiles, st);
-    case 4: return launch_direct_t<MT, NT, 4, SWIGLU, OUT_BF16>(a, max_tiles, st);
-    default: return launch_direct_t<MT, NT, 8, SWIGLU, OUT_BF16>(a, max_tiles, st);
+    case 1: return launch_direct_t<MT, NT, 1, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    case 2: return launch_direct_t<MT, NT, 2, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    case 4: return launch_direct_t<MT, NT, 4, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    default: return launch_direct_t<MT, NT, 8, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
   }
 }
 
@@ -785,9 +797,10 @@ constexpr int direct_batch() {
   return 24 / lps < 2 ? 2 : (24 / lps > 8 ? 8 : 24 / lps);
 }
 
-template <bool SWIGLU, bool OUT_BF16>
-static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, hipStream_t st) {
-  const int steps = a.K / 32;
+// Waves per block of the direct kernel for a row tile and contraction.
+template <bool SWIGLU>
+static int direct_nw(int BM, int K) {
+  const int steps = K / 32;
   // 16-row tiles: at most 8 waves, so two blocks share a CU: one block's LDS
   // reduction and stores overlap the other's weight loads (16-wave blocks
   // left the CU's loads idle during them; 8 ran the gate/up GEMM 9-11%
@@ -800,17 +813,45 @@ static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, hipS
   // for the down projection ran the layer 3-15% faster than 8 at 16-32 rows
   // per expert
   const int max_nw_big = SWIGLU ? 4 : 2;
-  if (BM == 16)
-    return launch_direct_nw<1, DIRECT_NT16, SWIGLU, OUT_BF16>(
-        a, pick_nw(steps, max_nw16, direct_batch<1, DIRECT_NT16, SWIGLU>()), max_tiles, st);
-  if (BM == 32)
-    return launch_direct_nw<2, DIRECT_NT32, SWIGLU, OUT_BF16>(
-        a, pick_nw(steps, max_nw_big, direct_batch<2, DIRECT_NT32, SWIGLU>()), max_tiles, st);
-  return launch_direct_nw<4, DIRECT_NT64, SWIGLU, OUT_BF16>(
-      a, pick_nw(steps, max_nw_big, direct_batch<4, DIRECT_NT64, SWIGLU>()), max_tiles, st);
+  if (BM == 16) return pick_nw(steps, max_nw16, direct_batch<1, DIRECT_NT16, SWIGLU>());
+  if (BM == 32) return pick_nw(steps, max_nw_big, direct_batch<2, DIRECT_NT32, SWIGLU>());
+  return pick_nw(steps, max_nw_big, direct_batch<4, DIRECT_NT64, SWIGLU>());
 }
 
-hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {
+// b (optional, b_tiles row tiles): a second problem in the same launch; its
+// waves per block must equal a's (the caller checks).
+template <bool SWIGLU, bool OUT_BF16>
+static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, const DirectArgs* b,
+                                int b_tiles, hipStream_t st) {
+  const int nw = direct_nw<SWIGLU>(BM, a.K);
+  if (BM == 16)
+    return launch_direct_nw<1, DIRECT_NT16, SWIGLU, OUT_BF16>(a, nw, max_tiles, b, b_tiles, st);
+  if (BM == 32)
+    return launch_direct_nw<2, DIRECT_NT32, SWIGLU, OUT_BF16>(a, nw, max_tiles, b, b_tiles, st);
+  return launch_direct_nw<4, DIRECT_NT64, SWIGLU, OUT_BF16>(a, nw, max_tiles, b, b_tiles, st);
+}
+
+static DirectArgs gate_up_direct(const FfnArgs& a) {
+  return DirectArgs{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
+                    (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h};
+}
+static DirectArgs down_direct(const FfnArgs& a) {
+  return DirectArgs{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
+                    (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y};
+}
+
+bool ffn_can_share_launch(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM) {
+  if (a.dt != 1 || b.dt != 1 || a.y_dt != b.y_dt || BM != b_BM || is_tile_bm(BM)) return false;
+  if (a.max_tiles <= 0 || b.max_tiles <= 0) return false;
+  return direct_nw<true>(BM, a.H) == direct_nw<true>(BM, b.H) &&
+         direct_nw<false>(BM, a.I_loc) == direct_nw<false>(BM, b.I_loc);
+}
+
+hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also) {
+  if (also) {
+    const DirectArgs g1 = gate_up_direct(a), g2 = gate_up_direct(*also);
+    return launch_direct<true, true>(g1, BM, a.max_tiles, &g2, also->max_tiles, st);
+  }
   if (a.max_tiles <= 0) return hipSuccess;
   if (a.dt == 0) {
     F32Args g1{(const float*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
@@ -824,12 +865,15 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st) {
                a.x_rows * a.H * 2};
     return launch_tile<true, true>(t, BM, a.mean_rows, a.max_tiles, st);
   }
-  DirectArgs g1{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
-                (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h};
-  return launch_direct<true, true>(g1, BM, a.max_tiles, st);
+  return launch_direct<true, true>(gate_up_direct(a), BM, a.max_tiles, nullptr, 0, st);
 }
 
-hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st) {
+hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also) {
+  if (also) {
+    const DirectArgs g1 = down_direct(a), g2 = down_direct(*also);
+    if (a.y_dt == 0) return launch_direct<false, false>(g1, BM, a.max_tiles, &g2, also->max_tiles, st);
+    return launch_direct<false, true>(g1, BM, a.max_tiles, &g2, also->max_tiles, st);
+  }
   if (a.max_tiles <= 0) return hipSuccess;
   if (a.dt == 0) {
     F32Args g2{(const float*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
@@ -844,10 +888,8 @@ hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st) {
     if (a.y_dt == 0) return launch_tile<false, false>(t, BM, a.mean_rows, a.max_tiles, st);
     return launch_tile<false, true>(t, BM, a.mean_rows, a.max_tiles, st);
   }
-  DirectArgs g2{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
-                (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y};
-  if (a.y_dt == 0) return launch_direct<false, false>(g2, BM, a.max_tiles, st);
-  return launch_direct<false, true>(g2, BM, a.max_tiles, st);
+  if (a.y_dt == 0) return launch_direct<false, false>(down_direct(a), BM, a.max_tiles, nullptr, 0, st);
+  return launch_direct<false, true>(down_direct(a), BM, a.max_tiles, nullptr, 0, st);
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st) {

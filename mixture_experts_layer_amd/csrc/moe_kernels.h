@@ -106,8 +106,16 @@ struct FfnArgs {
 // tiled kernel), from the expected rows per expert and the number of experts
 // the rows spread over.
 int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts);
-hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st);
-hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st);
+// `also` (optional): a second problem run in the same launch, for which
+// ffn_can_share_launch(a, BM, *also, BM) holds -- the shared expert beside
+// the routed experts at a few tokens, where its own launches would leave most
+// CUs idle.
+hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st,
+                              const FfnArgs* also = nullptr);
+hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also = nullptr);
+// Both problems on the direct kernel (bf16) with one row tile and the same
+// waves per block in each GEMM.
+bool ffn_can_share_launch(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM);
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st);
 
 hipError_t launch_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row,
