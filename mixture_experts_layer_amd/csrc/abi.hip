@@ -643,11 +643,13 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   f.H = d->H; f.I_loc = d->I_loc; f.w13 = d->w13; f.w2 = d->w2;
   f.h = l.h; f.y = l.y_perm; f.dt = d->dt; f.y_dt = d->dt;
   f.x_rows = T; f.h_rows = l.max_rows;
-  // a8: shared expert over every token -- in the routed GEMMs' launches when
-  // both take the same direct-kernel tiles (a few tokens: its own grid would
-  // leave most CUs idle), else its own two launches after them
+  // a8: shared expert over every token.  Where its own row tile would give
+  // its gate/up GEMM fewer blocks than there are CUs (up to a few hundred
+  // tokens), it takes the routed GEMMs' row tile instead and rides in their
+  // launches; else its own two launches follow them.
   FfnArgs g{};
   int BMs = 0;
+  bool share = false;
   if (d->I_shared > 0) {
     BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared, 1);
     g.x = x; g.src_token = nullptr; g.tile_map = nullptr; g.n_tiles = nullptr;
@@ -655,8 +657,17 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
     g.H = d->H; g.I_loc = d->I_shared; g.w13 = d->w13_shared; g.w2 = d->w2_shared;
     g.h = l.h_s; g.y = l.y_s; g.dt = d->dt; g.y_dt = d->dt;
     g.x_rows = T; g.h_rows = T;
+    share = ffn_can_share_launch(f, l.BM, g, BMs);
+    if (!share && ffn_gate_up_blocks(g, BMs) < 256) {   // the 256 CUs
+      FfnArgs g2 = g;
+      g2.max_tiles = cdiv(T, l.BM);
+      if (ffn_can_share_launch(f, l.BM, g2, l.BM)) {
+        g = g2;
+        BMs = l.BM;
+        share = true;
+      }
+    }
   }
-  const bool share = d->I_shared > 0 && ffn_can_share_launch(f, l.BM, g, BMs);
   MOE_TRY(launch_ffn_gate_up(f, l.BM, s, share ? &g : nullptr));
   MOE_TRY(mark(2));
   MOE_TRY(launch_ffn_down(f, l.BM, s, share ? &g : nullptr));

@@ -322,8 +322,12 @@ struct TileOut {
 
 // BUF: operands reach LDS by raw-buffer loads (X and each expert's weights
 // within 4 GiB); otherwise by global loads from 64-bit per-lane pointers.
+// As in the direct kernel, blocks [0, grid0) take a0 and the rest a1.
 template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
-__global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0, TileArgs a1,
+                                                                    int grid0) {
+  const bool second = (int)blockIdx.x >= grid0;
+  const TileArgs a = second ? a1 : a0;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n_cols_tile = SWIGLU ? C::TN / 2 : C::TN;
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a) 
   int e = 0, off = 0, end = a.M_dense, ms = 0, n_active;
   if (a.tile_map) n_active = a.n_tiles[0] * NTn;
   else n_active = ((a.M_dense + C::TM - 1) / C::TM) * NTn;
-  int b = blockIdx.x;
+  int b = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
   if (b >= n_active) return;
   {
     const int per = n_active >> 3;                 // XCD-contiguous numbering
@@ -717,26 +721,35 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
 static bool is_tile_bm(int BM) { return BM == TileBig::TM || BM == TileMed::TM; }
 
 template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
-static hipError_t launch_tile_buf(const TileArgs& a, int max_tiles, hipStream_t st) {
+static hipError_t launch_tile_buf(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
+                                  hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t err = ensure_lds_limit(
       reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF>),
       TileOut<C, SWIGLU, OUT_BF16>::LDS, lds_set);
   if (err != hipSuccess) return err;
-  const int ntn = a.N_out / (SWIGLU ? C::TN / 2 : C::TN);
+  constexpr int cols = SWIGLU ? C::TN / 2 : C::TN;
+  const int grid0 = max_tiles * (a.N_out / cols);
+  const int grid1 = b ? b_tiles * (b->N_out / cols) : 0;
   ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF>
-      <<<max_tiles * ntn, C::NTHR, TileOut<C, SWIGLU, OUT_BF16>::LDS, st>>>(a);
+      <<<grid0 + grid1, C::NTHR, TileOut<C, SWIGLU, OUT_BF16>::LDS, st>>>(a, b ? *b : a, grid0);
   return hipGetLastError();
 }
 
 // Raw-buffer loads (no vector address arithmetic per load: the gate/up GEMM
 // ran 7-9% faster) whenever X's extent is known and X and one expert's
-// weights each fit the 32-bit buffer range.
+// weights each fit the 32-bit buffer range (for both problems of a shared
+// launch).
+static bool tile_buf_ok(const TileArgs& a) {
+  return a.x_bytes > 0 && a.x_bytes <= 0xffffffffLL && a.w_stride * 2 <= 0xffffffffLL;
+}
+
 template <class C, bool SWIGLU, bool OUT_BF16>
-static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, hipStream_t st) {
-  const bool buf = a.x_bytes > 0 && a.x_bytes <= 0xffffffffLL && a.w_stride * 2 <= 0xffffffffLL;
-  if (buf) return launch_tile_buf<C, SWIGLU, OUT_BF16, true>(a, max_tiles, st);
-  return launch_tile_buf<C, SWIGLU, OUT_BF16, false>(a, max_tiles, st);
+static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
+                                  hipStream_t st) {
+  const bool buf = tile_buf_ok(a) && (!b || tile_buf_ok(*b));
+  if (buf) return launch_tile_buf<C, SWIGLU, OUT_BF16, true>(a, max_tiles, b, b_tiles, st);
+  return launch_tile_buf<C, SWIGLU, OUT_BF16, false>(a, max_tiles, b, b_tiles, st);
 }
 
 // N-tiles per group.  One N-tile per group (all M-tiles of an expert that
@@ -744,15 +757,28 @@ static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, hipStream_t 
 // from beyond L2 and ran fastest among groups of 1, 2, 4 and all N-tiles.
 static int tile_group(int /*mean_rows*/, int /*tm*/, int /*ntn*/) { return 1; }
 
+// Tile shape for a row tile and output width: 256-row tiles, 128-row tiles,
+// or (gate/up widths not a multiple of 128) the narrow 128x128 tiles.
+enum TileShape { TILE_BIG, TILE_MED, TILE_NARROW };
+static TileShape tile_shape(int BM, bool swiglu, int N_out) {
+  if (BM == TileBig::TM) return TILE_BIG;
+  if (swiglu && N_out % (TL_N / 2) != 0) return TILE_NARROW;
+  return TILE_MED;
+}
+
 template <bool SWIGLU, bool OUT_BF16>
-static hipError_t launch_tile(TileArgs a, int BM, int mean_rows, int max_tiles, hipStream_t st) {
+static hipError_t launch_tile(TileArgs a, int BM, int mean_rows, int max_tiles, const TileArgs* b,
+                              int b_tiles, hipStream_t st) {
   const int ntn = a.N_out / (SWIGLU ? TL_N / 2 : TL_N);
   a.group = tile_group(mean_rows, BM, ntn);
-  if (BM == TileBig::TM) return launch_tile_cfg<TileBig, SWIGLU, OUT_BF16>(a, max_tiles, st);
-  if constexpr (SWIGLU) {
-    if (a.N_out % (TL_N / 2) != 0) return launch_tile_cfg<TileNarrow, SWIGLU, OUT_BF16>(a, max_tiles, st);
+  switch (tile_shape(BM, SWIGLU, a.N_out)) {
+    case TILE_BIG: return launch_tile_cfg<TileBig, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    case TILE_NARROW:
+      if constexpr (SWIGLU)
+        return launch_tile_cfg<TileNarrow, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+      [[fallthrough]];
+    default: return launch_tile_cfg<TileMed, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
   }
-  return launch_tile_cfg<TileMed, SWIGLU, OUT_BF16>(a, max_tiles, st);
 }
 
 // Waves per block: enough that each wave's K share is one load batch where
@@ -839,18 +865,45 @@ static DirectArgs down_direct(const FfnArgs& a) {
   return DirectArgs{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
                     (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y};
 }
+static TileArgs gate_up_tile(const FfnArgs& a) {
+  return TileArgs{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
+                  (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h, 1,
+                  a.x_rows * a.H * 2};
+}
+static TileArgs down_tile(const FfnArgs& a) {
+  return TileArgs{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
+                  (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y, 1,
+                  a.h_rows * a.I_loc * 2};
+}
 
 bool ffn_can_share_launch(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM) {
-  if (a.dt != 1 || b.dt != 1 || a.y_dt != b.y_dt || BM != b_BM || is_tile_bm(BM)) return false;
+  if (a.dt != 1 || b.dt != 1 || a.y_dt != b.y_dt || BM != b_BM) return false;
   if (a.max_tiles <= 0 || b.max_tiles <= 0) return false;
+  if (is_tile_bm(BM))
+    return tile_shape(BM, true, a.I_loc) == tile_shape(BM, true, b.I_loc) &&
+           ffn_tile_ok(a.H, a.I_loc) && ffn_tile_ok(b.H, b.I_loc);
   return direct_nw<true>(BM, a.H) == direct_nw<true>(BM, b.H) &&
          direct_nw<false>(BM, a.I_loc) == direct_nw<false>(BM, b.I_loc);
 }
 
+long long ffn_gate_up_blocks(const FfnArgs& a, int BM) {
+  if (a.dt == 0) return (long long)a.max_tiles * (a.I_loc / 16);
+  if (is_tile_bm(BM)) {
+    const int cols = tile_shape(BM, true, a.I_loc) == TILE_NARROW ? TileNarrow::TN / 2 : TL_N / 2;
+    return (long long)a.max_tiles * (a.I_loc / cols);
+  }
+  return (long long)a.max_tiles * (a.I_loc / (BM == 16 ? 16 * DIRECT_NT16 : 32));
+}
+
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also) {
   if (also) {
-    const DirectArgs g1 = gate_up_direct(a), g2 = gate_up_direct(*also);
-    return launch_direct<true, true>(g1, BM, a.max_tiles, &g2, also->max_tiles, st);
+    if (is_tile_bm(BM)) {
+      const TileArgs t2 = gate_up_tile(*also);
+      return launch_tile<true, true>(gate_up_tile(a), BM, a.mean_rows, a.max_tiles, &t2,
+                                     also->max_tiles, st);
+    }
+    const DirectArgs g2 = gate_up_direct(*also);
+    return launch_direct<true, true>(gate_up_direct(a), BM, a.max_tiles, &g2, also->max_tiles, st);
   }
   if (a.max_tiles <= 0) return hipSuccess;
   if (a.dt == 0) {
@@ -859,37 +912,38 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st, const Ff
     ffn_f32_kernel<true><<<a.max_tiles * (a.I_loc / 16), 256, 0, st>>>(g1);
     return hipGetLastError();
   }
-  if (is_tile_bm(BM)) {
-    TileArgs t{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
-               (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h, 1,
-               a.x_rows * a.H * 2};
-    return launch_tile<true, true>(t, BM, a.mean_rows, a.max_tiles, st);
-  }
+  if (is_tile_bm(BM))
+    return launch_tile<true, true>(gate_up_tile(a), BM, a.mean_rows, a.max_tiles, nullptr, 0, st);
   return launch_direct<true, true>(gate_up_direct(a), BM, a.max_tiles, nullptr, 0, st);
 }
 
-hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also) {
-  if (also) {
-    const DirectArgs g1 = down_direct(a), g2 = down_direct(*also);
-    if (a.y_dt == 0) return launch_direct<false, false>(g1, BM, a.max_tiles, &g2, also->max_tiles, st);
-    return launch_direct<false, true>(g1, BM, a.max_tiles, &g2, also->max_tiles, st);
+template <bool OUT_BF16>
+static hipError_t launch_down_bf16(const FfnArgs& a, int BM, const FfnArgs* also, hipStream_t st) {
+  if (is_tile_bm(BM)) {
+    if (also) {
+      const TileArgs t2 = down_tile(*also);
+      return launch_tile<false, OUT_BF16>(down_tile(a), BM, a.mean_rows, a.max_tiles, &t2,
+                                          also->max_tiles, st);
+    }
+    return launch_tile<false, OUT_BF16>(down_tile(a), BM, a.mean_rows, a.max_tiles, nullptr, 0, st);
   }
-  if (a.max_tiles <= 0) return hipSuccess;
+  if (also) {
+    const DirectArgs g2 = down_direct(*also);
+    return launch_direct<false, OUT_BF16>(down_direct(a), BM, a.max_tiles, &g2, also->max_tiles, st);
+  }
+  return launch_direct<false, OUT_BF16>(down_direct(a), BM, a.max_tiles, nullptr, 0, st);
+}
+
+hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also) {
+  if (!also && a.max_tiles <= 0) return hipSuccess;
   if (a.dt == 0) {
     F32Args g2{(const float*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
                (const float*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, (float*)a.y};
     ffn_f32_kernel<false><<<a.max_tiles * (a.H / 16), 256, 0, st>>>(g2);
     return hipGetLastError();
   }
-  if (is_tile_bm(BM)) {
-    TileArgs t{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
-               (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y, 1,
-               a.h_rows * a.I_loc * 2};
-    if (a.y_dt == 0) return launch_tile<false, false>(t, BM, a.mean_rows, a.max_tiles, st);
-    return launch_tile<false, true>(t, BM, a.mean_rows, a.max_tiles, st);
-  }
-  if (a.y_dt == 0) return launch_direct<false, false>(down_direct(a), BM, a.max_tiles, nullptr, 0, st);
-  return launch_direct<false, true>(down_direct(a), BM, a.max_tiles, nullptr, 0, st);
+  if (a.y_dt == 0) return launch_down_bf16<false>(a, BM, also, st);
+  return launch_down_bf16<true>(a, BM, also, st);
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st) {

@@ -113,9 +113,11 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts);
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st,
                               const FfnArgs* also = nullptr);
 hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also = nullptr);
-// Both problems on the direct kernel (bf16) with one row tile and the same
-// waves per block in each GEMM.
+// Both problems bf16 with one row tile and the same kernel configuration in
+// each GEMM (tile shape, or waves per block of the direct kernel).
 bool ffn_can_share_launch(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM);
+// Blocks of a's gate/up launch with row tile BM (a.max_tiles row tiles).
+long long ffn_gate_up_blocks(const FfnArgs& a, int BM);
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st);
 
 hipError_t launch_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row,
