@@ -287,6 +287,28 @@ def test_layer_tile_path(name, H, I, E, T):
     check_layer(gl2, gl2.run(T), T)
 
 
+# The shared expert rides in the routed GEMMs' launches or runs in its own,
+# by both problems' tile choices.  At H = 1024, I = 256, E = 64, k = 8 a
+# 256-wide shared expert shares the direct launches (T = 1), takes the
+# routed 16-row tile in place of its own LDS tile (T = 16), shares the
+# LDS-tiled launches (T = 64) and takes the routed 128-row tile in place of
+# its own 256-row one (T = 600).  A 512-wide one runs in its own launches at
+# T = 1 (its down projection takes more waves per block than the routed
+# one) and shares the LDS-tiled launches at T = 64.
+@pytest.mark.parametrize("I_shared,T", [(256, 1), (256, 16), (256, 64), (256, 600), (512, 1),
+                                        (512, 64)])
+def test_shared_expert_with_the_routed_launches(I_shared, T):
+    cfg = W.CONFIGS["deepseek_v3"]
+    H, I, E = 1024, 256, 64
+    L = W.make_layer(cfg, device=DEV, seed=8, T_max=T, H=H, I=I, E=E)
+    s = 1.0 / H ** 0.5
+    L.w13_shared = (torch.randn((2 * I_shared, H), device=DEV) * s).to(torch.bfloat16)
+    L.w2_shared = (torch.randn((H, I_shared), device=DEV) * s).to(torch.bfloat16)
+    for kw in (dict(), dict(e_begin=8, e_end=40)):
+        gl = GpuLayer(L, **kw)
+        check_layer(gl, gl.run(T), T)
+
+
 @pytest.mark.parametrize("T", [1, 9, 64, 200])
 def test_layer_small_tp_and_ep_shares(T):
     cfg = W.CONFIGS["qwen3_ep_all128"]

@@ -88,7 +88,7 @@ CONFIGS = {
         describe="Qwen3-shaped layer, tensor-parallel share of rank 0 of 8 (I/P = 192)"),
     "deepseek_v3": MoEConfig(
         "deepseek_v3", H=7168, I=2048, E=256, k=8, mode=MODE_SIGMOID_BIAS_RENORM,
-        dtype="bf16", T_list=(1, 64, 4096), I_shared=2048, zipf_beta=0.30, sel_bias_std=0.5,
+        dtype="bf16", T_list=(1, 16, 64, 4096), I_shared=2048, zipf_beta=0.30, sel_bias_std=0.5,
         describe="DeepSeek-V3-shaped layer, sigmoid + selection bias, 1 shared expert"),
 }
 
