@@ -163,4 +163,66 @@ __device__ inline void block_build_tile_map(const int* cnt, const int* off, int 
   if (threadIdx.x == 0) n_tiles[0] = min(total, max_tiles);
 }
 
+// ---------------------------------------------------------------------------
+// Routing metadata from per-expert pair totals, by one wave (E_loc <= 256;
+// lane l owns local experts 4l .. 4l + 3): kept = min(total, capacity) per
+// expert into counts; offsets = exclusive prefix sums of kept (el * capacity
+// when padded), offsets[E_loc] their end; the dropped total; and the GEMM
+// tile map (tile_map may be null).  DPP scans give the same values as
+// block_exclusive_scan and block_build_tile_map.  s_off (E_loc + 1 ints of
+// LDS) receives the offsets for the caller.  The host has checked that
+// E_loc * capacity fits an int in the padded layout.
+// ---------------------------------------------------------------------------
+__device__ inline void wave_routing_metadata(const int* total, int E_loc, int capacity, bool padded,
+                                             int BM, int max_rows, int max_tiles, int* s_off,
+                                             int32_t* counts, int32_t* offsets, int32_t* dropped,
+                                             int4* tile_map, int32_t* n_tiles) {
+  const int lane = threadIdx.x & 63;
+  int c[4], rows = 0, drop = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int el = 4 * lane + j;
+    const int n = el < E_loc ? total[el] : 0;
+    c[j] = min(n, capacity);
+    drop += n - c[j];
+    rows += c[j];
+  }
+  const int rs = wave_inclusive_scan(rows);
+  const int end = padded ? E_loc * capacity : __builtin_amdgcn_readlane(rs, 63);
+  int off = rs - rows, o[4], nt[4], tiles = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int el = 4 * lane + j;
+    o[j] = padded ? el * capacity : off;
+    nt[j] = 0;
+    if (el < E_loc) {
+      s_off[el] = o[j];
+      counts[el] = c[j];
+      offsets[el] = o[j];
+      if (tile_map) nt[j] = tiles_of(c[j], o[j], BM, max_rows);
+    }
+    tiles += nt[j];
+    off += c[j];
+  }
+  if (dropped) {
+    const int ds = wave_inclusive_scan(drop);
+    if (lane == 63) dropped[0] = ds;
+  }
+  if (lane == 0) {
+    s_off[E_loc] = end;
+    offsets[E_loc] = end;
+  }
+  if (tile_map) {
+    const int ts = wave_inclusive_scan(tiles);
+    int tb = ts - tiles;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int4 entry = make_int4(4 * lane + j, o[j], o[j] + c[j], tb);
+      for (int q = 0; q < nt[j] && tb + q < max_tiles; ++q) tile_map[tb + q] = entry;
+      tb += nt[j];
+    }
+    if (lane == 63) n_tiles[0] = min(ts, max_tiles);
+  }
+}
+
 }  // namespace moe

@@ -342,56 +342,11 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 // single tile: finish the permutation here (an expert over capacity keeps
 // its first pairs in token order: their ranks are below the capacity)
   if (E_loc <= 256) {
-    // wave 0 alone: lane l owns local experts [4l, 4l + 4), and DPP scans
-    // give the row offsets and then the GEMM tile map's entry offsets (the
-    // same values block_exclusive_scan and block_build_tile_map produce)
-    if (wid == 0) {
-      int c[4], rows = 0, drop = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int el = 4 * lane + j;
-        const int n = el < E_loc ? s_cnt[el] : 0;
-        c[j] = min(n, a.capacity);
-        drop += n - c[j];
-        rows += c[j];
-      }
-      const int rs = wave_inclusive_scan(rows);
-      const int total = __builtin_amdgcn_readlane(rs, 63);
-      int off = rs - rows, o[4], nt[4], tiles = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int el = 4 * lane + j;
-        o[j] = off;
-        nt[j] = 0;
-        if (el < E_loc) {
-          s_off[el] = off;
-          a.counts[el] = c[j];
-          a.offsets[el] = off;
-          nt[j] = tiles_of(c[j], off, a.BM, a.max_rows);
-        }
-        tiles += nt[j];
-        off += c[j];
-      }
-      if (a.dropped) {
-        const int ds = wave_inclusive_scan(drop);
-        if (lane == 63) a.dropped[0] = ds;
-      }
-      if (lane == 0) {
-        s_off[E_loc] = total;
-        a.offsets[E_loc] = total;
-      }
-      if (a.tile_map) {
-        const int ts = wave_inclusive_scan(tiles);
-        int tb = ts - tiles;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int4 entry = make_int4(4 * lane + j, o[j], o[j] + c[j], tb);
-          for (int q = 0; q < nt[j] && tb + q < a.max_tiles; ++q) a.tile_map[tb + q] = entry;
-          tb += nt[j];
-        }
-        if (lane == 63) a.n_tiles[0] = min(ts, a.max_tiles);
-      }
-    }
+    // wave 0 alone (DPP scans; the block-wide scans below are for more
+    // experts)
+    if (wid == 0)
+      wave_routing_metadata(s_cnt, E_loc, a.capacity, false, a.BM, a.max_rows, a.max_tiles, s_off,
+                            a.counts, a.offsets, a.dropped, a.tile_map, a.n_tiles);
     lds_barrier();
     for (int p = threadIdx.x; p < npair; p += NT) {
       const int e = s_ids[p];
