@@ -706,7 +706,14 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
     // a handful of rows each the direct kernel stays ahead.
     // (narrow gate/up tiles -- widths not a multiple of 128 -- run one wave
     // per SIMD and only pay from 16 rows per expert)
-    const int min_rows = I_loc % (TL_N / 2) != 0 ? 16 : (H >= 6144 ? 2 : 4);
+    // With the long contraction the LDS-tiled kernel pays from one row per
+    // expert once the touched experts' gate/up tiles give every CU two
+    // blocks: DeepSeek-V3 shape at T = 8 and 32 (about one row per touched
+    // expert), gate/up GEMM 12-16% faster; with 8 touched experts (T = 1)
+    // its 128 blocks left the CUs short and the direct kernel stayed ahead.
+    int min_rows = 4;
+    if (I_loc % (TL_N / 2) != 0) min_rows = 16;
+    else if (H >= 6144) min_rows = (long long)experts * (I_loc / (TL_N / 2)) >= 512 ? 1 : 2;
     const long long blocks = (long long)experts * ((mean_rows + TileMed::TM - 1) / TileMed::TM) *
                              (H / TileMed::TN);
     if (mean_rows >= min_rows && (blocks >= 256 || mean_rows >= 16)) return TileMed::TM;
