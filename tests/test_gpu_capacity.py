@@ -81,6 +81,31 @@ def test_permute_capacity_matches_oracle(T, cap, eb, ee, padded):
         assert torch.count_nonzero(xp[~live]).item() == 0
 
 
+# More than 256 local experts: the scan block finishes counts, offsets and
+# the dropped total with block-wide scans instead of one wave (T = 40: the
+# gating kernel's own single-tile finish; T = 1000: the scan kernel).
+@pytest.mark.parametrize("T", [40, 1000])
+@pytest.mark.parametrize("cap", ["cf1", "big"])
+@pytest.mark.parametrize("eb,ee", [(0, 300), (10, 290)])
+@pytest.mark.parametrize("padded", [0, 1])
+def test_permute_capacity_many_local_experts(T, cap, eb, ee, padded):
+    E, k = 300, 8
+    ids = _skewed_ids(T, k, E, seed=3 * T + eb)
+    C = O.expert_capacity(1.0, T * k, E) if cap == "cf1" else BIG
+    if padded and cap == "big":
+        pytest.skip("E_loc * capacity does not fit an int (rejected on the host, see test_abi)")
+    out = _permute(ids, E, eb, ee, C, padded)
+    rc, ro, rs, rd, rdrop = O.permute_capacity(ids, eb, ee, C, padded=bool(padded))
+    assert np.array_equal(to_np(out["counts"]), rc)
+    assert np.array_equal(to_np(out["offsets"]), ro)
+    rows = int(ro[-1])
+    assert np.array_equal(to_np(out["src"])[:rows], rs)
+    assert np.array_equal(to_np(out["dst"])[:T], rd)
+    assert int(out["dropped"][0]) == rdrop
+    if cap == "cf1":
+        assert rdrop > 0, "the skew should overflow a capacity at the mean"
+
+
 def test_padded_permute_of_an_empty_batch():
     out = _permute(np.zeros((0, 4), int), 16, 2, 10, 5, 1)
     assert to_np(out["counts"]).tolist() == [0] * 8
