@@ -643,13 +643,19 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   f.H = d->H; f.I_loc = d->I_loc; f.w13 = d->w13; f.w2 = d->w2;
   f.h = l.h; f.y = l.y_perm; f.dt = d->dt; f.y_dt = d->dt;
   f.x_rows = T; f.h_rows = l.max_rows;
-  // a8: shared expert over every token.  Where its own row tile would give
-  // its gate/up GEMM fewer blocks than there are CUs (up to a few hundred
-  // tokens), it takes the routed GEMMs' row tile instead and rides in their
-  // launches; else its own two launches follow them.
+  // the down projection may walk the gate/up GEMM's tile map with a smaller
+  // row tile of its own
+  const int BM_dn = ffn_down_row_tile(d->dt, mean_rows(T, d->k, d->E), d->H, d->I_loc, l.BM);
+  FfnArgs fd = f;
+  if (BM_dn != l.BM) fd.map_bm = l.BM;
+  // a8: shared expert over every token.  For each GEMM: where its own row
+  // tile would give it fewer blocks than there are CUs (up to a few hundred
+  // tokens), it takes the routed GEMM's row tile instead and rides in its
+  // launch; else it has launches of its own.
   FfnArgs g{};
-  int BMs = 0;
-  bool share = false;
+  int BMs = 0, BMs_dn = 0;
+  bool share_up = false, share_dn = false;
+  FfnArgs g_up{}, g_dn{};
   if (d->I_shared > 0) {
     BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared, 1);
     g.x = x; g.src_token = nullptr; g.tile_map = nullptr; g.n_tiles = nullptr;
@@ -657,22 +663,32 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
     g.H = d->H; g.I_loc = d->I_shared; g.w13 = d->w13_shared; g.w2 = d->w2_shared;
     g.h = l.h_s; g.y = l.y_s; g.dt = d->dt; g.y_dt = d->dt;
     g.x_rows = T; g.h_rows = T;
-    share = ffn_can_share_launch(f, l.BM, g, BMs);
-    if (!share && ffn_gate_up_blocks(g, BMs) < 256) {   // the 256 CUs
+    const bool thin = ffn_gate_up_blocks(g, BMs) < 256;   // the 256 CUs
+    auto pick = [&](const FfnArgs& r, int BMr, bool gate_up, FfnArgs& out, int& BMo) {
+      out = g;
+      BMo = BMs;
+      if (ffn_can_share_gemm(r, BMr, g, BMs, gate_up)) return true;
+      if (!thin) return false;
       FfnArgs g2 = g;
-      g2.max_tiles = cdiv(T, l.BM);
-      if (ffn_can_share_launch(f, l.BM, g2, l.BM)) {
-        g = g2;
-        BMs = l.BM;
-        share = true;
-      }
-    }
+      g2.max_tiles = cdiv(T, BMr);
+      if (!ffn_can_share_gemm(r, BMr, g2, BMr, gate_up)) return false;
+      out = g2;
+      BMo = BMr;
+      return true;
+    };
+    int BMs_up = 0;
+    share_up = pick(f, l.BM, true, g_up, BMs_up);
+    share_dn = pick(fd, BM_dn, false, g_dn, BMs_dn);
+    if (!share_dn) { g_dn = g; BMs_dn = BMs; }
   }
-  MOE_TRY(launch_ffn_gate_up(f, l.BM, s, share ? &g : nullptr));
+  MOE_TRY(launch_ffn_gate_up(f, l.BM, s, share_up ? &g_up : nullptr));
   MOE_TRY(mark(2));
-  MOE_TRY(launch_ffn_down(f, l.BM, s, share ? &g : nullptr));
+  // the shared expert's h must be complete before a launch that reads it
+  if (d->I_shared > 0 && !share_up && share_dn) MOE_TRY(launch_ffn_gate_up(g, BMs, s));
+  MOE_TRY(launch_ffn_down(fd, BM_dn, s, share_dn ? &g_dn : nullptr));
   MOE_TRY(mark(3));
-  if (d->I_shared > 0 && !share) MOE_TRY(launch_grouped_ffn(g, BMs, s));
+  if (d->I_shared > 0 && !share_up && !share_dn) MOE_TRY(launch_grouped_ffn(g, BMs, s));
+  else if (d->I_shared > 0 && !share_dn) MOE_TRY(launch_ffn_down(g_dn, BMs_dn, s));
   MOE_TRY(mark(4));
   // a9: inverse permutation + weighted sum (+ shared expert)
   MOE_TRY(launch_combine(l.y_perm, d->dt, l.dst_row, l.w, T, d->k, d->H,

@@ -28,6 +28,7 @@ struct DirectArgs {
   int N_out;                // output columns (multiple of 16 * NT)
   int up_off;               // SwiGLU: row offset of the up half in W
   void* Y;                  // [rows][N_out]
+  int map_bm;               // rows per tile-map entry (>= the kernel's row tile)
 };
 
 // ---------------------------------------------------------------------------
@@ -44,17 +45,12 @@ struct DirectArgs {
 //
 // SWIGLU: W rows [n] (gate) and [up_off + n] (up) are multiplied together and
 // the epilogue writes SiLU(gate) * up.
-//
-// One launch may carry two problems of the same tile shape: blocks
-// [0, grid0) take a0 and the rest a1 (the shared expert beside the routed
-// experts, so that one grid covers the CUs).
 // ---------------------------------------------------------------------------
+// Rows [r0, r1) (at most 16 * MT) of expert e against output columns
+// [n0, n0 + 16 * NT).
 template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, DirectArgs a1,
-                                                             int grid0) {
-  const bool second = (int)blockIdx.x >= grid0;
-  const DirectArgs a = second ? a1 : a0;
-  const int bid = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
+__device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, int r1, int n0,
+                                            float* red) {
   constexpr int NS = SWIGLU ? 2 : 1;
   constexpr int BM = 16 * MT;
   constexpr int BN = 16 * NT;
@@ -63,21 +59,6 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
   // K steps per load batch: about 24 16-byte loads in flight per wave
   constexpr int LPS = NT * NS + MT;                     // loads per K step
   constexpr int U = 24 / LPS < 2 ? 2 : (24 / LPS > 8 ? 8 : 24 / LPS);
-  __shared__ float red[NW > 1 ? NW * NACC * 4 * PITCH : 1];
-
-  const int n_ntiles = a.N_out / BN;
-  const int tile = bid / n_ntiles;
-  const int ntile = bid - tile * n_ntiles;
-  int e, r0, r1;
-  if (a.tile_map) {
-    if (tile >= a.n_tiles[0]) return;
-    const int4 tm = a.tile_map[tile];
-    e = tm.x; r0 = tm.y + (tile - tm.w) * BM; r1 = min(r0 + BM, tm.z);
-  } else {
-    e = 0; r0 = tile * BM; r1 = min(r0 + BM, a.M_dense);
-    if (r0 >= a.M_dense) return;
-  }
-  const int n0 = ntile * BN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int kg = 8 * (lane >> 4);
 
@@ -206,6 +187,46 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
     const size_t yi = (size_t)row * a.N_out + n0 + n;
     if (OUT_BF16) reinterpret_cast<bf16_t*>(a.Y)[yi] = f32_to_bf16(out);
     else reinterpret_cast<float*>(a.Y)[yi] = out;
+  }
+}
+
+// One launch may carry two problems of the same tile shape: blocks
+// [0, grid0) take a0 and the rest a1 (the shared expert beside the routed
+// experts, so that one grid covers the CUs).  WALK: a tile-map entry may
+// cover more rows than the kernel's row tile (map_bm > 16 * MT: the down
+// projection reading the gate/up GEMM's map), and the block walks them
+// 16 * MT rows at a time (a separate instance: the loop cost the other
+// launches a few percent).
+template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16, bool WALK>
+__global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, DirectArgs a1,
+                                                             int grid0) {
+  const bool second = (int)blockIdx.x >= grid0;
+  const DirectArgs a = second ? a1 : a0;
+  const int bid = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
+  constexpr int BM = 16 * MT;
+  constexpr int BN = 16 * NT;
+  constexpr int NACC = MT * NT * (SWIGLU ? 2 : 1);
+  __shared__ float red[NW > 1 ? NW * NACC * 4 * 65 : 1];
+
+  const int n_ntiles = a.N_out / BN;
+  const int tile = bid / n_ntiles;
+  const int ntile = bid - tile * n_ntiles;
+  int e, r0, r1;
+  if (a.tile_map) {
+    if (tile >= a.n_tiles[0]) return;
+    const int4 tm = a.tile_map[tile];
+    e = tm.x; r0 = tm.y + (tile - tm.w) * a.map_bm; r1 = min(r0 + a.map_bm, tm.z);
+  } else {
+    e = 0; r0 = tile * BM; r1 = min(r0 + BM, a.M_dense);
+    if (r0 >= a.M_dense) return;
+  }
+  if constexpr (WALK) {
+    for (int rs = r0; rs < r1; rs += BM) {
+      direct_rows<MT, NT, NW, SWIGLU, OUT_BF16>(a, e, rs, min(rs + BM, r1), ntile * BN, red);
+      if (NW > 1) __syncthreads();    // red is written again by the next rows
+    }
+  } else {
+    direct_rows<MT, NT, NW, SWIGLU, OUT_BF16>(a, e, r0, r1, ntile * BN, red);
   }
 }
 
@@ -801,7 +822,15 @@ static hipError_t launch_direct_t(const DirectArgs& a, int max_tiles, const Dire
                                   int b_tiles, hipStream_t st) {
   const int grid0 = max_tiles * (a.N_out / (16 * NT));
   const int grid1 = b ? b_tiles * (b->N_out / (16 * NT)) : 0;
-  ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16><<<grid0 + grid1, NW * 64, 0, st>>>(
+  if constexpr (!SWIGLU && MT == 1 && NT == 1) {
+    if (a.map_bm > 16 || (b && b->map_bm > 16)) {
+      ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16, true><<<grid0 + grid1, NW * 64, 0, st>>>(
+          a, b ? *b : a, grid0);
+      return hipGetLastError();
+    }
+  }
+  if (a.map_bm > 16 * MT || (b && b->map_bm > 16 * MT)) return hipErrorInvalidValue;
+  ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16, false><<<grid0 + grid1, NW * 64, 0, st>>>(
       a, b ? *b : a, grid0);
   return hipGetLastError();
 }
@@ -864,13 +893,15 @@ static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, cons
   return launch_direct_nw<4, DIRECT_NT64, SWIGLU, OUT_BF16>(a, nw, max_tiles, b, b_tiles, st);
 }
 
-static DirectArgs gate_up_direct(const FfnArgs& a) {
+static DirectArgs gate_up_direct(const FfnArgs& a, int BM) {
   return DirectArgs{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
-                    (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h};
+                    (const bf16_t*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, a.h,
+                    a.map_bm > 0 ? a.map_bm : BM};
 }
-static DirectArgs down_direct(const FfnArgs& a) {
+static DirectArgs down_direct(const FfnArgs& a, int BM) {
   return DirectArgs{(const bf16_t*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
-                    (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y};
+                    (const bf16_t*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, a.y,
+                    a.map_bm > 0 ? a.map_bm : BM};
 }
 static TileArgs gate_up_tile(const FfnArgs& a) {
   return TileArgs{(const bf16_t*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
@@ -883,14 +914,24 @@ static TileArgs down_tile(const FfnArgs& a) {
                   a.h_rows * a.I_loc * 2};
 }
 
-bool ffn_can_share_launch(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM) {
+bool ffn_can_share_gemm(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM, bool gate_up) {
   if (a.dt != 1 || b.dt != 1 || a.y_dt != b.y_dt || BM != b_BM) return false;
   if (a.max_tiles <= 0 || b.max_tiles <= 0) return false;
   if (is_tile_bm(BM))
-    return tile_shape(BM, true, a.I_loc) == tile_shape(BM, true, b.I_loc) &&
-           ffn_tile_ok(a.H, a.I_loc) && ffn_tile_ok(b.H, b.I_loc);
-  return direct_nw<true>(BM, a.H) == direct_nw<true>(BM, b.H) &&
-         direct_nw<false>(BM, a.I_loc) == direct_nw<false>(BM, b.I_loc);
+    return tile_shape(BM, gate_up, gate_up ? a.I_loc : a.H) ==
+               tile_shape(BM, gate_up, gate_up ? b.I_loc : b.H) &&
+           ffn_tile_ok(a.H, a.I_loc) && ffn_tile_ok(b.H, b.I_loc) && a.map_bm <= 0 &&
+           b.map_bm <= 0;
+  if (gate_up) return direct_nw<true>(BM, a.H) == direct_nw<true>(BM, b.H);
+  return direct_nw<false>(BM, a.I_loc) == direct_nw<false>(BM, b.I_loc);
+}
+
+int ffn_down_row_tile(int dt, int mean_rows, int H, int I_loc, int BM) {
+  // the one-row rule of ffn_row_tile (long contraction, fewer than 2 rows
+  // per expert) put the gate/up GEMM on LDS tiles: DeepSeek-V3 shape at
+  // T = 4, 8 and 16, down projection 4-9% faster in the direct kernel
+  if (dt == 1 && is_tile_bm(BM) && H >= 6144 && mean_rows < 2 && I_loc % 32 == 0) return 16;
+  return BM;
 }
 
 long long ffn_gate_up_blocks(const FfnArgs& a, int BM) {
@@ -909,24 +950,28 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st, const Ff
       return launch_tile<true, true>(gate_up_tile(a), BM, a.mean_rows, a.max_tiles, &t2,
                                      also->max_tiles, st);
     }
-    const DirectArgs g2 = gate_up_direct(*also);
-    return launch_direct<true, true>(gate_up_direct(a), BM, a.max_tiles, &g2, also->max_tiles, st);
+    const DirectArgs g2 = gate_up_direct(*also, BM);
+    return launch_direct<true, true>(gate_up_direct(a, BM), BM, a.max_tiles, &g2, also->max_tiles, st);
   }
   if (a.max_tiles <= 0) return hipSuccess;
   if (a.dt == 0) {
+    if (a.map_bm > 0 && a.map_bm != 16) return hipErrorInvalidValue;
     F32Args g1{(const float*)a.x, a.src_token, a.tile_map, a.n_tiles, a.M_dense,
                (const float*)a.w13, 2LL * a.I_loc * a.H, a.H, a.I_loc, a.I_loc, (float*)a.h};
     ffn_f32_kernel<true><<<a.max_tiles * (a.I_loc / 16), 256, 0, st>>>(g1);
     return hipGetLastError();
   }
-  if (is_tile_bm(BM))
+  if (is_tile_bm(BM)) {
+    if (a.map_bm > 0 && a.map_bm != BM) return hipErrorInvalidValue;
     return launch_tile<true, true>(gate_up_tile(a), BM, a.mean_rows, a.max_tiles, nullptr, 0, st);
-  return launch_direct<true, true>(gate_up_direct(a), BM, a.max_tiles, nullptr, 0, st);
+  }
+  return launch_direct<true, true>(gate_up_direct(a, BM), BM, a.max_tiles, nullptr, 0, st);
 }
 
 template <bool OUT_BF16>
 static hipError_t launch_down_bf16(const FfnArgs& a, int BM, const FfnArgs* also, hipStream_t st) {
   if (is_tile_bm(BM)) {
+    if (a.map_bm > 0 && a.map_bm != BM) return hipErrorInvalidValue;
     if (also) {
       const TileArgs t2 = down_tile(*also);
       return launch_tile<false, OUT_BF16>(down_tile(a), BM, a.mean_rows, a.max_tiles, &t2,
@@ -935,15 +980,16 @@ static hipError_t launch_down_bf16(const FfnArgs& a, int BM, const FfnArgs* also
     return launch_tile<false, OUT_BF16>(down_tile(a), BM, a.mean_rows, a.max_tiles, nullptr, 0, st);
   }
   if (also) {
-    const DirectArgs g2 = down_direct(*also);
-    return launch_direct<false, OUT_BF16>(down_direct(a), BM, a.max_tiles, &g2, also->max_tiles, st);
+    const DirectArgs g2 = down_direct(*also, BM);
+    return launch_direct<false, OUT_BF16>(down_direct(a, BM), BM, a.max_tiles, &g2, also->max_tiles, st);
   }
-  return launch_direct<false, OUT_BF16>(down_direct(a), BM, a.max_tiles, nullptr, 0, st);
+  return launch_direct<false, OUT_BF16>(down_direct(a, BM), BM, a.max_tiles, nullptr, 0, st);
 }
 
 hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also) {
   if (!also && a.max_tiles <= 0) return hipSuccess;
   if (a.dt == 0) {
+    if (a.map_bm > 0 && a.map_bm != 16) return hipErrorInvalidValue;
     F32Args g2{(const float*)a.h, nullptr, a.tile_map, a.n_tiles, a.M_dense,
                (const float*)a.w2, (long long)a.H * a.I_loc, a.I_loc, a.H, 0, (float*)a.y};
     ffn_f32_kernel<false><<<a.max_tiles * (a.H / 16), 256, 0, st>>>(g2);

@@ -101,21 +101,30 @@ struct FfnArgs {
   int dt, y_dt;
   long long x_rows;         // rows of x (0: not known)
   long long h_rows;         // rows of h
+  int map_bm;               // rows per tile-map entry when it differs from the
+                            // launch's row tile (direct kernel only); 0: the same
 };
 // Row tile of the expert GEMMs: 16/32/64 (direct kernel) or 128/256 (LDS-
 // tiled kernel), from the expected rows per expert and the number of experts
 // the rows spread over.
 int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts);
 // `also` (optional): a second problem run in the same launch, for which
-// ffn_can_share_launch(a, BM, *also, BM) holds -- the shared expert beside
+// ffn_can_share_gemm(a, BM, *also, BM, ...) holds -- the shared expert beside
 // the routed experts at a few tokens, where its own launches would leave most
 // CUs idle.
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st,
                               const FfnArgs* also = nullptr);
 hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnArgs* also = nullptr);
-// Both problems bf16 with one row tile and the same kernel configuration in
-// each GEMM (tile shape, or waves per block of the direct kernel).
-bool ffn_can_share_launch(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM);
+// Row tile of the down projection after a gate/up GEMM with row tile BM
+// over the same tile map: BM, except at about one row per expert with a
+// long contraction, where the gate/up GEMM takes LDS tiles and the down
+// projection's short one streams faster in the direct kernel (16-row tiles
+// walking the gate/up GEMM's map: FfnArgs::map_bm = BM).
+int ffn_down_row_tile(int dt, int mean_rows, int H, int I_loc, int BM);
+// Whether b can ride in a's launch of one GEMM (gate_up: the gate/up GEMM,
+// else the down projection): both bf16 with one row tile and the same kernel
+// configuration (tile shape, or waves per block of the direct kernel).
+bool ffn_can_share_gemm(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM, bool gate_up);
 // Blocks of a's gate/up launch with row tile BM (a.max_tiles row tiles).
 long long ffn_gate_up_blocks(const FfnArgs& a, int BM);
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st);
