@@ -1,0 +1,74 @@
+"""The expert-GEMM kernel choices at the workload shapes, checked on the host:
+a small program compiled against the library's ffn.hip prints the row tile
+of each GEMM (16/32/64: direct kernel, 128/256: LDS-tiled) and whether the
+shared expert's GEMMs ride in the routed launches.  The expected values are
+the measured choices the kernel sources document."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixture_experts_layer_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def tile_choice(tmp_path_factory):
+    from mixture_experts_layer_amd import build as B
+    try:
+        hipcc = B.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path_factory.mktemp("host") / "tile_choice")
+    cmd = [hipcc, "-O1", "-std=c++17", f"--offload-arch={B.ARCH}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(ROOT, "tests", "host", "tile_choice.cpp"), os.path.join(CSRC, "ffn.hip"),
+           "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+
+    def run(H, I, Is, E, E_loc, k, T):
+        out = subprocess.run([exe] + [str(v) for v in (H, I, Is, E, E_loc, k, T)],
+                             capture_output=True, text=True, check=True).stdout.split()
+        return dict(zip(out[0::2], out[1::2]))
+    return run
+
+
+# (shape, T) -> expected choices
+CASES = [
+    # Qwen3 EP view: direct at a few rows, 128-row LDS tiles from 64 rows per
+    # expert, 256-row tiles at prefill
+    (("qwen3_ep", 4096, 1536, 0, 128, 128, 8, 16), dict(gate_up="16", down="16")),
+    (("qwen3_ep", 4096, 1536, 0, 128, 128, 8, 1024), dict(gate_up="128", down="128")),
+    (("qwen3_ep", 4096, 1536, 0, 128, 128, 8, 8192), dict(gate_up="256", down="256")),
+    # Qwen3 TP share (I/P = 192): direct kernel at T <= 64
+    (("qwen3_tp", 4096, 192, 0, 128, 128, 8, 64), dict(gate_up="16", down="16")),
+    # Mixtral: direct at T = 16, 256-row tiles at 4096
+    (("mixtral", 4096, 14336, 0, 8, 8, 2, 16), dict(gate_up="16", down="16")),
+    (("mixtral", 4096, 14336, 0, 8, 8, 2, 4096), dict(gate_up="256", down="256")),
+    # DeepSeek-V3: direct at T = 1 (shared expert in both routed launches);
+    # at T = 8 and 16 the gate/up GEMM on LDS tiles, the down projection
+    # direct walking its map, the shared expert riding in both (switched to
+    # the routed tile: its gate/up at T = 8, its down projection at T = 16,
+    # where its own tile already is the routed gate/up one); at T = 64 all
+    # on LDS tiles; at 4096 the shared expert in launches of its own
+    (("deepseek", 7168, 2048, 2048, 256, 256, 8, 1),
+     dict(gate_up="16", down="16", shared_gate_up="shared", shared_down="shared")),
+    (("deepseek", 7168, 2048, 2048, 256, 256, 8, 8),
+     dict(gate_up="128", down="16", shared_gate_up="shared_switched", shared_down="shared")),
+    (("deepseek", 7168, 2048, 2048, 256, 256, 8, 16),
+     dict(gate_up="128", down="16", shared_gate_up="shared", shared_down="shared_switched")),
+    (("deepseek", 7168, 2048, 2048, 256, 256, 8, 64),
+     dict(gate_up="128", down="128", shared_gate_up="shared", shared_down="shared")),
+    (("deepseek", 7168, 2048, 2048, 256, 256, 8, 4096),
+     dict(gate_up="128", down="128", shared_gate_up="own", shared_down="own")),
+]
+
+
+@pytest.mark.parametrize("case,want", CASES, ids=[f"{c[0]}-T{c[-1]}" for c, _ in CASES])
+def test_tile_choice(tile_choice, case, want):
+    got = tile_choice(*case[1:])
+    for key, value in want.items():
+        assert got[key] == value, (key, got)
