@@ -7,9 +7,10 @@ A step is one pass of the whole layer (router, gating, histogram, prefix sum,
 permutation, grouped SwiGLU GEMMs, shared expert if any, combine) over one
 batch of T seeded synthetic tokens, through the fused C entry point
 moe_layer.  Inputs are resident in HBM before the timed region.  Steps
-rotate over `copies` byte-identical copies of the layer's weights at
-distinct addresses, so the 256 MB Infinity Cache cannot serve the weights
-of one step from the previous one.
+rotate over byte-identical copies of the layer's weights at distinct
+addresses, as many as make the bytes the rotation touches (the router and
+the experts the batch actually routes to, per copy) at least 1 GB, four
+times the 256 MB Infinity Cache, so no step finds its weights in that cache.
 
 Printed: one JSON line with tokens/s (value), the roofline of the dominant
 kernel (timed live with HIP events that moe_layer records on its stream at
@@ -54,7 +55,8 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "staged", "decode"],
                     help="layer entry point: moe_layer (auto), moe_layer_staged, moe_layer_decode")
     ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
-    ap.add_argument("--sweep-workloads", default="qwen3_ep_all128,qwen3_tp8_rank0",
+    ap.add_argument("--sweep-workloads",
+                    default="qwen3_ep_all128,qwen3_tp8_rank0,mixtral_8x7b,deepseek_v3",
                     help="workloads whose token counts are swept (comma list)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dispatch", action="store_true",
@@ -91,6 +93,37 @@ def layer_work(cfg, T, counts, I_loc, elt):
                 g1_bytes=g1_bytes)
 
 
+ROTATION_BYTES = 1.0e9     # bytes the weight rotation must touch (>= 4x the 256 MB MALL)
+MAX_COPIES = 64
+
+
+def copies_needed(cfg, work, T, elt):
+    """Weight copies for a batch: enough that copies x (bytes one step
+    touches: router + routed experts + shared expert) >= ROTATION_BYTES."""
+    touched = work["b_alg"] - 2 * elt * T * cfg.H
+    return max(2, min(MAX_COPIES, math.ceil(ROTATION_BYTES / max(touched, 1))))
+
+
+def routing_shape(counts, T, k, E):
+    """The expert-GEMM shape distribution of a batch: rows per expert (m),
+    their percentiles and maximum, the imbalance max / mean over all experts,
+    and a histogram of m over power-of-two bins."""
+    import numpy as np
+    c = np.asarray(counts, dtype=np.int64)
+    rows = int(c.sum())
+    mean = rows / max(len(c), 1)
+    hist = {}
+    for m in c.tolist():
+        key = "0" if m == 0 else f"{1 << (m.bit_length() - 1)}-{(1 << m.bit_length()) - 1}"
+        hist[key] = hist.get(key, 0) + 1
+    order = sorted(hist, key=lambda s: int(s.split("-")[0]))
+    return dict(rows=rows, touched_experts=int((c > 0).sum()),
+                imbalance_ratio=round(float(c.max() / mean), 3) if rows else 0.0,
+                load_p50=float(np.percentile(c, 50)), load_p95=float(np.percentile(c, 95)),
+                load_p99=float(np.percentile(c, 99)), load_max=int(c.max()),
+                m_hist={key: hist[key] for key in order})
+
+
 def roofs(cfg):
     if cfg.dtype == "f32":
         return HBM_PEAK_GBS, MFMA_F32_PEAK_TFLOPS
@@ -105,6 +138,10 @@ LAYER_FN = {"auto": "moe_layer", "staged": "moe_layer_staged", "decode": "moe_la
 
 
 class Bench:
+    """One workload's layer on the GPU: weights (with copies for the
+    rotation), workspace, input batch.  `copies` fixes the rotation length;
+    None sizes it per batch from the touched bytes (copies_needed)."""
+
     def __init__(self, name, T_max, copies, path="auto"):
         import torch
         import mixture_experts_layer_amd as M
@@ -119,23 +156,38 @@ class Bench:
         self.L = L
         self.elt = 4 if cfg.dtype == "f32" else 2
         self.I_loc = w13.shape[1] // 2
-        per_copy = (w13.numel() + w2.numel() + L.w_r.numel()) * self.elt
-        if copies is None:
-            copies = max(2, min(16, math.ceil(2.0e9 / per_copy)))
-        self.copies = copies
+        self.fixed_copies = copies
         self.layers = []
-        for c in range(copies):
-            a, b, r = (w13, w2, L.w_r) if c == 0 else (w13.clone(), w2.clone(), L.w_r.clone())
-            d = M.layer_desc(cfg.H, cfg.E, cfg.k, self.I_loc, cfg.mode, M.dtype_code(L.x), r, a, b,
-                             I_shared=cfg.I_shared, w13_shared=L.w13_shared,
-                             w2_shared=L.w2_shared, logit_bias=L.logit_bias, sel_bias=L.sel_bias)
-            self.layers.append((d, a, b, r))
+        self._add_copy(w13, w2, L.w_r, L.w13_shared, L.w2_shared)
+        self.copies = 1
         self.T_max = T_max
         self.ws = M.layer_workspace(self.layers[0][0], T_max)
         self.ws_bytes = self.ws.numel()
         self.y_full = torch.empty((T_max, cfg.H), dtype=L.x.dtype, device="cuda")
         self.set_T(T_max)
         torch.cuda.synchronize()
+
+    def _add_copy(self, w13, w2, w_r, w13_s, w2_s):
+        cfg, M, L = self.cfg, self.M, self.L
+        d = self.M.layer_desc(cfg.H, cfg.E, cfg.k, self.I_loc, cfg.mode, M.dtype_code(L.x), w_r,
+                              w13, w2, I_shared=cfg.I_shared, w13_shared=w13_s, w2_shared=w2_s,
+                              logit_bias=L.logit_bias, sel_bias=L.sel_bias)
+        self.layers.append((d, w13, w2, w_r, w13_s, w2_s))
+
+    def set_copies(self, n):
+        """Rotate over n copies of every weight the layer reads (router,
+        experts, shared expert), cloning more if needed."""
+        _, w13, w2, w_r, w13_s, w2_s = self.layers[0]
+        clone = lambda t: None if t is None else t.clone()
+        while len(self.layers) < n:
+            self._add_copy(clone(w13), clone(w2), clone(w_r), clone(w13_s), clone(w2_s))
+        self.copies = n
+
+    def size_rotation(self, work):
+        """Set the rotation for the current batch from its touched bytes."""
+        n = self.fixed_copies or copies_needed(self.cfg, work, self.T, self.elt)
+        self.set_copies(n)
+        return n
 
     def set_T(self, T):
         self.T = T
@@ -557,6 +609,7 @@ def main():
     bench = Bench(args.workload, T, args.copies, args.path)
     counts = bench.counts()
     work = layer_work(cfg, T, counts, bench.I_loc, bench.elt)
+    bench.size_rotation(work)
     ms, split = bench.timed_eager(args.steps, args.warmup)
     path = bench.path_of(T)
     l_bound, t_roof_ms, l_frac = layer_roof_frac(cfg, work, ms)
@@ -596,20 +649,26 @@ def main():
                 Bench(name, max(Ts), None, args.path)
             for T2 in Ts:
                 b2.set_T(T2)
-                w2k = layer_work(c2, T2, b2.counts(), b2.I_loc, b2.elt)
+                c2counts = b2.counts()
+                w2k = layer_work(c2, T2, c2counts, b2.I_loc, b2.elt)
+                n_copies = b2.size_rotation(w2k)
                 ms2 = b2.timed_graph(max(args.steps, 20), args.warmup)
                 bd, tr, fr = layer_roof_frac(c2, w2k, ms2)
                 sweep.append(dict(workload=WORKLOAD_NAMES[name], T=T2, path=b2.path_of(T2),
                                   ms=round(ms2, 4),
                                   tokens_per_s=round(T2 / (ms2 * 1e-3), 1), bound=bd,
                                   roofline_ms=round(tr, 4), frac=round(fr, 4),
-                                  touched_experts=w2k["touched"]))
+                                  weight_copies=n_copies,
+                                  rotation_touched_bytes=int(
+                                      n_copies * (w2k["b_alg"] - 2 * b2.elt * T2 * c2.H)),
+                                  routing=routing_shape(c2counts, T2, c2.k, c2.E)))
                 print(f"# sweep {name} T={T2}: {ms2:.4f} ms, {fr:.3f} of roofline ({bd})",
                       file=sys.stderr, flush=True)
             if b2 is not bench:
                 del b2
                 torch.cuda.empty_cache()
             bench.set_T(T)
+            bench.size_rotation(work)
 
     dispatch = None
     if not args.no_dispatch:
@@ -623,7 +682,6 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, args.cpu_sample, args.cpu_seconds)
 
-    imb = max(counts) / (sum(counts) / len(counts)) if sum(counts) else 0.0
     line = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -640,6 +698,8 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.workload], "T": T, "H": cfg.H,
                    "I_loc": bench.I_loc, "E": cfg.E, "k": cfg.k, "gating_mode": cfg.mode,
                    "I_shared": cfg.I_shared, "weight_copies": bench.copies,
+                   "rotation_touched_bytes": int(bench.copies * (work["b_alg"] - 2 * bench.elt * T
+                                                                 * cfg.H)),
                    "parallelism": "single-gpu share", "entry_point": LAYER_FN[args.path],
                 "path": path},
         "roofline": roof,
@@ -648,8 +708,7 @@ def main():
                            "f_alg_flops": work["f_alg"]},
         "ms_per_step_graph": round(ms_graph, 4),
         "stage_ms": {k2: round(v, 4) for k2, v in split.items()},
-        "routing": {"rows": work["rows"], "touched_experts": work["touched"],
-                    "imbalance_ratio": round(imb, 3)},
+        "routing": routing_shape(counts, T, cfg.k, cfg.E),
         "sweep": sweep,
         "capacity": capacity,
         "dispatch": dispatch,

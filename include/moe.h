@@ -77,7 +77,9 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 2,   /* valid but outside the shape / dtype / mode limits above */
   MOE_ERR_WORKSPACE = 3,     /* workspace pointer null or smaller than the size query */
   MOE_ERR_HIP = 4,           /* a HIP launch returned an error */
-  MOE_ERR_METADATA = 5       /* the metadata check of MOE_VALIDATE=1 failed (below) */
+  MOE_ERR_METADATA = 5,      /* the metadata check of MOE_VALIDATE=1 failed (below) */
+  MOE_ERR_WAIT = 6           /* a decode-path wait for another workgroup ran out; the call's
+                                outputs are undefined (moe_layer_status, MOE_VALIDATE=1) */
 } moe_status;
 
 typedef enum {
@@ -98,6 +100,11 @@ int moe_abi_version(void);
 
 /* Static description of a status code; never NULL. */
 const char* moe_status_str(int status);
+
+/* SHA-256 (hex) of the sources and compile flags the library was built from,
+ * or "unstamped".  The Python binding refuses a library whose stamp differs
+ * from the sources beside it, so a stale binary is never run. */
+const char* moe_source_sha256(void);
 
 /*
  * moe_route -- router scores and top-k gating.
@@ -371,9 +378,19 @@ typedef struct {
  * metadata check.  Bytes 4..7 hold an int32 error word that the decode path
  * sets (bit 0: the router wait, bit 1: an expert wait) if a wait for another
  * workgroup exceeds its bound -- a grid that could not be resident at once;
- * that call's outputs are then undefined.  It stays set until the caller
- * clears it. */
+ * that call's outputs are then undefined.  It stays set until it is read by
+ * moe_layer_status (below) or by a call under MOE_VALIDATE=1, which return
+ * MOE_ERR_WAIT and clear it.  A caller that runs the decode path without
+ * MOE_VALIDATE=1 polls moe_layer_status to learn of such a failure. */
 size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max);
+
+/* The decode path's wait error word of a layer workspace (bytes 4..7 above),
+ * read after the work already enqueued on `stream`: MOE_OK if it is zero;
+ * otherwise it is cleared and MOE_ERR_WAIT is returned (some decode-path call
+ * on this workspace since the last read had undefined outputs).  Waits for the
+ * stream, so it cannot be captured in a graph.  MOE_ERR_INVALID_ARG for a null
+ * or misaligned ws or ws_bytes below the synchronisation block. */
+int moe_layer_status(void* ws, size_t ws_bytes, void* stream);
 
 /* The layer share, choosing the single-launch decode path (moe_layer_decode)
  * for shapes it supports while the expert weights the call can touch

@@ -23,7 +23,7 @@ __all__ = [
     "moe_combine", "moe_pack_by_rank", "moe_pack_workspace_size", "moe_unpack_sum",
     "moe_reshard_ep_to_tp_pack", "moe_reshard_tp_to_ep_interleave", "moe_layer",
     "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
-    "moe_layer_workspace_size",
+    "moe_layer_workspace_size", "moe_layer_status", "moe_source_sha256", "MOE_ERR_WAIT",
     "layer_workspace", "layer_desc", "dtype_code", "LAYER_SYNC_BYTES",
     "MoELayerDesc", "MoEDebugOut",
 ]
@@ -59,6 +59,13 @@ def moe_abi_version() -> int:
 
 def moe_status_str(status: int) -> str:
     return lib.moe_status_str(status).decode()
+
+
+def moe_source_sha256() -> str:
+    return lib.moe_source_sha256().decode()
+
+
+MOE_ERR_WAIT = 6
 
 
 def dtype_code(t) -> int:
@@ -222,6 +229,12 @@ def moe_layer_decode(desc: MoELayerDesc, T, x, y, ws, ws_bytes, dbg: MoEDebugOut
     _check("moe_layer_decode",
            lib.moe_layer_decode(ctypes.byref(desc), T, _p(x), _p(y), _p(ws), ws_bytes,
                                 None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+
+
+def moe_layer_status(ws, ws_bytes, stream=None):
+    """Read (and clear) the decode path's wait error word of a layer
+    workspace; raises MoEError(MOE_ERR_WAIT) if it was set."""
+    _check("moe_layer_status", lib.moe_layer_status(_p(ws), ws_bytes, _stream(stream)))
 
 
 def layer_workspace(desc: MoELayerDesc, T_max: int, device="cuda", capacity=None, padded=0):

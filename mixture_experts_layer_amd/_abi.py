@@ -34,6 +34,7 @@ class MoEDebugOut(ctypes.Structure):
 # name -> (restype, argtypes)
 _SIGS = {
     "moe_abi_version": (c_int, []),
+    "moe_source_sha256": (c_char_p, []),
     "moe_status_str": (c_char_p, [c_int]),
     "moe_route": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -64,6 +65,7 @@ _SIGS = {
     "moe_layer": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p, c_void_p,
                           c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
     "moe_layer_path": (c_int, [ctypes.POINTER(MoELayerDesc), c_int]),
+    "moe_layer_status": (c_int, [c_void_p, c_size_t, c_void_p]),
     "moe_layer_staged": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p,
                                  c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
     "moe_layer_capacity": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_int, c_int, c_void_p,
@@ -84,13 +86,29 @@ def lib_path():
 
 
 def load_library():
+    """Load the built library.  Raises ImportError if it is missing, or if it
+    was built from other sources than those in the tree (a stale binary);
+    MOE_MI355X_LIB names another library explicitly and skips that check."""
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(f"HIP library not built: {path} is missing "
                           "(run `python -m mixture_experts_layer_amd.build`)")
+    # torch first: its HIP runtime (soname libamdhip64.so.7) is then the one
+    # the library binds to.  Loaded the other way round, torch would load a
+    # second runtime beside the library's, and the stream handles the binding
+    # takes from torch would be foreign to the runtime that launches the
+    # kernels.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if "MOE_MI355X_LIB" not in os.environ:
+        from .build import source_sha256
+        built, want = lib.moe_source_sha256().decode(), source_sha256()
+        if built != want:
+            raise ImportError(f"stale HIP library {path}: built from sources {built[:12]}, the "
+                              f"tree holds {want[:12]} (run `python -m "
+                              "mixture_experts_layer_amd.build`)")
     return lib

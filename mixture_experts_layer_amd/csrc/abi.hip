@@ -205,6 +205,20 @@ int check_meta(const int32_t* ids, int npair, int E, int e_begin, int e_end, con
   return word ? MOE_ERR_METADATA : MOE_OK;
 }
 
+// The decode path's error word (int 1 of the synchronisation block): read it
+// after the stream's work, clear it if set, and return MOE_ERR_WAIT if it was.
+// Synchronises the stream.
+int take_wait_word(int* sync, hipStream_t s) {
+  int32_t word = 0;
+  MOE_TRY(hipMemcpyAsync(&word, sync + DECODE_ERR_INT, sizeof(word), hipMemcpyDeviceToHost, s));
+  MOE_TRY(hipStreamSynchronize(s));
+  if (word == 0) return MOE_OK;
+  static const int32_t zero = 0;
+  MOE_TRY(hipMemcpyAsync(sync + DECODE_ERR_INT, &zero, sizeof(zero), hipMemcpyHostToDevice, s));
+  MOE_TRY(hipStreamSynchronize(s));
+  return MOE_ERR_WAIT;
+}
+
 int run_decode(const moe_layer_desc* d, int T, const void* x, void* y, const LayerWs& l,
                moe_debug_out* dbg, hipStream_t s) {
   auto mark = [&](int i) -> hipError_t {
@@ -236,9 +250,13 @@ int run_decode(const moe_layer_desc* d, int T, const void* x, void* y, const Lay
   MOE_TRY(mark(0));
   MOE_TRY(launch_decode(a, s));
   for (int i = 1; i < MOE_STAGE_EVENTS; ++i) MOE_TRY(mark(i));
-  if (check)
-    return check_meta(a.ids_out, T * d->k, d->E, d->e_begin, d->e_end, a.counts_out,
-                      a.offsets_out, INT_MAX, 0, nullptr, l.sync + LAYER_VALIDATE_INT, s);
+  if (check) {
+    const int st = check_meta(a.ids_out, T * d->k, d->E, d->e_begin, d->e_end, a.counts_out,
+                              a.offsets_out, INT_MAX, 0, nullptr, l.sync + LAYER_VALIDATE_INT, s);
+    // a wait that ran out is the cause of any other inconsistency: report it first
+    const int wst = take_wait_word(l.sync, s);
+    return wst != MOE_OK ? wst : st;
+  }
   return MOE_OK;
 }
 
@@ -249,6 +267,11 @@ extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+#ifndef MOE_SOURCE_SHA256
+#define MOE_SOURCE_SHA256 "unstamped"
+#endif
+const char* moe_source_sha256(void) { return MOE_SOURCE_SHA256; }
+
 const char* moe_status_str(int s) {
   switch (s) {
     case MOE_OK: return "ok";
@@ -257,6 +280,7 @@ const char* moe_status_str(int s) {
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch error";
     case MOE_ERR_METADATA: return "routing metadata check failed";
+    case MOE_ERR_WAIT: return "a decode-path wait for another workgroup ran out (outputs undefined)";
     default: return "unknown status";
   }
 }
@@ -553,6 +577,11 @@ int moe_reshard_tp_to_ep_interleave(const void* w13_recv, const void* w2_recv, i
   return reshard_call(false, w13_recv, w2_recv, E_rank, I, H, P, dt, w13_ep, w2_ep, stream);
 }
 
+int moe_layer_status(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned16(ws) || ws_bytes < (size_t)DECODE_SYNC_BYTES) return MOE_ERR_INVALID_ARG;
+  return take_wait_word(static_cast<int*>(ws), static_cast<hipStream_t>(stream));
+}
+
 size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max) {
   if (check_desc(d) != MOE_OK || T_max < 0) return 0;
   return layer_layout(d, T_max, nullptr, nullptr);
@@ -643,43 +672,31 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   f.H = d->H; f.I_loc = d->I_loc; f.w13 = d->w13; f.w2 = d->w2;
   f.h = l.h; f.y = l.y_perm; f.dt = d->dt; f.y_dt = d->dt;
   f.x_rows = T; f.h_rows = l.max_rows;
+  // the launches: routed row tiles, and whether the shared expert's GEMMs
+  // ride in the routed launches (a8: the shared expert over every token)
+  const GemmPlan plan = plan_layer_gemms(d->dt, T, d->k, d->E, E_loc, d->H, d->I_loc,
+                                         d->I_shared);
+  if (plan.BM != l.BM) return MOE_ERR_HIP;   // the workspace's tile map was sized for l.BM
   // the down projection may walk the gate/up GEMM's tile map with a smaller
   // row tile of its own
-  const int BM_dn = ffn_down_row_tile(d->dt, mean_rows(T, d->k, d->E), d->H, d->I_loc, l.BM);
+  const int BM_dn = plan.BM_dn;
   FfnArgs fd = f;
   if (BM_dn != l.BM) fd.map_bm = l.BM;
-  // a8: shared expert over every token.  For each GEMM: where its own row
-  // tile would give it fewer blocks than there are CUs (up to a few hundred
-  // tokens), it takes the routed GEMM's row tile instead and rides in its
-  // launch; else it has launches of its own.
   FfnArgs g{};
-  int BMs = 0, BMs_dn = 0;
-  bool share_up = false, share_dn = false;
+  const int BMs = plan.BMs;
+  const bool share_up = plan.up != SHARE_NONE, share_dn = plan.dn != SHARE_NONE;
   FfnArgs g_up{}, g_dn{};
+  int BMs_dn = plan.BMs_dn;
   if (d->I_shared > 0) {
-    BMs = ffn_row_tile(d->dt, T, d->H, d->I_shared, 1);
     g.x = x; g.src_token = nullptr; g.tile_map = nullptr; g.n_tiles = nullptr;
     g.M_dense = T; g.max_tiles = cdiv(T, BMs); g.mean_rows = T;
     g.H = d->H; g.I_loc = d->I_shared; g.w13 = d->w13_shared; g.w2 = d->w2_shared;
     g.h = l.h_s; g.y = l.y_s; g.dt = d->dt; g.y_dt = d->dt;
     g.x_rows = T; g.h_rows = T;
-    const bool thin = ffn_gate_up_blocks(g, BMs) < 256;   // the 256 CUs
-    auto pick = [&](const FfnArgs& r, int BMr, bool gate_up, FfnArgs& out, int& BMo) {
-      out = g;
-      BMo = BMs;
-      if (ffn_can_share_gemm(r, BMr, g, BMs, gate_up)) return true;
-      if (!thin) return false;
-      FfnArgs g2 = g;
-      g2.max_tiles = cdiv(T, BMr);
-      if (!ffn_can_share_gemm(r, BMr, g2, BMr, gate_up)) return false;
-      out = g2;
-      BMo = BMr;
-      return true;
-    };
-    int BMs_up = 0;
-    share_up = pick(f, l.BM, true, g_up, BMs_up);
-    share_dn = pick(fd, BM_dn, false, g_dn, BMs_dn);
-    if (!share_dn) { g_dn = g; BMs_dn = BMs; }
+    g_up = g;
+    g_up.max_tiles = cdiv(T, plan.BMs_up);
+    g_dn = g;
+    g_dn.max_tiles = cdiv(T, BMs_dn);
   }
   MOE_TRY(launch_ffn_gate_up(f, l.BM, s, share_up ? &g_up : nullptr));
   MOE_TRY(mark(2));

@@ -106,7 +106,7 @@ __device__ __forceinline__ uint4 load_coherent16(const bf16_t* p) {
 }
 
 __device__ __forceinline__ void set_error(int* sync, int bit) {
-  __hip_atomic_fetch_or(sync + 1, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_or(sync + DECODE_ERR_INT, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Poll a go flag until it holds `want` or, if `alt_ok`, want + 1; false

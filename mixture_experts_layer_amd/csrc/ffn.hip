@@ -999,6 +999,39 @@ hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnAr
   return launch_down_bf16<true>(a, BM, also, st);
 }
 
+GemmPlan plan_layer_gemms(int dt, int T, int k, int E, int E_loc, int H, int I_loc,
+                          int I_shared) {
+  auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
+  GemmPlan p{};
+  const int mean = cdiv(T * k, E);
+  p.BM = ffn_row_tile(dt, mean, H, I_loc, T * k < E_loc ? T * k : E_loc);
+  p.BM_dn = ffn_down_row_tile(dt, mean, H, I_loc, p.BM);
+  if (I_shared <= 0 || T <= 0) return p;
+  // the routed problems as the launches see them (any tile count > 0)
+  FfnArgs f{};
+  f.dt = dt; f.y_dt = dt; f.H = H; f.I_loc = I_loc; f.max_tiles = 1;
+  FfnArgs fd = f;
+  if (p.BM_dn != p.BM) fd.map_bm = p.BM;
+  FfnArgs g{};
+  g.dt = dt; g.y_dt = dt; g.H = H; g.I_loc = I_shared; g.M_dense = T;
+  p.BMs = ffn_row_tile(dt, T, H, I_shared, 1);
+  g.max_tiles = cdiv(T, p.BMs);
+  const bool thin = ffn_gate_up_blocks(g, p.BMs) < 256;   // fewer blocks than CUs
+  auto pick = [&](const FfnArgs& r, int BMr, bool gate_up, int& BMo) {
+    BMo = p.BMs;
+    if (ffn_can_share_gemm(r, BMr, g, p.BMs, gate_up)) return (int)SHARE_OWN_TILE;
+    if (!thin) return (int)SHARE_NONE;
+    FfnArgs g2 = g;
+    g2.max_tiles = cdiv(T, BMr);
+    if (!ffn_can_share_gemm(r, BMr, g2, BMr, gate_up)) return (int)SHARE_NONE;
+    BMo = BMr;
+    return (int)SHARE_ROUTED_TILE;
+  };
+  p.up = pick(f, p.BM, true, p.BMs_up);
+  p.dn = pick(fd, p.BM_dn, false, p.BMs_dn);
+  return p;
+}
+
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st) {
   hipError_t err = launch_ffn_gate_up(a, BM, st);
   if (err != hipSuccess) return err;

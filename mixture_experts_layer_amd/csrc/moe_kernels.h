@@ -129,6 +129,23 @@ bool ffn_can_share_gemm(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM, bo
 long long ffn_gate_up_blocks(const FfnArgs& a, int BM);
 hipError_t launch_grouped_ffn(const FfnArgs& a, int BM, hipStream_t st);
 
+// The expert-GEMM launches of one staged layer call: the routed row tiles and
+// how the shared expert's two GEMMs run.  A shared GEMM either rides in the
+// routed launch (SHARE_OWN_TILE: its own row tile is the routed one's
+// configuration; SHARE_ROUTED_TILE: its own tile would give it fewer blocks
+// than there are CUs, so it takes the routed row tile) or has a launch of its
+// own (SHARE_NONE).
+enum SharedLaunch { SHARE_NONE = 0, SHARE_OWN_TILE = 1, SHARE_ROUTED_TILE = 2 };
+struct GemmPlan {
+  int BM;         // routed gate/up row tile
+  int BM_dn;      // routed down row tile (walks the gate/up tile map when != BM)
+  int BMs;        // the shared expert's own row tile (0: no shared expert)
+  int up, dn;     // SharedLaunch of the shared gate/up and down GEMMs
+  int BMs_up;     // row tile the shared gate/up GEMM runs with
+  int BMs_dn;     // row tile the shared down GEMM runs with
+};
+GemmPlan plan_layer_gemms(int dt, int T, int k, int E, int E_loc, int H, int I_loc, int I_shared);
+
 hipError_t launch_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row,
                           const float* w, int T, int k, int H, const void* y_shared, void* y,
                           int dt, hipStream_t st);
@@ -168,6 +185,7 @@ constexpr int DECODE_MAX_BLOCKS = 1024;  // grid bound (workgroups resident at o
 // sync block at the start of the workspace: a 4 KiB header, then one
 // 128-byte go-flag line per workgroup
 constexpr int DECODE_SYNC_BYTES = 4096 + DECODE_MAX_BLOCKS * 128;
+constexpr int DECODE_ERR_INT = 1;        // int index of the wait error word in the sync block
 
 struct DecodeLaunch {
   const void* x;

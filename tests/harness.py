@@ -130,6 +130,7 @@ class GpuLayer:
             dbg = M.debug_out(out["logits"], out["ids"], out["w"], out["counts"], out["offsets"],
                               out["src_token"], out["dst_row"])
         getattr(M, LAYER_FNS[path])(self.desc, T, x, y, self.ws, self.ws_bytes, dbg)
+        self.last_path = path if path != "auto" else M.moe_layer_path(self.desc, T)
         return out
 
     def sync_error(self):
@@ -139,9 +140,14 @@ class GpuLayer:
 
 def check_layer(gl: GpuLayer, out, T, sample=None, check_rows=True):
     """Apply the parity protocol to one moe_layer run.  `sample`: token indices
-    whose outputs are checked (None = all); routing metadata is always checked
-    for the whole batch.  Returns a dict of measured errors."""
+    whose outputs are checked (None = all), or a function of the run's outputs
+    returning them (called once the routing metadata has matched); routing
+    metadata is always checked for the whole batch.  Returns a dict of
+    measured errors."""
     torch.cuda.synchronize()
+    if getattr(gl, "last_path", None) == "decode":
+        # no wait of the single-launch path ran out (raises MoEError otherwise)
+        M.moe_layer_status(gl.ws, gl.ws_bytes)
     L, cfg = gl.L, gl.L.cfg
     x = to_np(L.x[:T])
     logits_gpu = to_np(out["logits"])
@@ -170,7 +176,10 @@ def check_layer(gl: GpuLayer, out, T, sample=None, check_rows=True):
     if not check_rows:
         return res
     # 3. outputs
+    if callable(sample):
+        sample = sample(out)
     idx = np.arange(T) if sample is None else np.asarray(sample)
+    res["tokens_checked"] = int(len(idx))
     share = OracleShare(L.w13, L.w2, gl.e_begin, gl.tp_P, gl.tp_rank)
     w13, w2 = share.view(0), share.view(1)
     kw = {}
@@ -184,3 +193,27 @@ def check_layer(gl: GpuLayer, out, T, sample=None, check_rows=True):
     tol = TOL[cfg.dtype]
     assert res["y_rel"] <= tol, f"layer output rel err {res['y_rel']} > {tol}"
     return res
+
+
+def boundary_sample(T, n_random, seed, tiles=(128, 256)):
+    """A function of a run's outputs giving the tokens whose outputs a
+    full-size case checks: every token whose copy sits on an expert
+    segment's first or last row, on the first row of its last row tile or on
+    the last row before it (for each GEMM row tile in `tiles`: the ragged
+    tails and the tile boundaries), plus `n_random` seeded tokens.  Exact
+    for a dropless layer: a token's output depends on that token alone."""
+    def pick(out):
+        offsets = to_np(out["offsets"]).astype(np.int64)
+        src = to_np(out["src_token"]).astype(np.int64)
+        toks = set(W.sample_rows(T, n_random, seed=seed).tolist())
+        for e in range(len(offsets) - 1):
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 <= r0:
+                continue
+            rows = {r0, r1 - 1}
+            for bm in tiles:
+                last = r0 + bm * ((r1 - 1 - r0) // bm)
+                rows.update((last, max(last - 1, r0)))
+            toks.update(int(src[r]) for r in rows)
+        return np.array(sorted(toks), dtype=np.int64)
+    return pick

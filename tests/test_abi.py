@@ -17,12 +17,12 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(moe_\w+)", out))
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert M.moe_abi_version() == 1
-    for s in range(6):
+    for s in range(7):
         assert M.moe_status_str(s)
     assert M.moe_status_str(99) == "unknown status"
 
@@ -278,3 +278,16 @@ def test_validate_mode_keeps_its_result_word_in_the_workspace(monkeypatch):
         M.moe_permute(P, 4, 2, 8, 0, 8, None, 0, 0, P, P, P, P, None, None, 0, stream=0)
     assert e.value.status == 3
     assert M.moe_status_str(5) == "routing metadata check failed"
+
+
+def test_library_stamp_matches_the_sources():
+    """The loader refuses a library built from other sources (a stale
+    binary); the loaded one carries the tree's stamp."""
+    from mixture_experts_layer_amd import build as B
+    assert M.moe_source_sha256() == B.source_sha256()
+
+
+def test_layer_status_rejects_bad_workspace():
+    assert M.lib.moe_layer_status(None, 1 << 20, None) == 1
+    assert M.lib.moe_layer_status(ctypes.c_void_p(MIS.addr), 1 << 20, None) == 1
+    assert M.lib.moe_layer_status(ctypes.c_void_p(P.addr), 4096, None) == 1

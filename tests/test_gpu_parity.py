@@ -249,6 +249,9 @@ def test_layer_small(name, H, I, E, T):
         L.w2_shared = (torch.randn((H, I), device=DEV) * s).to(torch.bfloat16)
     gl = GpuLayer(L)
     check_layer(gl, gl.run(T), T)
+    # where moe_layer takes the single-launch path, the staged one as well
+    if M.moe_layer_path(gl.desc, T) == "decode":
+        check_layer(gl, gl.run(T, path="staged"), T)
 
 
 # the ABI's limits: many experts and k > 16 (gating with 4-wave tiles and
@@ -287,26 +290,43 @@ def test_layer_tile_path(name, H, I, E, T):
     check_layer(gl2, gl2.run(T), T)
 
 
-# The shared expert rides in the routed GEMMs' launches or runs in its own,
-# by both problems' tile choices.  At H = 1024, I = 256, E = 64, k = 8 a
-# 256-wide shared expert shares the direct launches (T = 1), takes the
-# routed 16-row tile in place of its own LDS tile (T = 16), shares the
-# LDS-tiled launches (T = 64) and takes the routed 128-row tile in place of
-# its own 256-row one (T = 600).  A 512-wide one runs in its own launches at
-# T = 1 (its down projection takes more waves per block than the routed
-# one) and shares the LDS-tiled launches at T = 64.
-@pytest.mark.parametrize("I_shared,T", [(256, 1), (256, 16), (256, 64), (256, 600), (512, 1),
-                                        (512, 64)])
-def test_shared_expert_with_the_routed_launches(I_shared, T):
+# The shared expert's GEMMs ride in the routed GEMMs' launches or run in
+# launches of their own, each GEMM by its own choice (plan_layer_gemms; the
+# host test test_host_tile_choice.py asserts these plans).  Always through
+# the staged path, which is the one that makes these launches (moe_layer
+# would take the single-launch path at the smaller T here).  At H = 1024,
+# I = 256, E = 64, k = 8:
+#   I_shared = 256: both GEMMs ride in the direct launches (T = 1), both take
+#     the routed 16-row tile in place of their own LDS tile (T = 16), both ride
+#     in the LDS-tiled launches (T = 64), both take the routed 128-row tile in
+#     place of their own 256-row one (T = 600);
+#   I_shared = 512: the gate/up GEMM rides in the routed launch and the down
+#     projection has its own (T = 1: it takes more waves per block than the
+#     routed one; T = 16: the gate/up GEMM switched to the routed tile, the
+#     down projection on its own 128-row tile); both ride at T = 64.
+# The opposite mix -- the gate/up GEMM in its own launch, the down projection
+# riding -- needs a long contraction: H = 6144, I = 2048, I_shared = 4096,
+# E = 32, k = 8, T = 4 (routed gate/up on LDS tiles, its down projection
+# direct, the shared expert's direct 16-row tile fitting only the latter).
+SHARED_CASES = [(1024, 256, 64, 256, 1), (1024, 256, 64, 256, 16), (1024, 256, 64, 256, 64),
+                (1024, 256, 64, 256, 600), (1024, 256, 64, 512, 1), (1024, 256, 64, 512, 16),
+                (1024, 256, 64, 512, 64), (6144, 2048, 32, 4096, 4)]
+
+
+@pytest.mark.parametrize("H,I,E,I_shared,T", SHARED_CASES)
+def test_shared_expert_with_the_routed_launches(H, I, E, I_shared, T):
     cfg = W.CONFIGS["deepseek_v3"]
-    H, I, E = 1024, 256, 64
     L = W.make_layer(cfg, device=DEV, seed=8, T_max=T, H=H, I=I, E=E)
     s = 1.0 / H ** 0.5
-    L.w13_shared = (torch.randn((2 * I_shared, H), device=DEV) * s).to(torch.bfloat16)
-    L.w2_shared = (torch.randn((H, I_shared), device=DEV) * s).to(torch.bfloat16)
-    for kw in (dict(), dict(e_begin=8, e_end=40)):
+    g = torch.Generator(device=DEV).manual_seed(8)
+    L.w13_shared = (torch.randn((2 * I_shared, H), device=DEV, generator=g) * s).to(torch.bfloat16)
+    L.w2_shared = (torch.randn((H, I_shared), device=DEV, generator=g) * s).to(torch.bfloat16)
+    ranges = (dict(), dict(e_begin=8, e_end=24)) if E <= 32 else (dict(), dict(e_begin=8, e_end=40))
+    for kw in ranges:
         gl = GpuLayer(L, **kw)
-        check_layer(gl, gl.run(T), T)
+        check_layer(gl, gl.run(T, path="staged"), T)
+    del L
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("T", [1, 9, 64, 200])

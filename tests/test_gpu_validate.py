@@ -109,3 +109,39 @@ def test_capacity_layer_passes(validate):
         M.moe_layer_capacity(gl.desc, T, C, padded, L.x[:T], y, ws_tensor(nb), nb, None, dropped)
         torch.cuda.synchronize()
         assert int(dropped[0]) > 0
+
+
+WAIT = 6
+
+
+def _decode_layer():
+    cfg = W.CONFIGS["qwen3_tp8_rank0"]
+    L = W.make_layer(cfg, device=DEV, seed=12, T_max=8, H=512, I=256, E=32)
+    return GpuLayer(L)
+
+
+def test_wait_error_word_is_reported_by_a_validated_call(validate):
+    """A wait error word left in the workspace (written here from the host;
+    no kernel is made to wait) makes the next validated decode-path call
+    return MOE_ERR_WAIT, and that call clears it."""
+    gl = _decode_layer()
+    assert M.moe_layer_path(gl.desc, 8) == "decode"
+    gl.run(8)                                   # a clean validated call passes
+    gl.ws[4:8].view(torch.int32).fill_(2)       # bit 1: an expert wait ran out
+    with pytest.raises(M.MoEError) as e:
+        gl.run(8)
+    assert e.value.status == WAIT
+    assert gl.sync_error() == 0                 # read and cleared
+    gl.run(8)
+
+
+def test_layer_status_reads_and_clears_the_wait_word():
+    gl = _decode_layer()
+    gl.run(8)
+    M.moe_layer_status(gl.ws, gl.ws_bytes)      # clean
+    gl.ws[4:8].view(torch.int32).fill_(1)       # bit 0: the router wait ran out
+    with pytest.raises(M.MoEError) as e:
+        M.moe_layer_status(gl.ws, gl.ws_bytes)
+    assert e.value.status == WAIT
+    assert gl.sync_error() == 0
+    M.moe_layer_status(gl.ws, gl.ws_bytes)

@@ -64,6 +64,26 @@ CASES = [
      dict(gate_up="128", down="128", shared_gate_up="shared", shared_down="shared")),
     (("deepseek", 7168, 2048, 2048, 256, 256, 8, 4096),
      dict(gate_up="128", down="128", shared_gate_up="own", shared_down="own")),
+    # the shapes of the GPU test of the shared expert's launches
+    # (test_gpu_parity.py), one per combination of the two choices
+    (("small_shared", 1024, 256, 256, 64, 64, 8, 1),
+     dict(gate_up="16", shared_gate_up="shared", shared_down="shared")),
+    (("small_shared", 1024, 256, 256, 64, 64, 8, 16),
+     dict(gate_up="16", shared_gate_up="shared_switched", shared_down="shared_switched")),
+    (("small_shared", 1024, 256, 256, 64, 64, 8, 64),
+     dict(gate_up="128", shared_gate_up="shared", shared_down="shared")),
+    (("small_shared", 1024, 256, 256, 64, 64, 8, 600),
+     dict(gate_up="128", shared_expert="256", shared_gate_up="shared_switched",
+          shared_down="shared_switched")),
+    (("small_shared", 1024, 256, 512, 64, 64, 8, 1),
+     dict(gate_up="16", shared_gate_up="shared", shared_down="own")),
+    (("small_shared", 1024, 256, 512, 64, 64, 8, 16),
+     dict(gate_up="16", shared_gate_up="shared_switched", shared_down="own",
+          shared_down_tile="128")),
+    (("small_shared", 1024, 256, 512, 64, 64, 8, 64),
+     dict(gate_up="128", shared_gate_up="shared", shared_down="shared")),
+    (("wide_shared", 6144, 2048, 4096, 32, 32, 8, 4),
+     dict(gate_up="128", down="16", shared_gate_up="own", shared_down="shared")),
 ]
 
 
