@@ -451,6 +451,33 @@ size_t moe_layer_capacity_workspace_size(const moe_layer_desc* d, int T_max, int
 int moe_layer_decode(const moe_layer_desc* d, int T, const void* x, void* y,
                      void* ws, size_t ws_bytes, moe_debug_out* dbg, void* stream);
 
+/* Bytes of the device array moe_layer_static uses as its workspace. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* moe_layer without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a file-scope device array of
+ * MOE_STATIC_SCRATCH_BYTES (64 MiB), one per GPU the library runs on,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends; the call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).  Same arguments (less ws, ws_bytes), path
+ * choice, results and debug copies as moe_layer.
+ *   The first call on a device looks up the array's address and clears its
+ * synchronisation block by a small kernel on `stream`, ahead of the call's
+ * own launches.  Every later call on that GPU reuses the array, which keeps
+ * the last call's contents; calls that may overlap on one GPU (different
+ * streams, or several threads) race on it and must be ordered by the caller.
+ * Returns MOE_ERR_WORKSPACE, before touching the GPU, when
+ * moe_layer_workspace_size(d, T) exceeds MOE_STATIC_SCRATCH_BYTES (it serves
+ * decode-sized batches: T up to 400 for the DeepSeek-V3 shape with its shared
+ * expert, 737 for the Qwen3-shaped share with all 128 experts, 907 for the
+ * Mixtral shape, 966 for the Qwen3 TP share at P = 8); other errors as
+ * moe_layer.  The wait error word (see
+ * moe_layer_workspace_size) lives in the array too and cannot be read by
+ * moe_layer_status: use MOE_VALIDATE=1 to have it checked. */
+int moe_layer_static(const moe_layer_desc* d, int T, const void* x, void* y,
+                     moe_debug_out* dbg, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

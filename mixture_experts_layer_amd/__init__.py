@@ -14,7 +14,8 @@ import os
 
 from ._abi import (MOE_F32, MOE_BF16, MOE_OK, GATE_TOPK_SOFTMAX, GATE_SOFTMAX_TOPK,  # noqa: F401
                    GATE_SOFTMAX_TOPK_RENORM, GATE_SIGMOID_BIAS_RENORM, MoELayerDesc, MoEDebugOut,
-                   EXPORTED_SYMBOLS, LAYER_SYNC_BYTES, lib_path, load_library)
+                   EXPORTED_SYMBOLS, LAYER_SYNC_BYTES, STATIC_SCRATCH_BYTES, lib_path,
+                   load_library)
 
 __all__ = [
     "MoEError", "lib", "get_lib", "moe_abi_version", "moe_status_str", "moe_route", "moe_permute",
@@ -22,7 +23,8 @@ __all__ = [
     "moe_grouped_ffn_workspace_size", "moe_layer_capacity", "moe_layer_capacity_workspace_size",
     "moe_combine", "moe_pack_by_rank", "moe_pack_workspace_size", "moe_unpack_sum",
     "moe_reshard_ep_to_tp_pack", "moe_reshard_tp_to_ep_interleave", "moe_layer",
-    "moe_layer_path", "moe_layer_staged", "moe_layer_decode",
+    "moe_layer_path", "moe_layer_staged", "moe_layer_decode", "moe_layer_static",
+    "STATIC_SCRATCH_BYTES",
     "moe_layer_workspace_size", "moe_layer_status", "moe_source_sha256", "MOE_ERR_WAIT",
     "layer_workspace", "layer_desc", "dtype_code", "LAYER_SYNC_BYTES",
     "MoELayerDesc", "MoEDebugOut",
@@ -235,6 +237,12 @@ def moe_layer_status(ws, ws_bytes, stream=None):
     """Read (and clear) the decode path's wait error word of a layer
     workspace; raises MoEError(MOE_ERR_WAIT) if it was set."""
     _check("moe_layer_status", lib.moe_layer_status(_p(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_static(desc: MoELayerDesc, T, x, y, dbg: MoEDebugOut | None = None, stream=None):
+    _check("moe_layer_static",
+           lib.moe_layer_static(ctypes.byref(desc), T, _p(x), _p(y),
+                                None if dbg is None else ctypes.byref(dbg), _stream(stream)))
 
 
 def layer_workspace(desc: MoELayerDesc, T_max: int, device="cuda", capacity=None, padded=0):

@@ -75,7 +75,11 @@ _SIGS = {
                                                      c_int]),
     "moe_layer_decode": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p,
                                  c_void_p, c_size_t, ctypes.POINTER(MoEDebugOut), c_void_p]),
+    "moe_layer_static": (c_int, [ctypes.POINTER(MoELayerDesc), c_int, c_void_p, c_void_p,
+                                 ctypes.POINTER(MoEDebugOut), c_void_p]),
 }
+# bytes of the device array moe_layer_static uses as its workspace
+STATIC_SCRATCH_BYTES = 64 << 20
 # bytes at the start of a layer workspace that the decode path keeps between calls
 LAYER_SYNC_BYTES = 4096 + 1024 * 128
 EXPORTED_SYMBOLS = tuple(_SIGS)

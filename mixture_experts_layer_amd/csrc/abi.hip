@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <climits>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_kernels.h"
@@ -260,6 +261,42 @@ int run_decode(const moe_layer_desc* d, int T, const void* x, void* y, const Lay
   return MOE_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// Workspace of the allocation-free entry point: one array per GPU, reserved
+// when the code object is loaded on it and held until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// its device address comes from hipGetSymbolAddress, once per device, and
+// only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// The current device's scratch address; at the first call on a device, look
+// it up and clear its decode synchronisation block on `s` (a fill kernel,
+// stream-ordered before the call's own launches).
+int static_scratch(void** out, hipStream_t s) {
+  int dev = 0;
+  MOE_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || !aligned16(p)) return MOE_ERR_HIP;
+    zero_words_kernel<<<32, 256, 0, s>>>(static_cast<int*>(p), DECODE_SYNC_BYTES / 4);
+    MOE_TRY(hipGetLastError());
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -608,6 +645,20 @@ int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y, void* ws, 
               moe_debug_out* dbg, void* stream) {
   if (moe_layer_path(d, T) == 1) return moe_layer_decode(d, T, x, y, ws, ws_bytes, dbg, stream);
   return moe_layer_staged(d, T, x, y, ws, ws_bytes, dbg, stream);
+}
+
+int moe_layer_static(const moe_layer_desc* d, int T, const void* x, void* y, moe_debug_out* dbg,
+                     void* stream) {
+  const int st = check_desc(d);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (layer_layout(d, T, nullptr, nullptr) > (size_t)MOE_STATIC_SCRATCH_BYTES)
+    return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int sst = static_scratch(&ws, static_cast<hipStream_t>(stream));
+  if (sst) return sst;
+  return moe_layer(d, T, x, y, ws, MOE_STATIC_SCRATCH_BYTES, dbg, stream);
 }
 
 static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     out = subprocess.run(["nm", "-D", "--defined-only", M.lib_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(moe_\w+)", out))
@@ -291,3 +291,18 @@ def test_layer_status_rejects_bad_workspace():
     assert M.lib.moe_layer_status(None, 1 << 20, None) == 1
     assert M.lib.moe_layer_status(ctypes.c_void_p(MIS.addr), 1 << 20, None) == 1
     assert M.lib.moe_layer_status(ctypes.c_void_p(P.addr), 4096, None) == 1
+
+
+def test_static_entry_rejects_sizes_past_its_array():
+    """moe_layer_static refuses, on the host, a call whose workspace would
+    exceed its fixed device array (and an invalid description)."""
+    d = M.MoELayerDesc(H=4096, E=128, k=8, I_loc=1536, e_begin=0, e_end=128, I_shared=0, mode=2,
+                       dt=1, w_router=P.addr, w13=P.addr, w2=P.addr)
+    assert M.moe_layer_workspace_size(d, 8192) > M.STATIC_SCRATCH_BYTES
+    assert M.lib.moe_layer_static(ctypes.byref(d), 8192, ctypes.c_void_p(P.addr),
+                                  ctypes.c_void_p(P.addr), None, None) == 3
+    assert M.lib.moe_layer_static(ctypes.byref(d), 0, None, None, None, None) == 0
+    assert M.lib.moe_layer_static(ctypes.byref(d), -1, None, None, None, None) == 1
+    d.k = 200
+    assert M.lib.moe_layer_static(ctypes.byref(d), 16, ctypes.c_void_p(P.addr),
+                                  ctypes.c_void_p(P.addr), None, None) == 1
