@@ -215,6 +215,46 @@ def test_grouped_ffn_and_combine(dt, T, E, k):
     assert np.abs(to_np(y) - y_ref).max() / np.abs(y_ref).max() <= tol
 
 
+# Expert segments crafted around the 256-row tile of the prefill GEMMs (mean
+# rows per expert >= 384): exact multiples of 256, one row, half tiles of up
+# to 128 rows (the second wave group idle), tails of 129-255 rows, an empty
+# expert; contractions of 2 to 16 LDS stages (K = 128 ... 1024).
+BIG_TILE_COUNTS = [767, 1, 128, 385, 256, 640, 0, 903]
+
+
+@pytest.mark.parametrize("H,I", [(512, 256), (1024, 128), (256, 512)])
+def test_grouped_ffn_big_tiles_ragged(H, I):
+    counts = np.array(BIG_TILE_COUNTS)
+    E, rows, T = len(counts), int(counts.sum()), 1000
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(H + I)
+    x = torch.randn((T, H), generator=g, device=DEV).to(torch.bfloat16)
+    w13 = (torch.randn((E, 2 * I, H), generator=g, device=DEV) / H ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn((E, H, I), generator=g, device=DEV) / H ** 0.5).to(torch.bfloat16)
+    src = np.random.default_rng(H + I).integers(0, T, rows).astype(np.int32)
+    y_perm = torch.empty((rows, H), dtype=torch.bfloat16, device=DEV)
+    nb = M.moe_grouped_ffn_workspace_size(rows, E, H, I, 1)
+    ws = ws_tensor(nb)
+    M.moe_grouped_ffn(None, x, _i32(src), _i32(offsets), E, rows, H, I, w13, w2, 1, y_perm, 1,
+                      ws, nb)
+    y32 = torch.empty((rows, H), dtype=torch.float32, device=DEV)
+    M.moe_grouped_ffn(None, x, _i32(src), _i32(offsets), E, rows, H, I, w13, w2, 1, y32, 0,
+                      ws, nb)
+    torch.cuda.synchronize()
+    ref = O.grouped_ffn(to_np(x), src, offsets, to_np(w13), to_np(w2))
+    scale = np.abs(ref).max()
+    for out in (y_perm, y32):
+        got = to_np(out).astype(np.float64)
+        # every row, and each expert's rows on their own (a wrong tile would
+        # show at its expert's scale)
+        assert np.abs(got - ref).max() / scale <= 1e-2
+        for e in range(E):
+            r0, r1 = offsets[e], offsets[e + 1]
+            if r1 > r0:
+                assert np.abs(got[r0:r1] - ref[r0:r1]).max() / scale <= 1e-2, e
+
+
 def test_combine_skips_nonlocal_and_adds_shared():
     T, k, H = 5, 3, 64
     y_perm = torch.randn((6, H), device=DEV)
@@ -268,6 +308,8 @@ def test_layer_many_experts(E, k, T):
 # shapes that take the LDS-tiled prefill kernel (>= 64 rows per expert,
 # I_loc a multiple of 128, H a multiple of 256), with ragged expert tails
 TILE = [
+    ("mixtral_8x7b", 512, 256, 8, 2000),        # 256-row tiles (500 rows per expert)
+    ("qwen3_ep_all128", 256, 128, 16, 1500),    # 256-row tiles, skewed
     ("mixtral_8x7b", 256, 256, 8, 300),
     ("mixtral_8x7b", 512, 384, 8, 1000),
     ("qwen3_ep_all128", 256, 128, 16, 1111),
