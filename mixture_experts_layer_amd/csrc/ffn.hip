@@ -231,6 +231,98 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
 }
 
 // ---------------------------------------------------------------------------
+// Down projection over at most 16 rows per tile-map entry with a contraction
+// of at most 2048 (a few rows per expert).  In ffn_direct_kernel every 16 x 16
+// output tile is its own block, and every one of them loads the same 16
+// activation rows: as many activation bytes as weight bytes cross each CU's
+// L1.  Here a block's 8 waves take 8 column tiles of the same rows: the rows'
+// activation fragments are loaded once, by the 8 waves together, into LDS
+// (global -> LDS, one 1 KB fragment per K step of 32), and each wave streams
+// only its own weight rows into MFMA fragments.  Each wave sums its whole
+// contraction, so no partial sums meet; a wave whose column tile is past the
+// output width only helps with the activation loads.
+// ---------------------------------------------------------------------------
+constexpr int DCOLS_WAVES = 8;       // column tiles per block
+constexpr int DCOLS_MAX_K = 2048;    // activation fragments held in LDS (64 KB)
+typedef __attribute__((address_space(3))) void dlds_void_t;
+typedef __attribute__((address_space(1))) void dgbl_void_t;
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(DirectArgs a0,
+                                                                          DirectArgs a1,
+                                                                          int grid0) {
+  constexpr int U = 8;               // K steps per weight load batch
+  const bool second = (int)blockIdx.x >= grid0;
+  const DirectArgs a = second ? a1 : a0;
+  const int bid = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
+  __shared__ __attribute__((aligned(16))) uint4 s_x[DCOLS_MAX_K / 32][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n_ct = a.N_out / 16;
+  const int n_cb = (n_ct + DCOLS_WAVES - 1) / DCOLS_WAVES;
+  const int tile = bid / n_cb;
+  const int cb = bid - tile * n_cb;
+  int e, r0, r1;
+  if (a.tile_map) {
+    if (tile >= a.n_tiles[0]) return;
+    const int4 tm = a.tile_map[tile];
+    e = tm.x; r0 = tm.y + (tile - tm.w) * a.map_bm; r1 = min(r0 + a.map_bm, tm.z);
+  } else {
+    e = 0; r0 = tile * 16; r1 = min(r0 + 16, a.M_dense);
+    if (r0 >= a.M_dense) return;
+  }
+  const int S = a.K / 32;
+  // the rows' activation fragments: fragment s holds, in lane l, row
+  // r0 + l % 16 and K elements 32 s + 8 (l / 16) + [0, 8); rows past r1
+  // read row r0 (their outputs are not stored)
+  {
+    const int row = r0 + (lane & 15) < r1 ? r0 + (lane & 15) : r0;
+    const int src = a.src_token ? max(a.src_token[row], 0) : row;
+    const bf16_t* xp = a.X + (size_t)src * a.K + 8 * (lane >> 4);
+    const int wu = __builtin_amdgcn_readfirstlane(wid);
+    for (int st = wu; st < S; st += DCOLS_WAVES)
+      __builtin_amdgcn_global_load_lds((dgbl_void_t*)(xp + 32 * st), (dlds_void_t*)&s_x[st][0], 16,
+                                       0, 0);
+  }
+  const int ct = cb * DCOLS_WAVES + wid;
+  const bool live = ct < n_ct;
+  const int n0 = 16 * (live ? ct : 0);
+  const bf16_t* wp =
+      a.W + (size_t)e * a.w_stride + (size_t)(n0 + (lane & 15)) * a.K + 8 * (lane >> 4);
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += U) {
+    uint4 wv[U];
+    if (live) {
+#pragma unroll
+      for (int q = 0; q < U; ++q) wv[q] = *reinterpret_cast<const uint4*>(wp + 32 * min(s0 + q, S - 1));
+    }
+    if (s0 == 0) {
+      // every wave's activation loads (and its first weight batch) have
+      // landed before any wave reads the fragments
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    if (live) {
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        if (s0 + q < S)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[q]), as_bf16x8(s_x[s0 + q][lane]),
+                                                        acc, 0, 0, 0);
+    }
+  }
+  if (!live) return;
+  // lane l holds columns n0 + 4 (l / 16) + [0, 4) of row r0 + l % 16
+  const int row = r0 + (lane & 15);
+  if (row >= r1) return;
+  const size_t yi = (size_t)row * a.N_out + n0 + 4 * (lane >> 4);
+  if (OUT_BF16)
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.Y) + yi) =
+        make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+  else
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + yi) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+
+// ---------------------------------------------------------------------------
 // LDS-tiled bf16 MFMA kernel for prefill-sized row counts.
 //
 // Block tile: TM rows x TN weight rows, K in chunks of TK, WM x WN waves,
@@ -882,9 +974,26 @@ static int direct_nw(int BM, int K) {
 
 // b (optional, b_tiles row tiles): a second problem in the same launch; its
 // waves per block must equal a's (the caller checks).
+// Whether a direct down projection runs as ffn_direct_cols_kernel: 16-row
+// tiles (no walk over a larger map entry), the activation fragments within
+// the LDS it reserves, output columns in whole tiles.
+static bool direct_cols_ok(const DirectArgs& a, bool swiglu, int BM) {
+  return !swiglu && BM == 16 && a.map_bm <= 16 && a.K <= DCOLS_MAX_K && a.N_out % 16 == 0;
+}
+
 template <bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, const DirectArgs* b,
                                 int b_tiles, hipStream_t st) {
+  if constexpr (!SWIGLU) {
+    if (direct_cols_ok(a, false, BM) && (!b || direct_cols_ok(*b, false, BM))) {
+      const int cb = (a.N_out / 16 + DCOLS_WAVES - 1) / DCOLS_WAVES;
+      const int grid0 = max_tiles * cb;
+      const int grid1 = b ? b_tiles * ((b->N_out / 16 + DCOLS_WAVES - 1) / DCOLS_WAVES) : 0;
+      ffn_direct_cols_kernel<OUT_BF16><<<grid0 + grid1, DCOLS_WAVES * 64, 0, st>>>(a, b ? *b : a,
+                                                                                 grid0);
+      return hipGetLastError();
+    }
+  }
   const int nw = direct_nw<SWIGLU>(BM, a.K);
   if (BM == 16)
     return launch_direct_nw<1, DIRECT_NT16, SWIGLU, OUT_BF16>(a, nw, max_tiles, b, b_tiles, st);
@@ -923,6 +1032,10 @@ bool ffn_can_share_gemm(const FfnArgs& a, int BM, const FfnArgs& b, int b_BM, bo
            ffn_tile_ok(a.H, a.I_loc) && ffn_tile_ok(b.H, b.I_loc) && a.map_bm <= 0 &&
            b.map_bm <= 0;
   if (gate_up) return direct_nw<true>(BM, a.H) == direct_nw<true>(BM, b.H);
+  // both in ffn_direct_cols_kernel, or both in ffn_direct_kernel with the
+  // same waves per block (launch_direct takes the first only if both can)
+  if (direct_cols_ok(down_direct(a, BM), false, BM) && direct_cols_ok(down_direct(b, BM), false, BM))
+    return true;
   return direct_nw<false>(BM, a.I_loc) == direct_nw<false>(BM, b.I_loc);
 }
 

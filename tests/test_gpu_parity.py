@@ -342,17 +342,21 @@ def test_layer_tile_path(name, H, I, E, T):
 #     the routed 16-row tile in place of their own LDS tile (T = 16), both ride
 #     in the LDS-tiled launches (T = 64), both take the routed 128-row tile in
 #     place of their own 256-row one (T = 600);
-#   I_shared = 512: the gate/up GEMM rides in the routed launch and the down
-#     projection has its own (T = 1: it takes more waves per block than the
-#     routed one; T = 16: the gate/up GEMM switched to the routed tile, the
-#     down projection on its own 128-row tile); both ride at T = 64.
+#   I_shared = 512: both ride as with 256 (the down projections in the
+#     kernel that shares its rows' activations through LDS);
+#   I_shared = 4096: the gate/up GEMM rides in the routed launch and the down
+#     projection has its own (T = 1: its 4096-long contraction takes the plain
+#     direct kernel, with more waves per block than the routed one; T = 16:
+#     the gate/up GEMM switched to the routed tile, the down projection on its
+#     own 128-row tile).
 # The opposite mix -- the gate/up GEMM in its own launch, the down projection
 # riding -- needs a long contraction: H = 6144, I = 2048, I_shared = 4096,
 # E = 32, k = 8, T = 4 (routed gate/up on LDS tiles, its down projection
 # direct, the shared expert's direct 16-row tile fitting only the latter).
 SHARED_CASES = [(1024, 256, 64, 256, 1), (1024, 256, 64, 256, 16), (1024, 256, 64, 256, 64),
                 (1024, 256, 64, 256, 600), (1024, 256, 64, 512, 1), (1024, 256, 64, 512, 16),
-                (1024, 256, 64, 512, 64), (6144, 2048, 32, 4096, 4)]
+                (1024, 256, 64, 512, 64), (1024, 256, 64, 4096, 1), (1024, 256, 64, 4096, 16),
+                (6144, 2048, 32, 4096, 4)]
 
 
 @pytest.mark.parametrize("H,I,E,I_shared,T", SHARED_CASES)

@@ -75,9 +75,20 @@ CASES = [
     (("small_shared", 1024, 256, 256, 64, 64, 8, 600),
      dict(gate_up="128", shared_expert="256", shared_gate_up="shared_switched",
           shared_down="shared_switched")),
+    # (both down projections in the kernel that shares its rows' activations
+    # through LDS, which any two can share a launch of)
     (("small_shared", 1024, 256, 512, 64, 64, 8, 1),
-     dict(gate_up="16", shared_gate_up="shared", shared_down="own")),
+     dict(gate_up="16", shared_gate_up="shared", shared_down="shared")),
     (("small_shared", 1024, 256, 512, 64, 64, 8, 16),
+     dict(gate_up="16", shared_gate_up="shared_switched", shared_down="shared_switched",
+          shared_down_tile="16")),
+    # a 4096-long shared down contraction is past that kernel's LDS, and its
+    # direct kernel takes more waves per block than the routed one: the
+    # shared gate/up GEMM rides in the routed launch, its down projection
+    # has its own
+    (("wide_shared_down", 1024, 256, 4096, 64, 64, 8, 1),
+     dict(gate_up="16", shared_gate_up="shared", shared_down="own")),
+    (("wide_shared_down", 1024, 256, 4096, 64, 64, 8, 16),
      dict(gate_up="16", shared_gate_up="shared_switched", shared_down="own",
           shared_down_tile="128")),
     (("small_shared", 1024, 256, 512, 64, 64, 8, 64),
