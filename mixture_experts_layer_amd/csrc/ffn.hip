@@ -387,7 +387,16 @@ struct TileCfg {
   static constexpr int NLOADS_H = XLOADS_H + WLOADS;
   static constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
   static constexpr int MFM = WTM / 32, MFN = WTN / 32;
-  static constexpr int LDS = STAGES * SBYTES;
+  // A half tile of the 256 x 256 two-stage configuration runs "wide": its
+  // TM/2 rows against 2 TN weight rows (two adjacent N-tiles), its 8 waves
+  // in one row of wave tiles of the usual shape.  Its stage holds TM/2 x rows
+  // and 2 TN weight rows, so every stage buffer is sized for the larger one.
+  static constexpr bool WIDE = TM == 256 && TN == 256 && STAGES == 2 && WM == 2 && WN == 4;
+  static constexpr int WLOADS_W = 2 * WLOADS;
+  static constexpr int NLOADS_W = XLOADS_H + WLOADS_W;
+  static constexpr int SSTRIDE =
+      WIDE ? (SBYTES > XBYTES / 2 + 2 * WBYTES ? SBYTES : XBYTES / 2 + 2 * WBYTES) : SBYTES;
+  static constexpr int LDS = STAGES * SSTRIDE;
   static_assert(TM % (RPI * NWAVE) == 0 && TN % (RPI * NWAVE) == 0, "load split");
   static_assert(WTM % 32 == 0 && WTN % 64 == 0, "wave tile");
   static_assert(TK % 16 == 0, "k step");
@@ -428,8 +437,11 @@ template <class C, bool SWIGLU, bool OUT_BF16>
 struct TileOut {
   static constexpr int OC = SWIGLU ? C::TN / 2 : C::TN;   // output columns per block
   static constexpr int PITCH = OC * 2 + 16;                // staged row bytes
+  static constexpr int PITCH_W = 2 * OC * 2 + 16;          // wide half tile: TM/2 rows, 2 OC
   static constexpr bool STAGED = OUT_BF16 && !SWIGLU;
-  static constexpr int LDS = (STAGED && C::TM * PITCH > C::LDS) ? C::TM * PITCH : C::LDS;
+  static constexpr int OUT_BYTES =
+      C::WIDE && C::TM / 2 * PITCH_W > C::TM * PITCH ? C::TM / 2 * PITCH_W : C::TM * PITCH;
+  static constexpr int LDS = (STAGED && OUT_BYTES > C::LDS) ? OUT_BYTES : C::LDS;
   static_assert(LDS <= 160 * 1024, "LDS per block");
 };
 
@@ -472,6 +484,20 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
   const int r0 = off + m_t * C::TM;
   const int r1 = min(r0 + C::TM, end);
   const int n0 = n_t * n_cols_tile;
+  // A tile of at most TM/2 rows (an expert's last) in a configuration that
+  // allows it takes two adjacent N-tiles at once: the block of the even one
+  // runs wide, the block of the odd one has nothing left to do.  (Its cost
+  // then matches a full tile's, which keeps the blocks of an expert running
+  // in step; a half tile finishing early had let them drift apart and fetch
+  // shared weight and token tiles again from beyond L2.)
+  const bool half_rows = C::HALF_OK && r1 - r0 <= C::TM / 2;
+  bool wide = false;
+  if constexpr (C::WIDE) {
+    if (half_rows) {
+      if (n_t & 1) return;
+      wide = n_t + 1 < NTn;
+    }
+  }
 
   // ---- per-lane global source pointers for the load instructions
   const int prow = lane / C::CPR;    // row inside a load instruction's row group
@@ -486,13 +512,17 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
     xsrc[j] = a.X + (size_t)src * a.K + (pchunk ^ tile_swz<C>(rt)) * 8;
   }
   const bf16_t* We = a.W + (size_t)e * a.w_stride;
-  const bf16_t* wsrc[C::WLOADS];
+  constexpr int WLA = C::WIDE ? C::WLOADS_W : C::WLOADS;   // weight loads of the widest mode
+  const bf16_t* wsrc[WLA];
+  // gate rows first (TN/2, or TN when wide), then the matching up rows
+  const int gate_rows = wide ? C::TN : C::TN / 2;
 #pragma unroll
-  for (int j = 0; j < C::WLOADS; ++j) {
+  for (int j = 0; j < WLA; ++j) {
     const int rt = (wid + C::NWAVE * j) * C::RPI + prow;
     int wrow;
-    if (SWIGLU) wrow = rt < C::TN / 2 ? n0 + rt : a.up_off + n0 + (rt - C::TN / 2);
+    if (SWIGLU) wrow = rt < gate_rows ? n0 + rt : a.up_off + n0 + (rt - gate_rows);
     else wrow = n0 + rt;
+    if (j >= C::WLOADS && !wide) wrow = n0;           // unused
     wsrc[j] = We + (size_t)wrow * a.K + (pchunk ^ tile_swz<C>(rt)) * 8;
   }
 
@@ -500,33 +530,36 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
   // upper half (padding) are not loaded and the waves that own them skip
   // their LDS reads and MFMAs, leaving their SIMD's MFMA pipe to the other
   // wave.  They still take part in the loads of weights and in every barrier.
-  const bool half = C::HALF_OK && r1 - r0 <= C::TM / 2;
+  const bool half = half_rows && !wide;
   // buffer path: byte offsets of the same addresses from the buffers' bases
-  uint32_t xo[C::XLOADS], wo[C::WLOADS];
+  uint32_t xo[C::XLOADS], wo[WLA];
   if constexpr (BUF) {
 #pragma unroll
     for (int j = 0; j < C::XLOADS; ++j)
       xo[j] = (uint32_t)(reinterpret_cast<const unsigned char*>(xsrc[j]) -
                          reinterpret_cast<const unsigned char*>(a.X));
 #pragma unroll
-    for (int j = 0; j < C::WLOADS; ++j)
+    for (int j = 0; j < WLA; ++j)
       wo[j] = (uint32_t)(reinterpret_cast<const unsigned char*>(wsrc[j]) -
                          reinterpret_cast<const unsigned char*>(We));
   }
   const uint32_t x_nbytes = (uint32_t)a.x_bytes;
   const uint32_t w_nbytes = (uint32_t)(a.w_stride * 2);
   const int wid_u = __builtin_amdgcn_readfirstlane(wid);
-  auto issue = [&](int ks, int buf, auto half_c) {
-    constexpr int XL = decltype(half_c)::value ? C::XLOADS_H : C::XLOADS;
-    unsigned char* sx = smem + buf * C::SBYTES;
-    unsigned char* sw = sx + C::XBYTES;
+  // mode 0: full tile, 1: half tile, 2: wide half tile
+  auto issue = [&](int ks, int buf, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr int XL = MODE == 0 ? C::XLOADS : C::XLOADS_H;
+    constexpr int WL = MODE == 2 ? C::WLOADS_W : C::WLOADS;
+    unsigned char* sx = smem + buf * C::SSTRIDE;
+    unsigned char* sw = sx + (MODE == 2 ? C::XBYTES / 2 : C::XBYTES);
     if constexpr (BUF) {
       const uint32_t soff = (uint32_t)ks * (C::TK * 2);
 #pragma unroll
       for (int j = 0; j < XL; ++j)
         buffer_load_lds16(a.X, x_nbytes, sx + (wid_u + C::NWAVE * j) * 1024, xo[j], soff);
 #pragma unroll
-      for (int j = 0; j < C::WLOADS; ++j)
+      for (int j = 0; j < WL; ++j)
         buffer_load_lds16(We, w_nbytes, sw + (wid_u + C::NWAVE * j) * 1024, wo[j], soff);
     } else {
       const int ko = ks * C::TK;
@@ -535,13 +568,14 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[j] + ko),
                                          (lds_void_t*)(sx + (wid_u + C::NWAVE * j) * 1024), 16, 0, 0);
 #pragma unroll
-      for (int j = 0; j < C::WLOADS; ++j)
+      for (int j = 0; j < WL; ++j)
         __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[j] + ko),
                                          (lds_void_t*)(sw + (wid_u + C::NWAVE * j) * 1024), 16, 0, 0);
     }
   };
 
-  const int wm = wid / C::WN, wn = wid % C::WN;
+  // wide: one row of 8 wave tiles (same shape) across 2 TN weight rows
+  const int wm = wide ? 0 : wid / C::WN, wn = wide ? wid : wid % C::WN;
   const int lrow = lane & 31;
   const bool idle = half && wm * C::WTM >= C::TM / 2;
   const int khalf = lane >> 5;
@@ -551,7 +585,7 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
   for (int ni = 0; ni < C::MFN; ++ni) {
     if (SWIGLU) {
       constexpr int HALF = C::MFN / 2;
-      nbase[ni] = (ni < HALF ? 0 : C::TN / 2) + wn * (C::WTN / 2) + (ni % HALF) * 32;
+      nbase[ni] = (ni < HALF ? 0 : gate_rows) + wn * (C::WTN / 2) + (ni % HALF) * 32;
     } else {
       nbase[ni] = wn * C::WTN + ni * 32;
     }
@@ -592,13 +626,14 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
       wf[ni] = *reinterpret_cast<const bf16x8_t*>(sw + woff[ni] + ((c ^ wsw[ni]) * 16));
   };
   // One stage loop, instantiated for full tiles, for the computing waves of
-  // half tiles and for their idle waves; the choice is made once per wave.
-  auto stage_loop = [&](auto half_c, auto compute_c) {
-  constexpr bool HALF = decltype(half_c)::value;
-  constexpr int NL = HALF ? C::NLOADS_H : C::NLOADS;
+  // half tiles, for their idle waves and for wide half tiles; the choice is
+  // made once per wave.
+  auto stage_loop = [&](auto mode_c, auto compute_c) {
+  constexpr int MODE = decltype(mode_c)::value;
+  constexpr int NL = MODE == 0 ? C::NLOADS : MODE == 1 ? C::NLOADS_H : C::NLOADS_W;
 #pragma unroll
   for (int s0 = 0; s0 < C::STAGES - 1; ++s0)
-    if (s0 < nk) issue(s0, s0, half_c);
+    if (s0 < nk) issue(s0, s0, mode_c);
   for (int ks = 0; ks < nk; ++ks) {
     // Stage ks has landed for this wave once at most the loads of the
     // STAGES-2 younger stages are outstanding; the barrier makes that true
@@ -614,10 +649,10 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
       case 3: wait_stage_barrier<(C::STAGES > 4 ? 3 : 1) * NL>(); break;
       default: wait_stage_barrier<(C::STAGES > 5 ? 4 : 1) * NL>(); break;
     }
-    if (ks + C::STAGES - 1 < nk) issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES, half_c);
+    if (ks + C::STAGES - 1 < nk) issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES, mode_c);
     if constexpr (!decltype(compute_c)::value) continue;
-    const unsigned char* sx = smem + (ks % C::STAGES) * C::SBYTES;
-    const unsigned char* sw = sx + C::XBYTES;
+    const unsigned char* sx = smem + (ks % C::STAGES) * C::SSTRIDE;
+    const unsigned char* sw = sx + (MODE == 2 ? C::XBYTES / 2 : C::XBYTES);
     bf16x8_t xf[2][C::MFM], wf[2][C::MFN];
     load_frags(sx, sw, 0, xf[0], wf[0]);
 #pragma unroll
@@ -635,9 +670,19 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
     }
   }
   };
-  if (!half) stage_loop(std::false_type{}, std::true_type{});
-  else if (!idle) stage_loop(std::true_type{}, std::true_type{});
-  else stage_loop(std::true_type{}, std::false_type{});
+  using Full = std::integral_constant<int, 0>;
+  using Half = std::integral_constant<int, 1>;
+  using Wide = std::integral_constant<int, 2>;
+  if constexpr (C::WIDE) {
+    if (wide) stage_loop(Wide{}, std::true_type{});
+    else if (!half) stage_loop(Full{}, std::true_type{});
+    else if (!idle) stage_loop(Half{}, std::true_type{});
+    else stage_loop(Half{}, std::false_type{});
+  } else {
+    if (!half) stage_loop(Full{}, std::true_type{});
+    else if (!idle) stage_loop(Half{}, std::true_type{});
+    else stage_loop(Half{}, std::false_type{});
+  }
 
   // ---- epilogue
   using O = TileOut<C, SWIGLU, OUT_BF16>;
@@ -645,10 +690,11 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
     // every wave is done reading the stage buffers (their loads all landed
     // before the last stage) before the tile is staged over them
     lds_barrier();
+    const int pitch = wide ? O::PITCH_W : O::PITCH;
 #pragma unroll
     for (int mi = 0; mi < C::MFM; ++mi) {
       if (idle) break;
-      unsigned char* so = smem + (wm * C::WTM + mi * 32 + lrow) * O::PITCH;
+      unsigned char* so = smem + (wm * C::WTM + mi * 32 + lrow) * pitch;
       if (SWIGLU) {
         constexpr int HALF = C::MFN / 2;
 #pragma unroll
@@ -677,15 +723,19 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
       }
     }
     lds_barrier();
-    constexpr int CPR_OUT = O::OC / 8;                   // 16-byte chunks per row
     const int nrows = r1 - r0;
     bf16_t* Y = reinterpret_cast<bf16_t*>(a.Y);
-    for (int c = threadIdx.x; c < C::TM * CPR_OUT; c += C::NTHR) {
-      const int r = c / CPR_OUT, cc = c - r * CPR_OUT;
-      if (r < nrows)
-        *reinterpret_cast<uint4*>(Y + (size_t)(r0 + r) * a.N_out + n0 + cc * 8) =
-            *reinterpret_cast<const uint4*>(smem + r * O::PITCH + cc * 16);
-    }
+    auto store_rows = [&](auto cpr_c, int rows, int pitch_b) {
+      constexpr int CPR_OUT = decltype(cpr_c)::value;   // 16-byte chunks per row
+      for (int c = threadIdx.x; c < rows * CPR_OUT; c += C::NTHR) {
+        const int r = c / CPR_OUT, cc = c - r * CPR_OUT;
+        if (r < nrows)
+          *reinterpret_cast<uint4*>(Y + (size_t)(r0 + r) * a.N_out + n0 + cc * 8) =
+              *reinterpret_cast<const uint4*>(smem + r * pitch_b + cc * 16);
+      }
+    };
+    if (wide) store_rows(std::integral_constant<int, 2 * O::OC / 8>{}, C::TM / 2, O::PITCH_W);
+    else store_rows(std::integral_constant<int, O::OC / 8>{}, C::TM, O::PITCH);
     return;
   }
 #pragma unroll

@@ -216,13 +216,14 @@ def test_grouped_ffn_and_combine(dt, T, E, k):
 
 
 # Expert segments crafted around the 256-row tile of the prefill GEMMs (mean
-# rows per expert >= 384): exact multiples of 256, one row, half tiles of up
-# to 128 rows (the second wave group idle), tails of 129-255 rows, an empty
-# expert; contractions of 2 to 16 LDS stages (K = 128 ... 1024).
+# rows per expert >= 384): exact multiples of 256, one row, tails of at most
+# 128 rows (which run two N-tiles wide, or as a plain half tile on the last
+# N-tile of an odd count: 1 and 3 N-tiles below), tails of 129-255 rows, an
+# empty expert; contractions of 2 to 16 LDS stages (K = 128 ... 1024).
 BIG_TILE_COUNTS = [767, 1, 128, 385, 256, 640, 0, 903]
 
 
-@pytest.mark.parametrize("H,I", [(512, 256), (1024, 128), (256, 512)])
+@pytest.mark.parametrize("H,I", [(512, 256), (1024, 128), (256, 512), (768, 384)])
 def test_grouped_ffn_big_tiles_ragged(H, I):
     counts = np.array(BIG_TILE_COUNTS)
     E, rows, T = len(counts), int(counts.sum()), 1000
