@@ -240,7 +240,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
 // (global -> LDS, one 1 KB fragment per K step of 32), and each wave streams
 // only its own weight rows into MFMA fragments.  Each wave sums its whole
 // contraction, so no partial sums meet; a wave whose column tile is past the
-// output width only helps with the activation loads.
+// output width only helps with the activation loads.  The LDS holds exactly
+// the K / 32 fragments (1 KB each), so a short contraction leaves room for
+// more blocks per CU, and more weight streams in flight.
 // ---------------------------------------------------------------------------
 constexpr int DCOLS_WAVES = 8;       // column tiles per block
 constexpr int DCOLS_MAX_K = 2048;    // activation fragments held in LDS (64 KB)
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
   const bool second = (int)blockIdx.x >= grid0;
   const DirectArgs a = second ? a1 : a0;
   const int bid = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
-  __shared__ __attribute__((aligned(16))) uint4 s_x[DCOLS_MAX_K / 32][64];
+  extern __shared__ __attribute__((aligned(16))) uint4 s_x[];   // [K / 32][64]
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n_ct = a.N_out / 16;
   const int n_cb = (n_ct + DCOLS_WAVES - 1) / DCOLS_WAVES;
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
     const bf16_t* xp = a.X + (size_t)src * a.K + 8 * (lane >> 4);
     const int wu = __builtin_amdgcn_readfirstlane(wid);
     for (int st = wu; st < S; st += DCOLS_WAVES)
-      __builtin_amdgcn_global_load_lds((dgbl_void_t*)(xp + 32 * st), (dlds_void_t*)&s_x[st][0], 16,
+      __builtin_amdgcn_global_load_lds((dgbl_void_t*)(xp + 32 * st), (dlds_void_t*)&s_x[st * 64], 16,
                                        0, 0);
   }
   const int ct = cb * DCOLS_WAVES + wid;
@@ -293,7 +295,8 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
     uint4 wv[U];
     if (live) {
 #pragma unroll
-      for (int q = 0; q < U; ++q) wv[q] = *reinterpret_cast<const uint4*>(wp + 32 * min(s0 + q, S - 1));
+      for (int q = 0; q < U; ++q)
+        if (s0 + q < S) wv[q] = *reinterpret_cast<const uint4*>(wp + 32 * (s0 + q));
     }
     if (s0 == 0) {
       // every wave's activation loads (and its first weight batch) have
@@ -305,8 +308,9 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
 #pragma unroll
       for (int q = 0; q < U; ++q)
         if (s0 + q < S)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[q]), as_bf16x8(s_x[s0 + q][lane]),
-                                                        acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[q]),
+                                                        as_bf16x8(s_x[(s0 + q) * 64 + lane]), acc, 0,
+                                                        0, 0);
     }
   }
   if (!live) return;
@@ -1039,8 +1043,14 @@ static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, cons
       const int cb = (a.N_out / 16 + DCOLS_WAVES - 1) / DCOLS_WAVES;
       const int grid0 = max_tiles * cb;
       const int grid1 = b ? b_tiles * ((b->N_out / 16 + DCOLS_WAVES - 1) / DCOLS_WAVES) : 0;
-      ffn_direct_cols_kernel<OUT_BF16><<<grid0 + grid1, DCOLS_WAVES * 64, 0, st>>>(a, b ? *b : a,
-                                                                                 grid0);
+      const int lds = (b ? std::max(a.K, b->K) : a.K) / 32 * 1024;
+      static std::atomic<uint64_t> lds_set{0};
+      hipError_t err = ensure_lds_limit(
+          reinterpret_cast<const void*>(&ffn_direct_cols_kernel<OUT_BF16>), DCOLS_MAX_K / 32 * 1024,
+          lds_set);
+      if (err != hipSuccess) return err;
+      ffn_direct_cols_kernel<OUT_BF16><<<grid0 + grid1, DCOLS_WAVES * 64, lds, st>>>(a, b ? *b : a,
+                                                                                   grid0);
       return hipGetLastError();
     }
   }
