@@ -37,7 +37,10 @@
  *   returns MOE_ERR_HIP.  T = 0 is a successful no-op (moe_permute still
  *   writes zero counts and offsets).
  * - Shape limits: 1 <= k <= 32, k <= E <= 1024, H and I_loc multiples of 32.
- *   Other shapes return MOE_ERR_UNSUPPORTED.
+ *   The device counts logits and token pairs in int: T * E (the layer,
+ *   moe_route, moe_permute) and T * k (moe_combine, moe_pack_by_rank,
+ *   moe_unpack_sum) must not exceed 2^31 - 1.  Other shapes return
+ *   MOE_ERR_UNSUPPORTED; the size queries return 0 for them.
  * - Results are bitwise repeatable: no kernel uses atomics to combine
  *   floating-point values or to order rows (the decode path's atomics only
  *   count finished work).

@@ -21,7 +21,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int elt_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 inline bool valid_dt(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
-inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline int cdiv(int a, int b) { return a / b + (a % b != 0); }   // a >= 0, b > 0, no overflow
 
 // Bump allocator over the caller's workspace (or a size count when base == 0).
 struct Carver {
@@ -36,10 +36,15 @@ struct Carver {
   }
 };
 
+// Token-pair and logit counts are int on the device: T * E (logits; k <= E,
+// so this bounds the T * k pairs as well) must fit an int.
+bool fits_int(long long a, long long b) { return a * b <= INT_MAX; }
+
 int check_route_shape(int T, int E, int k, int mode) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (mode < 0 || mode > 3) return MOE_ERR_INVALID_ARG;
   if (E > 1024 || k > KMAX) return MOE_ERR_UNSUPPORTED;
+  if (!fits_int(T, E)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -170,6 +175,7 @@ int check_layer_call(const moe_layer_desc* d, int T, const void* x, void* y, voi
   int st = check_desc(d);
   if (st) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!fits_int(T, d->E)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
   const size_t need = layer_layout(d, T, nullptr, nullptr, pad_rows);
@@ -358,7 +364,7 @@ static size_t permute_ws_base(int T, int k, int E_loc) {
 }
 
 size_t moe_permute_workspace_size(int T, int k, int E_loc) {
-  if (T < 0 || k < 1 || E_loc < 1) return 0;
+  if (T < 0 || k < 1 || E_loc < 1 || !fits_int(T, k)) return 0;
   return permute_ws_base(T, k, E_loc) + (validate_on() ? VALIDATE_BYTES : 0);
 }
 
@@ -509,7 +515,7 @@ int moe_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row, const
   if (!valid_dt(dt) || !valid_dt(y_perm_dt) || T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
   int st = check_hidden(H);
   if (st) return st;
-  if (k > KMAX) return MOE_ERR_UNSUPPORTED;
+  if (k > KMAX || !fits_int(T, k)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y_perm || !dst_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {y_perm, dst_row, topk_w, y, y_shared};
@@ -520,7 +526,7 @@ int moe_combine(const void* y_perm, int y_perm_dt, const int32_t* dst_row, const
 }
 
 size_t moe_pack_workspace_size(int T, int k, int P) {
-  if (T < 0 || k < 1 || P < 1 || P > 64) return 0;
+  if (T < 0 || k < 1 || P < 1 || P > 64 || !fits_int(T, k)) return 0;
   const size_t n_tiles = (size_t)cdiv(T, 64);
   return align_up((size_t)T * 8) + 2 * align_up(n_tiles * P * 4);
 }
@@ -531,7 +537,7 @@ int moe_pack_by_rank(const int32_t* topk_ids, const float* topk_w, int T, int k,
                      void* x_send, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || k < 1 || E < 1 || k > E || P < 1) return MOE_ERR_INVALID_ARG;
   if (E % P) return MOE_ERR_INVALID_ARG;
-  if (k > KMAX || E > 1024 || P > 64) return MOE_ERR_UNSUPPORTED;
+  if (k > KMAX || E > 1024 || P > 64 || !fits_int(T, k)) return MOE_ERR_UNSUPPORTED;
   if (!send_counts || !send_offsets) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !send_token || !send_row)) return MOE_ERR_INVALID_ARG;
   if (send_w && !topk_w) return MOE_ERR_INVALID_ARG;
@@ -575,7 +581,7 @@ int moe_unpack_sum(const void* y_ret, int y_ret_dt, const int32_t* send_row, int
   if (!valid_dt(dt) || !valid_dt(y_ret_dt) || T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
   int st = check_hidden(H);
   if (st) return st;
-  if (k > KMAX) return MOE_ERR_UNSUPPORTED;
+  if (k > KMAX || !fits_int(T, k)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y_ret || !send_row || !y) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {y_ret, send_row, y};
@@ -620,7 +626,7 @@ int moe_layer_status(void* ws, size_t ws_bytes, void* stream) {
 }
 
 size_t moe_layer_workspace_size(const moe_layer_desc* d, int T_max) {
-  if (check_desc(d) != MOE_OK || T_max < 0) return 0;
+  if (check_desc(d) != MOE_OK || T_max < 0 || !fits_int(T_max, d->E)) return 0;
   return layer_layout(d, T_max, nullptr, nullptr);
 }
 
@@ -638,6 +644,7 @@ int moe_layer_path(const moe_layer_desc* d, int T) {
   const int st = check_desc(d);
   if (st) return -st;
   if (T < 0) return -MOE_ERR_INVALID_ARG;
+  if (!fits_int(T, d->E)) return -MOE_ERR_UNSUPPORTED;
   return (T > 0 && decode_shape_ok(d, T) && decode_preferred(d, T)) ? 1 : 0;
 }
 
@@ -652,6 +659,7 @@ int moe_layer_static(const moe_layer_desc* d, int T, const void* x, void* y, moe
   const int st = check_desc(d);
   if (st) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (!fits_int(T, d->E)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (layer_layout(d, T, nullptr, nullptr) > (size_t)MOE_STATIC_SCRATCH_BYTES)
     return MOE_ERR_WORKSPACE;
@@ -664,8 +672,9 @@ int moe_layer_static(const moe_layer_desc* d, int T, const void* x, void* y, moe
 static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void* y, void* ws,
                              size_t ws_bytes, moe_debug_out* dbg, int capacity, int padded,
                              int32_t* dropped, void* stream) {
-  // padded: expert blocks of `capacity` rows in h and y_perm (pad_rows >= 0)
-  const int pad_rows = padded ? padded_rows(d->e_end - d->e_begin, capacity) : -1;
+  // padded: expert blocks of `capacity` rows in h and y_perm (pad_rows >= 0);
+  // a missing desc is reported by check_layer_call
+  const int pad_rows = padded && d ? padded_rows(d->e_end - d->e_begin, capacity) : -1;
   int st = check_layer_call(d, T, x, y, ws, ws_bytes, dbg, pad_rows);
   if (st || T == 0) return st;
   LayerWs l;
@@ -777,6 +786,7 @@ size_t moe_layer_capacity_workspace_size(const moe_layer_desc* d, int T_max, int
                                          int padded) {
   if (check_desc(d) != MOE_OK || T_max < 0 || capacity < 0 || (padded != 0 && padded != 1))
     return 0;
+  if (!fits_int(T_max, d->E)) return 0;
   if (!padded) return layer_layout(d, T_max, nullptr, nullptr);
   const int pad_rows = padded_rows(d->e_end - d->e_begin, capacity);
   if (pad_rows < 0) return 0;

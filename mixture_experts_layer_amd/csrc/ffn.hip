@@ -1174,7 +1174,7 @@ hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnAr
 
 GemmPlan plan_layer_gemms(int dt, int T, int k, int E, int E_loc, int H, int I_loc,
                           int I_shared) {
-  auto cdiv = [](int a, int b) { return (a + b - 1) / b; };
+  auto cdiv = [](int a, int b) { return a / b + (a % b != 0); };   // a >= 0, no overflow
   GemmPlan p{};
   const int mean = cdiv(T * k, E);
   p.BM = ffn_row_tile(dt, mean, H, I_loc, T * k < E_loc ? T * k : E_loc);

@@ -49,6 +49,11 @@ def test_workspace_queries():
     n = M.moe_layer_workspace_size(d, 8192)
     assert n >= 8192 * 8 * (1536 + 4096) * 2
     assert M.moe_layer_workspace_size(d, 16) < n
+    # the device counts T * E logits in int: one token past that is rejected
+    assert M.moe_layer_workspace_size(d, (2 ** 31 - 1) // 128) > 0
+    assert M.moe_layer_workspace_size(d, (2 ** 31 - 1) // 128 + 1) == 0
+    assert M.moe_permute_workspace_size(2 ** 31 - 1, 2, 8) == 0
+    assert M.moe_permute_workspace_size(2 ** 31 - 1, 1, 8) > 0
     d.k = 200
     assert M.moe_layer_workspace_size(d, 16) == 0
 
