@@ -357,7 +357,11 @@ def test_layer_tile_path(name, H, I, E, T):
 SHARED_CASES = [(1024, 256, 64, 256, 1), (1024, 256, 64, 256, 16), (1024, 256, 64, 256, 64),
                 (1024, 256, 64, 256, 600), (1024, 256, 64, 512, 1), (1024, 256, 64, 512, 16),
                 (1024, 256, 64, 512, 64), (1024, 256, 64, 4096, 1), (1024, 256, 64, 4096, 16),
-                (6144, 2048, 32, 4096, 4)]
+                (6144, 2048, 32, 4096, 4),
+                # 256-row tiles for the routed experts (about 409 rows each) and
+                # 1636 dense shared-expert rows: six full tiles and a 100-row
+                # tail that runs two N-tiles wide
+                (512, 256, 32, 256, 1636)]
 
 
 @pytest.mark.parametrize("H,I,E,I_shared,T", SHARED_CASES)

@@ -95,6 +95,12 @@ CASES = [
      dict(gate_up="128", shared_gate_up="shared", shared_down="shared")),
     (("wide_shared", 6144, 2048, 4096, 32, 32, 8, 4),
      dict(gate_up="128", down="16", shared_gate_up="own", shared_down="shared")),
+    # 256-row tiles on both problems: the shared expert's 1636 dense rows end
+    # in a 100-row tile inside the routed launches (the GPU test of this shape
+    # checks its wide half tile)
+    (("big_shared", 512, 256, 256, 32, 32, 8, 1636),
+     dict(gate_up="256", down="256", shared_gate_up="shared", shared_down="shared",
+          shared_gate_up_tile="256", shared_down_tile="256")),
 ]
 
 
