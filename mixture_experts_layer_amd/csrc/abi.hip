@@ -194,6 +194,11 @@ int check_layer_call(const moe_layer_desc* d, int T, const void* x, void* y, voi
 // metadata is built, check it on the device and return MOE_ERR_METADATA if it
 // is inconsistent.  The check copies its result word to the host and waits
 // for the stream, so such calls cannot be captured in a graph.
+// Single-tile batches from this many tokens gate over several blocks of
+// GATE_SPLIT_TPB tokens before the one-block metadata pass.
+constexpr int GATE_SPLIT_MIN_T = 16;
+constexpr int GATE_SPLIT_TPB = 4;
+
 bool validate_on() {
   const char* v = getenv("MOE_VALIDATE");
   return v && v[0] == '1' && v[1] == '\0';
@@ -713,7 +718,21 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   a.BM = l.BM; a.tile_map = l.tile_map; a.n_tiles = l.n_tiles;
   a.max_rows = l.max_rows; a.max_tiles = l.max_tiles;
   a.capacity = capacity; a.dropped = dropped;
-  MOE_TRY(launch_gate_tiles(a, l.n_tt, s));
+  if (single && T >= GATE_SPLIT_MIN_T && E_loc <= 256) {
+    // The k arg-max rounds of a whole tile on one CU are bound by its vector
+    // ALUs (16 waves, four per SIMD): gate GATE_SPLIT_TPB tokens per block
+    // over several CUs, then build the metadata from the chosen ids in a
+    // one-block pass, as moe_permute does.
+    GateTileArgs g = a;
+    g.do_permute = 0;
+    g.tok_per_block = GATE_SPLIT_TPB;
+    MOE_TRY(launch_gate_tiles(g, cdiv(T, GATE_SPLIT_TPB), s));
+    a.do_gate = 0;
+    a.ids_in = l.ids;
+    MOE_TRY(launch_gate_tiles(a, 1, s));
+  } else {
+    MOE_TRY(launch_gate_tiles(a, l.n_tt, s));
+  }
   if (!single) {
     MOE_TRY(launch_permute_scan(l.tile_counts, l.n_tt, E_loc, l.tile_base, l.counts, l.offsets,
                                 l.BM, l.max_rows, l.max_tiles, l.tile_map, l.n_tiles, capacity,

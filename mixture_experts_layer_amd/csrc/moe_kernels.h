@@ -52,6 +52,8 @@ struct GateTileArgs {
   int32_t* n_tiles;         // [1]
   int capacity;             // pairs kept per expert (INT_MAX: dropless)
   int32_t* dropped;         // [1] or null: local pairs dropped by the capacity
+  // gating only (do_permute == 0): tokens per block, 0 = TOK_TILE
+  int tok_per_block;
 };
 
 hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,

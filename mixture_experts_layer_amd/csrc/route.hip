@@ -209,8 +209,9 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int tile = blockIdx.x;
-  const int t0 = tile * TOK_TILE;
-  const int ntok = max(0, min(TOK_TILE, a.T - t0));
+  const int tpb = a.tok_per_block > 0 ? a.tok_per_block : TOK_TILE;
+  const int t0 = tile * tpb;
+  const int ntok = max(0, min(tpb, a.T - t0));
   const int k = a.k, E = a.E;
   const int mode = a.mode;
 
@@ -421,6 +422,9 @@ static void launch_gate_epr(const GateTileArgs& a, int grid, hipStream_t st) {
 }
 
 hipError_t launch_gate_tiles(const GateTileArgs& a, int n_tiles_tok, hipStream_t st) {
+  // a token count per block other than the tile's serves the gating alone
+  if (a.tok_per_block < 0 || a.tok_per_block > TOK_TILE || (a.tok_per_block > 0 && a.do_permute))
+    return hipErrorInvalidValue;
   const int grid = n_tiles_tok > 0 ? n_tiles_tok : 1;
   const int epr = (a.E + 15) / 16;          // experts per lane of a 16-lane row
   if (epr <= 1) launch_gate_epr<1>(a, grid, st);
