@@ -13,6 +13,8 @@
 // 64-bit mask (P <= 64), so per rank a wave ballot over a 64-token tile gives
 // the tile's count (popcount) and every token's place in it (popcount of the
 // lanes below): no sort and no atomics.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -188,29 +190,54 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
   }
 }
 
-// x_send[row] = x[send_token[row]] for the rows that exist (send_offsets[P]
-// on the device); one wave per row, every 16-byte load of a lane issued
-// before its stores.
+// x_send[row] = x[t] for each copy row of each token t (its distinct
+// send_row[t][j]).  A wave takes one token, or one of `splits` column slices
+// of a token when the batch is small, loads that part of the token's row once
+// and stores it to every copy, every 16-byte load of a lane issued before its
+// stores.  (One wave per copy row had read each token's row once per copy:
+// 4.7 times at DeepSeek-V3 routing over 8 ranks.)
+template <int KP>
 __global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* __restrict__ x,
-                                                        const int32_t* __restrict__ send_token,
-                                                        const int32_t* __restrict__ n_rows, int P,
-                                                        int row_vecs, uint4* __restrict__ out) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                        const int32_t* __restrict__ send_row,
+                                                        int T, int k, int row_vecs, int splits,
+                                                        uint4* __restrict__ out) {
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= n_rows[P]) return;
+  const int t = gw / splits;
+  if (t >= T) return;
+  const int chunk = (row_vecs + splits - 1) / splits;
+  const int cb = (gw - t * splits) * chunk;
+  const int ce = min(cb + chunk, row_vecs);
+  // the token's distinct copy rows (slots sent to one rank share a row)
+  int rows[KP];
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const int r = j < k ? send_row[(size_t)t * k + j] : -1;
+    bool fresh = r >= 0;
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+      if (i < n && rows[i] == r) fresh = false;
+    if (fresh) rows[n++] = r;
+  }
+  if (n == 0 || cb >= ce) return;
   // 16-byte vectors as a clang vector type: an array of them stays in
   // registers (an array of the HIP uint4 struct would go to scratch)
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  const v4u* src = reinterpret_cast<const v4u*>(x) + (size_t)send_token[row] * row_vecs;
-  v4u* dst = reinterpret_cast<v4u*>(out) + (size_t)row * row_vecs;
+  const v4u* src = reinterpret_cast<const v4u*>(x) + (size_t)t * row_vecs;
   constexpr int B = 8;
-  for (int c0 = lane; c0 < row_vecs; c0 += 64 * B) {
+  for (int c0 = cb + lane; c0 < ce; c0 += 64 * B) {
     v4u v[B];
 #pragma unroll
-    for (int i = 0; i < B; ++i) v[i] = src[min(c0 + 64 * i, row_vecs - 1)];
+    for (int i = 0; i < B; ++i) v[i] = src[min(c0 + 64 * i, ce - 1)];
 #pragma unroll
-    for (int i = 0; i < B; ++i)
-      if (c0 + 64 * i < row_vecs) dst[c0 + 64 * i] = v[i];
+    for (int q = 0; q < KP; ++q) {
+      if (q >= n) break;
+      v4u* dst = reinterpret_cast<v4u*>(out) + (size_t)rows[q] * row_vecs;
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if (c0 + 64 * i < ce) dst[c0 + 64 * i] = v[i];
+    }
   }
 }
 
@@ -312,10 +339,22 @@ hipError_t launch_pack_by_rank(const PackArgs& a, const void* x, int H, int elt_
   if (a.k <= 8) launch_pack_kp<8>(a, st);
   else launch_pack_kp<32>(a, st);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || !x || max_rows <= 0) return err;
-  copy_rows_kernel<<<(max_rows + 3) / 4, 256, 0, st>>>(
-      static_cast<const uint4*>(x), a.send_token, a.send_offsets, a.P, H * elt_bytes / 16,
-      static_cast<uint4*>(x_send));
+  if (err != hipSuccess || !x || max_rows <= 0 || a.T <= 0) return err;
+  // small batches: split each token's row over several waves (64 vectors of
+  // 16 bytes at least), so that about 2048 waves share the copies
+  const int row_vecs = H * elt_bytes / 16;
+  int splits = 2048 / a.T;
+  splits = std::max(1, std::min(splits, row_vecs / 64));
+  const long long waves = (long long)a.T * splits;
+  const int blocks = (int)((waves + 3) / 4);
+  if (a.k <= 8)
+    copy_rows_kernel<8><<<blocks, 256, 0, st>>>(static_cast<const uint4*>(x), a.send_row, a.T,
+                                                 a.k, row_vecs, splits,
+                                                 static_cast<uint4*>(x_send));
+  else
+    copy_rows_kernel<32><<<blocks, 256, 0, st>>>(static_cast<const uint4*>(x), a.send_row, a.T,
+                                                  a.k, row_vecs, splits,
+                                                  static_cast<uint4*>(x_send));
   return hipGetLastError();
 }
 
