@@ -16,8 +16,11 @@
 // stacked axis, so that SwiGLU stays local to a TP rank.
 //
 // Pure data movement, HBM-bound: each thread copies 16-byte vectors, the
-// consecutive threads of a wave consecutive vectors of one row (or of one W2
-// row segment of s elements), all of its loads before its stores.
+// consecutive threads of a wave consecutive vectors of one row (or of
+// consecutive W2 row segments of s elements), all of a batch's loads before
+// its stores.  The layout arithmetic is done once per block (and per thread
+// for W2), not per vector with four integer divisions as in the first
+// version (1-3% faster).
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -26,77 +29,99 @@ namespace moe {
 namespace {
 
 constexpr int RS_THREADS = 256;
-constexpr int RS_PER_THREAD = 4;
+constexpr int RS_BATCH = 4;            // vectors per thread per load batch
+constexpr int RS_W2_ROWS = 256;        // W2 rows (h) per block
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// Vector offsets of element vector `idx` of the chunk layout, in the chunk
-// buffer and in the EP buffer.
-__device__ __forceinline__ void w13_offsets(int idx, int hv, int s, int n, int I,
-                                            long long& chunk, long long& ep) {
-  const int v = idx % hv;
-  int rest = idx / hv;
-  const int j = rest % (2 * s);
-  rest /= 2 * s;
-  const int e = rest % n;
-  const int p = rest / n;
+// W13: one block per chunk row r = (p, e, j), j < 2s; the row's hv vectors
+// are contiguous in both layouts (EP row p*s + j of the gate half for j < s,
+// else I + p*s + (j - s)), so the index arithmetic is once per block.
+template <bool PACK>
+__global__ __launch_bounds__(RS_THREADS) void reshard_w13_kernel(const v4u* __restrict__ src,
+                                                                 v4u* __restrict__ dst, int hv,
+                                                                 int s, int n, int I) {
+  const int r = blockIdx.x;
+  const int j = r % (2 * s);
+  const int pe = r / (2 * s);
+  const int e = pe % n, p = pe / n;
   const int row = j < s ? p * s + j : I + p * s + (j - s);
-  chunk = (long long)idx;
-  ep = ((long long)e * 2 * I + row) * hv + v;
-}
-
-__device__ __forceinline__ void w2_offsets(int idx, int sv, int iv, int H, int n,
-                                           long long& chunk, long long& ep) {
-  const int v = idx % sv;
-  int rest = idx / sv;
-  const int h = rest % H;
-  rest /= H;
-  const int e = rest % n;
-  const int p = rest / n;
-  chunk = (long long)idx;
-  ep = ((long long)e * H + h) * iv + (long long)p * sv + v;
-}
-
-// PACK: EP -> chunks; otherwise chunks -> EP.  W2: the W2 layouts, else W13.
-template <bool PACK, bool W2>
-__global__ __launch_bounds__(RS_THREADS) void reshard_kernel(const v4u* __restrict__ src,
-                                                             v4u* __restrict__ dst, int total,
-                                                             int a0, int a1, int a2, int a3) {
-  const int base = blockIdx.x * RS_THREADS * RS_PER_THREAD + threadIdx.x;
-  v4u v[RS_PER_THREAD];
-  long long d[RS_PER_THREAD];
+  const long long c_off = (long long)r * hv;
+  const long long e_off = ((long long)e * 2 * I + row) * hv;
+  const v4u* sp = src + (PACK ? e_off : c_off);
+  v4u* dp = dst + (PACK ? c_off : e_off);
+  for (int v0 = threadIdx.x; v0 < hv; v0 += RS_THREADS * RS_BATCH) {
+    v4u v[RS_BATCH];
 #pragma unroll
-  for (int u = 0; u < RS_PER_THREAD; ++u) {
-    const int idx = min(base + u * RS_THREADS, total - 1);
-    long long chunk, ep;
-    if constexpr (W2) w2_offsets(idx, a0, a1, a2, a3, chunk, ep);
-    else w13_offsets(idx, a0, a1, a2, a3, chunk, ep);
-    v[u] = PACK ? src[ep] : src[chunk];
-    d[u] = PACK ? chunk : ep;
+    for (int u = 0; u < RS_BATCH; ++u) v[u] = sp[min(v0 + u * RS_THREADS, hv - 1)];
+#pragma unroll
+    for (int u = 0; u < RS_BATCH; ++u)
+      if (v0 + u * RS_THREADS < hv) dp[v0 + u * RS_THREADS] = v[u];
   }
+}
+
+// W2: one block per (p, e) and RS_W2_ROWS rows h.  The chunk's rows are
+// contiguous (sv vectors each); in the EP layout row h's segment p starts at
+// (e*H + h)*iv + p*sv.  Each thread walks its vectors f = tid, tid + 256, ...
+// of the block's range, advancing (row, column) without a division.
+template <bool PACK>
+__global__ __launch_bounds__(RS_THREADS) void reshard_w2_kernel(const v4u* __restrict__ src,
+                                                                v4u* __restrict__ dst, int sv,
+                                                                int iv, int H, int n) {
+  const int nhb = (H + RS_W2_ROWS - 1) / RS_W2_ROWS;
+  const int hb = blockIdx.x % nhb;
+  const int pe = blockIdx.x / nhb;
+  const int e = pe % n, p = pe / n;
+  const int h0 = hb * RS_W2_ROWS;
+  const int total = (min(h0 + RS_W2_ROWS, H) - h0) * sv;
+  const long long c_base = ((long long)pe * H + h0) * sv;
+  const long long e_base = ((long long)e * H + h0) * iv + (long long)p * sv;
+  const int step_h = RS_THREADS / sv, step_v = RS_THREADS - step_h * sv;
+  int f = threadIdx.x;
+  int hh = f / sv, vv = f - hh * sv;
+  while (f < total) {
+    long long cs[RS_BATCH], es[RS_BATCH];
+    int nb = 0;
 #pragma unroll
-  for (int u = 0; u < RS_PER_THREAD; ++u)
-    if (base + u * RS_THREADS < total) dst[d[u]] = v[u];
+    for (int u = 0; u < RS_BATCH; ++u) {
+      cs[u] = c_base + f;
+      es[u] = e_base + (long long)hh * iv + vv;
+      if (f < total) nb = u + 1;
+      f += RS_THREADS;
+      hh += step_h;
+      vv += step_v;
+      if (vv >= sv) {
+        vv -= sv;
+        ++hh;
+      }
+    }
+    v4u v[RS_BATCH];
+#pragma unroll
+    for (int u = 0; u < RS_BATCH; ++u)
+      if (u < nb) v[u] = src[PACK ? es[u] : cs[u]];
+#pragma unroll
+    for (int u = 0; u < RS_BATCH; ++u)
+      if (u < nb) dst[PACK ? cs[u] : es[u]] = v[u];
+  }
 }
 
 template <bool PACK>
 hipError_t launch_reshard_dir(const void* w13_src, const void* w2_src, int n, int I, int H, int P,
                               int elt, void* w13_dst, void* w2_dst, hipStream_t st) {
   const int s = I / P;
-  const int per_block = RS_THREADS * RS_PER_THREAD;
   if (w13_src) {
     const int hv = H * elt / 16;
-    const long long total = (long long)P * n * 2 * s * hv;
-    if (total > 0)
-      reshard_kernel<PACK, false><<<(int)((total + per_block - 1) / per_block), RS_THREADS, 0, st>>>(
-          static_cast<const v4u*>(w13_src), static_cast<v4u*>(w13_dst), (int)total, hv, s, n, I);
+    const long long rows = (long long)P * n * 2 * s;
+    if (rows > 0 && hv > 0)
+      reshard_w13_kernel<PACK><<<(int)rows, RS_THREADS, 0, st>>>(
+          static_cast<const v4u*>(w13_src), static_cast<v4u*>(w13_dst), hv, s, n, I);
   }
   if (w2_src) {
     const int sv = s * elt / 16, iv = I * elt / 16;
-    const long long total = (long long)P * n * H * sv;
-    if (total > 0)
-      reshard_kernel<PACK, true><<<(int)((total + per_block - 1) / per_block), RS_THREADS, 0, st>>>(
-          static_cast<const v4u*>(w2_src), static_cast<v4u*>(w2_dst), (int)total, sv, iv, H, n);
+    const long long blocks = (long long)P * n * ((H + RS_W2_ROWS - 1) / RS_W2_ROWS);
+    if (blocks > 0 && sv > 0)
+      reshard_w2_kernel<PACK><<<(int)blocks, RS_THREADS, 0, st>>>(
+          static_cast<const v4u*>(w2_src), static_cast<v4u*>(w2_dst), sv, iv, H, n);
   }
   return hipGetLastError();
 }
