@@ -270,27 +270,52 @@ __global__ __launch_bounds__(256) void unpack_sum_kernel(const void* __restrict_
   }
   constexpr int EPV = 8;                            // columns per step (8 bf16 or 2 x 4 f32)
   const int nv = H / EPV;
+  // rows past n_rows repeat the last row's address (a valid one) and are not
+  // added, so that a group's loads need no branch (a load under a branch per
+  // row had waited for each row in turn)
+  int rr[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) rr[i] = i < n_rows ? rows[i] : last;   // last: the largest row
 #pragma unroll 2
   for (int c = threadIdx.x; c < nv; c += 256) {
     float acc[EPV];
 #pragma unroll
     for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
+    // rows in groups of 8: every load of a group is issued before its adds
+    constexpr int G = KP < 8 ? KP : 8;
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      if (i >= n_rows) break;
-      const int row = rows[i];
-      float v[EPV];
+    for (int g = 0; g < KP; g += G) {
+      if (g >= n_rows) break;
       if constexpr (IN_BF16) {
-        const uint4 raw = reinterpret_cast<const uint4*>(y_ret)[(size_t)row * nv + c];
-        unpack_bf16x8(raw, v);
-      } else {
-        const float4* p = reinterpret_cast<const float4*>(y_ret) + ((size_t)row * nv + c) * 2;
-        const float4 u0 = p[0], u1 = p[1];
-        v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
-        v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
-      }
+        uint4 raw[G];
 #pragma unroll
-      for (int q = 0; q < EPV; ++q) acc[q] += v[q];
+        for (int i = 0; i < G; ++i)
+          raw[i] = reinterpret_cast<const uint4*>(y_ret)[(size_t)rr[g + i] * nv + c];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          if (g + i < n_rows) {
+            float v[EPV];
+            unpack_bf16x8(raw[i], v);
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) acc[q] += v[q];
+          }
+        }
+      } else {
+        float4 u0[G], u1[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const float4* p = reinterpret_cast<const float4*>(y_ret) + ((size_t)rr[g + i] * nv + c) * 2;
+          u0[i] = p[0];
+          u1[i] = p[1];
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          if (g + i < n_rows) {
+            acc[0] += u0[i].x; acc[1] += u0[i].y; acc[2] += u0[i].z; acc[3] += u0[i].w;
+            acc[4] += u1[i].x; acc[5] += u1[i].y; acc[6] += u1[i].z; acc[7] += u1[i].w;
+          }
+        }
+      }
     }
     if constexpr (OUT_BF16) {
       reinterpret_cast<uint4*>(y)[(size_t)t * nv + c] =
