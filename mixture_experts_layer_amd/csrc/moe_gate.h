@@ -142,12 +142,24 @@ __device__ __forceinline__ void gate_row(const float (&s)[EPR], bool live, int s
                                 const float* __restrict__ sel_bias, int& id0, float& g0, int& id1,
                                 float& g1) {
   const bool sig = mode == 3;
+  // the selection bias is loaded for all slots before any key is formed: a
+  // load per slot under the mode's branch had waited for each slot in turn
+  float sb[EPR];
+#pragma unroll
+  for (int i = 0; i < EPR; ++i) sb[i] = 0.f;
+  if (sig && sel_bias) {
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) {
+      const int e = sub + 16 * i;
+      sb[i] = e < E ? sel_bias[e] : 0.f;
+    }
+  }
   unsigned long long cand[EPR];
 #pragma unroll
   for (int i = 0; i < EPR; ++i) {
     const int e = sub + 16 * i;
     const bool ok = live && e < E;
-    cand[i] = ok ? pack_key((sig && sel_bias) ? s[i] + sel_bias[e] : s[i], e) : 0ull;
+    cand[i] = ok ? pack_key((sig && sel_bias) ? s[i] + sb[i] : s[i], e) : 0ull;
   }
   unsigned long long c0 = 0ull, c1 = 0ull, first = 0ull;
   for (int r = 0; r < k; ++r) {
@@ -202,12 +214,22 @@ __device__ __forceinline__ void gate_select64(const float (&s64)[EPR64], bool li
                                               unsigned long long& first) {
   const int lane = threadIdx.x & 63, sub = lane & 15;
   const bool sig = mode == 3;
+  float sb[EPR64];                      // the selection bias, all loads first
+#pragma unroll
+  for (int i = 0; i < EPR64; ++i) sb[i] = 0.f;
+  if (sig && sel_bias) {
+#pragma unroll
+    for (int i = 0; i < EPR64; ++i) {
+      const int e = lane + 64 * i;
+      sb[i] = e < E ? sel_bias[e] : 0.f;
+    }
+  }
   unsigned long long cand[EPR64];
 #pragma unroll
   for (int i = 0; i < EPR64; ++i) {
     const int e = lane + 64 * i;
     const bool ok = live && e < E;
-    cand[i] = ok ? pack_key((sig && sel_bias) ? s64[i] + sel_bias[e] : s64[i], e) : 0ull;
+    cand[i] = ok ? pack_key((sig && sel_bias) ? s64[i] + sb[i] : s64[i], e) : 0ull;
   }
   c0 = c1 = first = 0ull;
   for (int r = 0; r < k; ++r) {
