@@ -3,6 +3,7 @@
 // metadata kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "moe_kernels.h"
@@ -77,6 +78,30 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Inclusive prefix sum over the 64 lanes of a wave: a Hillis-Steele scan
 // inside each 16-lane row by DPP row shifts (a lane with no source lane in
 // its row adds 0), then the totals of the rows below, read with readlane.
+// Sum over the 64 lanes of a wave, the same bits in every lane: DPP steps
+// inside each 16-lane row (pairs, quads, half-row and row mirrors), then the
+// rows' sums across row pairs and halves with v_permlane16_swap and
+// v_permlane32_swap.  Each step adds two values that the two lanes concerned
+// hold in opposite roles, and float addition is commutative, so no lane
+// disagrees; the order of the additions is fixed.
+__device__ __forceinline__ float wave_sum_f(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, x), decltype(ctrl)::value, 0xF,
+                                         0xF, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  v += dpp(v, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  v += dpp(v, std::integral_constant<int, 0x140>{});   // row_mirror
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
   v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2

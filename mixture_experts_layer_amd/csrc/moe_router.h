@@ -10,8 +10,9 @@ namespace moe {
 
 // Logits of tokens t0 .. t0 + nt - 1 (nt <= NTM <= 8) against expert e, computed by
 // the calling wave (all 64 lanes): lane l takes the 16-byte chunks l, l + 64,
-// ... of the H axis and accumulates them in H order with fmaf; a fixed xor
-// butterfly then sums the 64 lanes.  Lane 0 stores logits[t][e] (+ bias[e]).
+// ... of the H axis and accumulates them in H order with fmaf; wave_sum_f
+// then sums the 64 lanes in a fixed order.  Lane 0 stores logits[t][e]
+// (+ bias[e]).
 // The chunks are taken in groups, and a group's weight loads and every
 // token's loads are issued before the first multiply, so a group costs one
 // memory round trip: 8 chunks per group for a single token, GM for several
@@ -43,6 +44,7 @@ __device__ __forceinline__ void router_dot_wave(const Tin* __restrict__ x, const
   constexpr int VEC = 16 / sizeof(Tin);  // elements per 16-byte load
   const int lane = threadIdx.x & 63;
   const Tin* wrow = wr + (size_t)e * H;
+  const float bias_e = bias ? bias[e] : 0.f;   // loaded ahead of the dot products
   float acc[NTM];
 #pragma unroll
   for (int i = 0; i < NTM; ++i) acc[i] = 0.f;
@@ -85,11 +87,9 @@ __device__ __forceinline__ void router_dot_wave(const Tin* __restrict__ x, const
 #pragma unroll
   for (int i = 0; i < NTM; ++i) {
     if (i < nt) {
-      float v = acc[i];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      const float v = wave_sum_f(acc[i]);
       if (lane == 0) {
-        const float out = bias ? v + bias[e] : v;
+        const float out = bias ? v + bias_e : v;
         float* dst = logits + (size_t)(t0 + i) * E + e;
         if constexpr (COHERENT)
           __hip_atomic_store(reinterpret_cast<uint32_t*>(dst), __float_as_uint(out),
