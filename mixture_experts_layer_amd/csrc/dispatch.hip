@@ -86,12 +86,7 @@ __global__ __launch_bounds__(64) void pack_single_kernel(PackArgs a) {
     const unsigned long long b = __ballot((m >> r) & 1ull);
     if (t == r) cnt = __popcll(b);
   }
-  int inc = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inc, o);
-    if (t >= o) inc += u;
-  }
+  const int inc = wave_inclusive_scan(cnt);
   const int off = inc - cnt;
   if (t < a.P) {
     a.send_counts[t] = cnt;
@@ -100,7 +95,7 @@ __global__ __launch_bounds__(64) void pack_single_kernel(PackArgs a) {
   if (t == a.P - 1) a.send_offsets[a.P] = inc;
   for (int r = 0; r < a.P; ++r) {
     const unsigned long long b = __ballot((m >> r) & 1ull);
-    const int base = __shfl(off, r);
+    const int base = __builtin_amdgcn_readlane(off, r);
     if ((m >> r) & 1ull) tr.write_copy(a, t, r, base + __popcll(b & lanes_below()));
   }
 }
@@ -142,26 +137,16 @@ __global__ __launch_bounds__(1024) void pack_scan_kernel(PackArgs a) {
     for (int t0 = 0; t0 < n_tiles; t0 += 64) {
       const int tile = t0 + lane;
       const int c = tile < n_tiles ? a.tile_counts[(size_t)tile * a.P + r] : 0;
-      int inc = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(inc, o);
-        if (lane >= o) inc += u;
-      }
+      const int inc = wave_inclusive_scan(c);
       if (tile < n_tiles) a.tile_base[(size_t)tile * a.P + r] = carry + inc - c;
-      carry += __shfl(inc, 63);
+      carry += __builtin_amdgcn_readlane(inc, 63);
     }
     if (lane == 0) s_total[r] = carry;
   }
   __syncthreads();
   if (wid == 0) {
     const int c = lane < a.P ? s_total[lane] : 0;
-    int inc = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(inc, o);
-      if (lane >= o) inc += u;
-    }
+    const int inc = wave_inclusive_scan(c);
     if (lane < a.P) {
       a.send_counts[lane] = c;
       a.send_offsets[lane] = inc - c;
@@ -185,7 +170,7 @@ __global__ __launch_bounds__(256) void pack_scatter_kernel(PackArgs a) {
   const int rb = lane < a.P ? a.send_offsets[lane] + a.tile_base[(size_t)tile * a.P + lane] : 0;
   for (int r = 0; r < a.P; ++r) {
     const unsigned long long b = __ballot((m >> r) & 1ull);
-    const int base = __shfl(rb, r);
+    const int base = __builtin_amdgcn_readlane(rb, r);
     if ((m >> r) & 1ull) tr.write_copy(a, t, r, base + __popcll(b & lanes_below()));
   }
 }

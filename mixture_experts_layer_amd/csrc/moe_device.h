@@ -129,12 +129,7 @@ __device__ inline int block_exclusive_scan(int* data, int n, int* tmp) {
   int local = 0;
   for (int i = 0; i < per; ++i)
     if (b + i < n) local += data[b + i];
-  int v = local;  // inclusive scan inside the wave
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
+  const int v = wave_inclusive_scan(local);  // inclusive scan inside the wave
   if (lane == 63) tmp[wid] = v;
   lds_barrier();
   int wbase = 0, total = 0;
