@@ -37,14 +37,32 @@ struct TokenRoute {
   float w[KP];
   unsigned long long mask;   // destination ranks (ids outside [0, E) are not sent)
 
+  // k a multiple of 4 (every shape here): 16-byte loads and stores of the
+  // routing rows (the buffers are 16-byte aligned, rows k * 4 bytes long)
   __device__ __forceinline__ void load(const PackArgs& a, int t, bool live) {
     mask = 0ull;
+    if ((a.k & 3) == 0) {
 #pragma unroll
-    for (int j = 0; j < KP; ++j) {
-      id[j] = (live && j < a.k) ? a.ids[(size_t)t * a.k + j] : -1;
-      w[j] = (live && j < a.k && a.send_w) ? a.w[(size_t)t * a.k + j] : 0.f;
-      if (id[j] >= 0 && id[j] < a.E) mask |= 1ull << (id[j] / a.per);
+      for (int j = 0; j < KP; j += 4) {
+        int4 iv = make_int4(-1, -1, -1, -1);
+        float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live && j < a.k) {
+          iv = *reinterpret_cast<const int4*>(a.ids + (size_t)t * a.k + j);
+          if (a.send_w) wv = *reinterpret_cast<const float4*>(a.w + (size_t)t * a.k + j);
+        }
+        id[j] = iv.x; id[j + 1] = iv.y; id[j + 2] = iv.z; id[j + 3] = iv.w;
+        w[j] = wv.x; w[j + 1] = wv.y; w[j + 2] = wv.z; w[j + 3] = wv.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        id[j] = (live && j < a.k) ? a.ids[(size_t)t * a.k + j] : -1;
+        w[j] = (live && j < a.k && a.send_w) ? a.w[(size_t)t * a.k + j] : 0.f;
+      }
     }
+#pragma unroll
+    for (int j = 0; j < KP; ++j)
+      if (id[j] >= 0 && id[j] < a.E) mask |= 1ull << (id[j] / a.per);
   }
 
   // token t's copy to rank r at `row`: the token, its routing (all k slots,
@@ -52,14 +70,31 @@ struct TokenRoute {
   // slot the copy serves
   __device__ __forceinline__ void write_copy(const PackArgs& a, int t, int r, int row) const {
     a.send_token[row] = t;
+    if ((a.k & 3) == 0) {
 #pragma unroll
-    for (int j = 0; j < KP; ++j) {
-      if (j < a.k) {
-        if (a.send_ids) a.send_ids[(size_t)row * a.k + j] = id[j];
-        if (a.send_w) a.send_w[(size_t)row * a.k + j] = w[j];
-        if (id[j] >= 0 && id[j] < a.E && id[j] / a.per == r) a.send_row[(size_t)t * a.k + j] = row;
+      for (int j = 0; j < KP; j += 4) {
+        if (j < a.k) {
+          if (a.send_ids)
+            *reinterpret_cast<int4*>(a.send_ids + (size_t)row * a.k + j) =
+                make_int4(id[j], id[j + 1], id[j + 2], id[j + 3]);
+          if (a.send_w)
+            *reinterpret_cast<float4*>(a.send_w + (size_t)row * a.k + j) =
+                make_float4(w[j], w[j + 1], w[j + 2], w[j + 3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        if (j < a.k) {
+          if (a.send_ids) a.send_ids[(size_t)row * a.k + j] = id[j];
+          if (a.send_w) a.send_w[(size_t)row * a.k + j] = w[j];
+        }
       }
     }
+#pragma unroll
+    for (int j = 0; j < KP; ++j)
+      if (j < a.k && id[j] >= 0 && id[j] < a.E && id[j] / a.per == r)
+        a.send_row[(size_t)t * a.k + j] = row;
   }
 
   __device__ __forceinline__ void clear_rows(const PackArgs& a, int t) const {
