@@ -102,6 +102,15 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 #pragma unroll
   for (int i = 0; i < E / 16; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int lrow = lane & 15, kq = lane >> 4;
+  // this lane's four experts' bias per 16-expert group, loaded ahead of the
+  // K loop (loaded in the epilogue, under its branches, each had cost a wait)
+  float4 bv[E / 16];
+#pragma unroll
+  for (int nb = 0; nb < E / 16; ++nb) {
+    const int e = e0 + nb * 16 + 4 * kq;
+    bv[nb] = (bias && e < E_all) ? *reinterpret_cast<const float4*>(bias + e)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int nk = H / RT_K;
   issue(0, 0);
   if (nk > 1) issue(1, 1);
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
       if (e >= E_all) continue;                 // E is a multiple of 4
       float4 v = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
       if (bias) {
-        v.x += bias[e]; v.y += bias[e + 1]; v.z += bias[e + 2]; v.w += bias[e + 3];
+        v.x += bv[nb].x; v.y += bv[nb].y; v.z += bv[nb].z; v.w += bv[nb].w;
       }
       *reinterpret_cast<float4*>(logits + (size_t)t * E_all + e) = v;
     }
