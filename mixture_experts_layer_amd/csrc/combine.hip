@@ -26,6 +26,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  // the shared expert's row segment is loaded first: its latency overlaps
+  // the routing loads below instead of following the sum
+  uint4 sh_raw[OUT_BF16 ? 1 : 2];
+  if (y_shared) {
+    if (OUT_BF16) {
+      sh_raw[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(y_shared) +
+                                                  (size_t)t * H + c0);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(y_shared) +
+                                                      (size_t)t * H + c0);
+      sh_raw[0] = p[0];
+      sh_raw[OUT_BF16 ? 0 : 1] = p[1];
+    }
+  }
   // up to 8 permuted rows per batch: their loads are all in flight before the
   // first multiply-add; the sum still runs in slot order
   for (int j0 = 0; j0 < k; j0 += 8) {
@@ -71,15 +85,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   if (y_shared) {
     float v[8];
     if (OUT_BF16) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(
-          reinterpret_cast<const bf16_t*>(y_shared) + (size_t)t * H + c0);
-      unpack_bf16x8(raw, v);
+      unpack_bf16x8(sh_raw[0], v);
     } else {
-      const float4* p = reinterpret_cast<const float4*>(
-          reinterpret_cast<const float*>(y_shared) + (size_t)t * H + c0);
-      const float4 lo = p[0], hi = p[1];
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      const uint4 lo = sh_raw[0], hi = sh_raw[OUT_BF16 ? 0 : 1];
+      v[0] = __uint_as_float(lo.x); v[1] = __uint_as_float(lo.y);
+      v[2] = __uint_as_float(lo.z); v[3] = __uint_as_float(lo.w);
+      v[4] = __uint_as_float(hi.x); v[5] = __uint_as_float(hi.y);
+      v[6] = __uint_as_float(hi.z); v[7] = __uint_as_float(hi.w);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] += v[q];
