@@ -429,6 +429,11 @@ template <int N>
 __device__ __forceinline__ void wait_stage_barrier() {
   static_assert(N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+  // The same lgkmcnt(0) where the compiler can see it (a no-op at run time):
+  // its wait insertion does not read the asm, and believing an older scalar
+  // load still pending, it had made the stage's first MFMAs wait for every
+  // LDS read issued ahead of them instead of only their own.
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
 }
 
 // The down projection's bf16 output leaves through LDS: the block's finished
