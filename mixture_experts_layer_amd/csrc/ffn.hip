@@ -45,20 +45,51 @@ struct DirectArgs {
 //
 // SWIGLU: W rows [n] (gate) and [up_off + n] (up) are multiplied together and
 // the epilogue writes SiLU(gate) * up.
+//
+// Weight loads.  In the fragment layout a wave instruction reads 64 bytes of
+// each of 16 rows, so each group of 16 consecutive lanes touches 16
+// different cache lines.  Read as 8 rows x 128 bytes instead (8 consecutive
+// lanes on one line: two K steps of one row), the same weight stream ran 9%
+// faster at 2-8 rows per expert.  So when a load batch holds an even number
+// of K steps, each pair of steps is loaded that way and regrouped into
+// fragments through a small LDS area private to the wave.
 // ---------------------------------------------------------------------------
+// The regrouping area of one wave and (column tile, gate/up) holds two K
+// steps of 16 rows x 64 B: step t at byte 1152 t, row r at 64 r, its chunk
+// g at 16 (g ^ (r / 4 % 4)).  Each 16-lane quarter of a write (2 rows x 2
+// steps x 4 chunks) and of a fragment read (16 rows, one chunk) then covers
+// the 64 banks once.
+constexpr int XP_STEP = 1152 / 16;                  // in 16-byte units
+constexpr int XP_AREA = (1152 + 1024) / 16;
+
+__device__ __forceinline__ int xp_slot(int t, int row, int g) {
+  return t * XP_STEP + row * 4 + (g ^ ((row >> 2) & 3));
+}
+
+// K steps per load batch: about 24 16-byte loads in flight per wave
+template <int MT, int NT, bool SWIGLU>
+constexpr int direct_u() {
+  constexpr int lps = NT * (SWIGLU ? 2 : 1) + MT;      // loads per K step
+  return 24 / lps < 2 ? 2 : (24 / lps > 8 ? 8 : 24 / lps);
+}
+// 16-byte LDS units of a block's regrouping areas (0: fragment-layout loads)
+template <int MT, int NT, int NW, bool SWIGLU>
+constexpr int direct_xp_units() {
+  return direct_u<MT, NT, SWIGLU>() % 2 == 0 ? NW * NT * (SWIGLU ? 2 : 1) * XP_AREA : 0;
+}
+
 // Rows [r0, r1) (at most 16 * MT) of expert e against output columns
 // [n0, n0 + 16 * NT).
 template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
 __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, int r1, int n0,
-                                            float* red) {
+                                            float* red, uint4* xp_all) {
   constexpr int NS = SWIGLU ? 2 : 1;
   constexpr int BM = 16 * MT;
   constexpr int BN = 16 * NT;
   constexpr int NACC = MT * NT * NS;
   constexpr int PITCH = 65;
-  // K steps per load batch: about 24 16-byte loads in flight per wave
-  constexpr int LPS = NT * NS + MT;                     // loads per K step
-  constexpr int U = 24 / LPS < 2 ? 2 : (24 / LPS > 8 ? 8 : 24 / LPS);
+  constexpr int U = direct_u<MT, NT, SWIGLU>();
+  constexpr bool PAIRED = U % 2 == 0;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int kg = 8 * (lane >> 4);
 
@@ -98,6 +129,91 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
   const int s_begin = (S * wid) / NW;
   const int s_end = (S * (wid + 1)) / NW;
 
+  if constexpr (PAIRED) {
+    // lane i loads row 8 h + i / 8 of a 16-row tile: 16 bytes at 16 (i % 4)
+    // of step 2 p + (i / 4) % 2 of the batch (a step past the share re-reads
+    // the share's last step, as the activation loads do)
+    const int lt = (lane >> 2) & 1;
+    const bf16_t* wq[NT][NS];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + 16 * nt + (lane >> 3);
+      wq[nt][0] = We + (size_t)n * a.K + 8 * (lane & 3);
+      if (SWIGLU) wq[nt][NS - 1] = We + (size_t)(a.up_off + n) * a.K + 8 * (lane & 3);
+    }
+    const size_t half = (size_t)8 * a.K;
+    bf16x8_t* area = reinterpret_cast<bf16x8_t*>(xp_all) + wid * (NT * NS * XP_AREA);
+    int wi[2], ri[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) wi[h] = xp_slot(lt, 8 * h + (lane >> 3), lane & 3);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ri[t] = xp_slot(t, lane & 15, lane >> 4);
+
+    for (int s = s_begin; s < s_end; s += U) {
+      uint4 xa[U][MT];
+      bf16x8_t wv[U / 2][NT][NS][2];
+#pragma unroll
+      for (int p = 0; p < U / 2; ++p) {
+        const int ko = min(s + 2 * p + lt, s_end - 1) * 32;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int w = 0; w < NS; ++w)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              wv[p][nt][w][h] = *reinterpret_cast<const bf16x8_t*>(wq[nt][w] + h * half + ko);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ko = min(s + u, s_end - 1) * 32;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          xa[u][mt] = xv[mt] ? *reinterpret_cast<const uint4*>(xp[mt] + ko) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s + u >= s_end) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) xa[u][mt] = make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < U / 2; ++p) {
+        bf16x8_t f[NT][NS][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int w = 0; w < NS; ++w) {
+            bf16x8_t* ar = area + (nt * NS + w) * XP_AREA;
+            ar[wi[0]] = wv[p][nt][w][0];
+            ar[wi[1]] = wv[p][nt][w][1];
+          }
+        wave_lds_sync();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int w = 0; w < NS; ++w) {
+            const bf16x8_t* ar = area + (nt * NS + w) * XP_AREA;
+            f[nt][w][0] = ar[ri[0]];
+            f[nt][w][1] = ar[ri[1]];
+          }
+        wave_lds_sync();   // the next pair's writes stay behind these reads
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              acc[mt][nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  f[nt][0][t], as_bf16x8(xa[2 * p + t][mt]), acc[mt][nt][0], 0, 0, 0);
+              if (SWIGLU)
+                acc[mt][nt][NS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    f[nt][NS - 1][t], as_bf16x8(xa[2 * p + t][mt]), acc[mt][nt][NS - 1],
+                    0, 0, 0);
+            }
+      }
+    }
+  } else
   for (int s = s_begin; s < s_end; s += U) {
     uint4 xa[U][MT], wa[U][NT], wb[U][NT];
 #pragma unroll
@@ -206,7 +322,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
   constexpr int BM = 16 * MT;
   constexpr int BN = 16 * NT;
   constexpr int NACC = MT * NT * (SWIGLU ? 2 : 1);
+  constexpr int XPU = direct_xp_units<MT, NT, NW, SWIGLU>();
   __shared__ float red[NW > 1 ? NW * NACC * 4 * 65 : 1];
+  __shared__ uint4 xp_lds[XPU > 0 ? XPU : 1];
 
   const int n_ntiles = a.N_out / BN;
   const int tile = bid / n_ntiles;
@@ -222,11 +340,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
   }
   if constexpr (WALK) {
     for (int rs = r0; rs < r1; rs += BM) {
-      direct_rows<MT, NT, NW, SWIGLU, OUT_BF16>(a, e, rs, min(rs + BM, r1), ntile * BN, red);
+      direct_rows<MT, NT, NW, SWIGLU, OUT_BF16>(a, e, rs, min(rs + BM, r1), ntile * BN, red,
+                                                xp_lds);
       if (NW > 1) __syncthreads();    // red is written again by the next rows
     }
   } else {
-    direct_rows<MT, NT, NW, SWIGLU, OUT_BF16>(a, e, r0, r1, ntile * BN, red);
+    direct_rows<MT, NT, NW, SWIGLU, OUT_BF16>(a, e, r0, r1, ntile * BN, red, xp_lds);
   }
 }
 
@@ -1006,8 +1125,7 @@ constexpr int DIRECT_NT16 = 1, DIRECT_NT32 = 2, DIRECT_NT64 = 2;
 
 template <int MT, int NT, bool SWIGLU>
 constexpr int direct_batch() {
-  constexpr int lps = NT * (SWIGLU ? 2 : 1) + MT;
-  return 24 / lps < 2 ? 2 : (24 / lps > 8 ? 8 : 24 / lps);
+  return direct_u<MT, NT, SWIGLU>();
 }
 
 // Waves per block of the direct kernel for a row tile and contraction.
