@@ -55,15 +55,14 @@ struct DirectArgs {
 // fragments through a small LDS area private to the wave.
 // ---------------------------------------------------------------------------
 // The regrouping area of one wave and (column tile, gate/up) holds two K
-// steps of 16 rows x 64 B: step t at byte 1152 t, row r at 64 r, its chunk
-// g at 16 (g ^ (r / 4 % 4)).  Each 16-lane quarter of a write (2 rows x 2
-// steps x 4 chunks) and of a fragment read (16 rows, one chunk) then covers
-// the 64 banks once.
-constexpr int XP_STEP = 1152 / 16;                  // in 16-byte units
-constexpr int XP_AREA = (1152 + 1024) / 16;
+// steps of 16 rows x 64 B: step t at byte 1024 t, row r in the 64-byte slot
+// (r + 2 t) % 16, its chunk g at 16 (g ^ (r / 4 % 4)).  Each 16-lane quarter
+// of a write (2 rows x 2 steps x 4 chunks) and of a fragment read (16 rows,
+// one chunk) then covers the 64 banks once.
+constexpr int XP_AREA = 2048 / 16;                  // in 16-byte units
 
 __device__ __forceinline__ int xp_slot(int t, int row, int g) {
-  return t * XP_STEP + row * 4 + (g ^ ((row >> 2) & 3));
+  return t * 64 + ((row + 2 * t) & 15) * 4 + (g ^ ((row >> 2) & 3));
 }
 
 // K steps per load batch: about 24 16-byte loads in flight per wave
@@ -359,9 +358,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
 // (global -> LDS, one 1 KB fragment per K step of 32), and each wave streams
 // only its own weight rows into MFMA fragments.  Each wave sums its whole
 // contraction, so no partial sums meet; a wave whose column tile is past the
-// output width only helps with the activation loads.  The LDS holds exactly
-// the K / 32 fragments (1 KB each), so a short contraction leaves room for
-// more blocks per CU, and more weight streams in flight.
+// output width only helps with the activation loads.  The weights are read
+// in step pairs and regrouped as in direct_rows (2 KB of LDS per wave).
+// Beyond that the LDS holds exactly the K / 32 fragments (1 KB each), so a
+// short contraction leaves room for more blocks per CU, and more weight
+// streams in flight.
 // ---------------------------------------------------------------------------
 constexpr int DCOLS_WAVES = 8;       // column tiles per block
 constexpr int DCOLS_MAX_K = 2048;    // activation fragments held in LDS (64 KB)
@@ -377,6 +378,7 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
   const DirectArgs a = second ? a1 : a0;
   const int bid = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
   extern __shared__ __attribute__((aligned(16))) uint4 s_x[];   // [K / 32][64]
+  __shared__ bf16x8_t s_xp[DCOLS_WAVES * XP_AREA];               // regrouping areas
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n_ct = a.N_out / 16;
   const int n_cb = (n_ct + DCOLS_WAVES - 1) / DCOLS_WAVES;
@@ -407,15 +409,27 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
   const int ct = cb * DCOLS_WAVES + wid;
   const bool live = ct < n_ct;
   const int n0 = 16 * (live ? ct : 0);
+  // weight step pairs as in direct_rows: lane i reads row 8 h + i / 8 of the
+  // column tile, 16 bytes at 16 (i % 4) of step (i / 4) % 2 of the pair (a
+  // step past the end re-reads the last one and is not multiplied), then the
+  // pair is regrouped into fragments through this wave's LDS area
+  const int lt = (lane >> 2) & 1;
   const bf16_t* wp =
-      a.W + (size_t)e * a.w_stride + (size_t)(n0 + (lane & 15)) * a.K + 8 * (lane >> 4);
+      a.W + (size_t)e * a.w_stride + (size_t)(n0 + (lane >> 3)) * a.K + 8 * (lane & 3);
+  const size_t half = (size_t)8 * a.K;
+  bf16x8_t* area = s_xp + wid * XP_AREA;
+  const int wi0 = xp_slot(lt, lane >> 3, lane & 3), wi1 = xp_slot(lt, 8 + (lane >> 3), lane & 3);
+  const int ri0 = xp_slot(0, lane & 15, lane >> 4), ri1 = xp_slot(1, lane & 15, lane >> 4);
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += U) {
-    uint4 wv[U];
+    bf16x8_t wv[U / 2][2];
     if (live) {
 #pragma unroll
-      for (int q = 0; q < U; ++q)
-        if (s0 + q < S) wv[q] = *reinterpret_cast<const uint4*>(wp + 32 * (s0 + q));
+      for (int p = 0; p < U / 2; ++p) {
+        const int ko = min(s0 + 2 * p + lt, S - 1) * 32;
+        wv[p][0] = *reinterpret_cast<const bf16x8_t*>(wp + ko);
+        wv[p][1] = *reinterpret_cast<const bf16x8_t*>(wp + half + ko);
+      }
     }
     if (s0 == 0) {
       // every wave's activation loads (and its first weight batch) have
@@ -425,11 +439,20 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
     }
     if (live) {
 #pragma unroll
-      for (int q = 0; q < U; ++q)
-        if (s0 + q < S)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[q]),
-                                                        as_bf16x8(s_x[(s0 + q) * 64 + lane]), acc, 0,
-                                                        0, 0);
+      for (int p = 0; p < U / 2; ++p) {
+        const int sp = s0 + 2 * p;
+        if (sp >= S) break;
+        area[wi0] = wv[p][0];
+        area[wi1] = wv[p][1];
+        wave_lds_sync();
+        const bf16x8_t f0 = area[ri0], f1 = area[ri1];
+        wave_lds_sync();   // the next pair's writes stay behind these reads
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, as_bf16x8(s_x[sp * 64 + lane]), acc, 0,
+                                                      0, 0);
+        if (sp + 1 < S)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              f1, as_bf16x8(s_x[(sp + 1) * 64 + lane]), acc, 0, 0, 0);
+      }
     }
   }
   if (!live) return;
