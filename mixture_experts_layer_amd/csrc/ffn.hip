@@ -599,7 +599,7 @@ struct TileOut {
 // BUF: operands reach LDS by raw-buffer loads (X and each expert's weights
 // within 4 GiB); otherwise by global loads from 64-bit per-lane pointers.
 // As in the direct kernel, blocks [0, grid0) take a0 and the rest a1.
-template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
+template <class C, bool SWIGLU, bool OUT_BF16, bool BUF, bool LS = false>
 __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0, TileArgs a1,
                                                                     int grid0) {
   const bool second = (int)blockIdx.x >= grid0;
@@ -697,21 +697,61 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
   const uint32_t x_nbytes = (uint32_t)a.x_bytes;
   const uint32_t w_nbytes = (uint32_t)(a.w_stride * 2);
   const int wid_u = __builtin_amdgcn_readfirstlane(wid);
-  // mode 0: full tile, 1: half tile, 2: wide half tile
-  auto issue = [&](int ks, int buf, auto mode_c) {
+  // LS: of the two waves on a SIMD (w and w ^ NWAVE/2), one issues both
+  // waves' operand loads and the other issues none, so that one of them
+  // always has MFMAs to issue while the other is held up issuing loads (a
+  // timing copy whose loads were never waited for had run no faster than the
+  // kernel: the cost sat in issuing and moving them, not in waiting).  In
+  // full and wide tiles waves [0, NWAVE/2) load; in half tiles the waves
+  // that own the empty upper rows (and compute nothing) load.
+  constexpr bool LSX = LS && BUF && C::NWAVE == 8;
+  constexpr int HW = C::NWAVE / 2;
+  uint32_t xo1[LSX ? C::XLOADS : 1], wo1[LSX ? WLA : 1];
+  if constexpr (LSX) {
+    const int pw = wid ^ HW;
+#pragma unroll
+    for (int j = 0; j < C::XLOADS; ++j) {
+      const int rt = (pw + C::NWAVE * j) * C::RPI + prow;
+      int row = r0 + rt;
+      if (row >= r1) row = r0;
+      const int src = a.src_token ? max(a.src_token[row], 0) : row;
+      xo1[j] = (uint32_t)(((size_t)src * a.K + (pchunk ^ tile_swz<C>(rt)) * 8) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < WLA; ++j) {
+      const int rt = (pw + C::NWAVE * j) * C::RPI + prow;
+      int wrow;
+      if (SWIGLU) wrow = rt < gate_rows ? n0 + rt : a.up_off + n0 + (rt - gate_rows);
+      else wrow = n0 + rt;
+      if (j >= C::WLOADS && !wide) wrow = n0;           // unused
+      wo1[j] = (uint32_t)(((size_t)wrow * a.K + (pchunk ^ tile_swz<C>(rt)) * 8) * 2);
+    }
+  }
+  // mode 0: full tile, 1: half tile, 2: wide half tile; role 0: this wave's
+  // share, 1: this wave's and its partner's, 2: none
+  auto issue = [&](int ks, int buf, auto mode_c, auto role_c) {
     constexpr int MODE = decltype(mode_c)::value;
+    constexpr int ROLE = decltype(role_c)::value;
     constexpr int XL = MODE == 0 ? C::XLOADS : C::XLOADS_H;
     constexpr int WL = MODE == 2 ? C::WLOADS_W : C::WLOADS;
+    if constexpr (ROLE == 2) return;
     unsigned char* sx = smem + buf * C::SSTRIDE;
     unsigned char* sw = sx + (MODE == 2 ? C::XBYTES / 2 : C::XBYTES);
     if constexpr (BUF) {
       const uint32_t soff = (uint32_t)ks * (C::TK * 2);
+      const int pw_u = wid_u ^ HW;
 #pragma unroll
-      for (int j = 0; j < XL; ++j)
+      for (int j = 0; j < XL; ++j) {
         buffer_load_lds16(a.X, x_nbytes, sx + (wid_u + C::NWAVE * j) * 1024, xo[j], soff);
+        if constexpr (ROLE == 1)
+          buffer_load_lds16(a.X, x_nbytes, sx + (pw_u + C::NWAVE * j) * 1024, xo1[j], soff);
+      }
 #pragma unroll
-      for (int j = 0; j < WL; ++j)
+      for (int j = 0; j < WL; ++j) {
         buffer_load_lds16(We, w_nbytes, sw + (wid_u + C::NWAVE * j) * 1024, wo[j], soff);
+        if constexpr (ROLE == 1)
+          buffer_load_lds16(We, w_nbytes, sw + (pw_u + C::NWAVE * j) * 1024, wo1[j], soff);
+      }
     } else {
       const int ko = ks * C::TK;
 #pragma unroll
@@ -779,12 +819,14 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
   // One stage loop, instantiated for full tiles, for the computing waves of
   // half tiles, for their idle waves and for wide half tiles; the choice is
   // made once per wave.
-  auto stage_loop = [&](auto mode_c, auto compute_c) {
+  auto stage_loop = [&](auto mode_c, auto compute_c, auto role_c) {
   constexpr int MODE = decltype(mode_c)::value;
-  constexpr int NL = MODE == 0 ? C::NLOADS : MODE == 1 ? C::NLOADS_H : C::NLOADS_W;
+  constexpr int ROLE = decltype(role_c)::value;
+  constexpr int NL1 = MODE == 0 ? C::NLOADS : MODE == 1 ? C::NLOADS_H : C::NLOADS_W;
+  constexpr int NL = ROLE == 0 ? NL1 : ROLE == 1 ? 2 * NL1 : 0;   // this wave's loads per stage
 #pragma unroll
   for (int s0 = 0; s0 < C::STAGES - 1; ++s0)
-    if (s0 < nk) issue(s0, s0, mode_c);
+    if (s0 < nk) issue(s0, s0, mode_c, role_c);
   for (int ks = 0; ks < nk; ++ks) {
     // Stage ks has landed for this wave once at most the loads of the
     // STAGES-2 younger stages are outstanding; the barrier makes that true
@@ -800,7 +842,8 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
       case 3: wait_stage_barrier<(C::STAGES > 4 ? 3 : 1) * NL>(); break;
       default: wait_stage_barrier<(C::STAGES > 5 ? 4 : 1) * NL>(); break;
     }
-    if (ks + C::STAGES - 1 < nk) issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES, mode_c);
+    if (ks + C::STAGES - 1 < nk)
+      issue(ks + C::STAGES - 1, (ks + C::STAGES - 1) % C::STAGES, mode_c, role_c);
     if constexpr (!decltype(compute_c)::value) continue;
     const unsigned char* sx = smem + (ks % C::STAGES) * C::SSTRIDE;
     const unsigned char* sw = sx + (MODE == 2 ? C::XBYTES / 2 : C::XBYTES);
@@ -824,15 +867,38 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
   using Full = std::integral_constant<int, 0>;
   using Half = std::integral_constant<int, 1>;
   using Wide = std::integral_constant<int, 2>;
-  if constexpr (C::WIDE) {
-    if (wide) stage_loop(Wide{}, std::true_type{});
-    else if (!half) stage_loop(Full{}, std::true_type{});
-    else if (!idle) stage_loop(Half{}, std::true_type{});
-    else stage_loop(Half{}, std::false_type{});
+  using Own = std::integral_constant<int, 0>;
+  using Both = std::integral_constant<int, 1>;
+  using None = std::integral_constant<int, 2>;
+  if constexpr (LSX) {
+    const bool lo = wid < HW;
+    bool done = false;
+    if constexpr (C::WIDE) {
+      if (wide) {
+        if (lo) stage_loop(Wide{}, std::true_type{}, Both{});
+        else stage_loop(Wide{}, std::true_type{}, None{});
+        done = true;
+      }
+    }
+    if (!done) {
+      if (!half) {
+        if (lo) stage_loop(Full{}, std::true_type{}, Both{});
+        else stage_loop(Full{}, std::true_type{}, None{});
+      } else if (!idle) {
+        stage_loop(Half{}, std::true_type{}, None{});
+      } else {
+        stage_loop(Half{}, std::false_type{}, Both{});
+      }
+    }
+  } else if constexpr (C::WIDE) {
+    if (wide) stage_loop(Wide{}, std::true_type{}, Own{});
+    else if (!half) stage_loop(Full{}, std::true_type{}, Own{});
+    else if (!idle) stage_loop(Half{}, std::true_type{}, Own{});
+    else stage_loop(Half{}, std::false_type{}, Own{});
   } else {
-    if (!half) stage_loop(Full{}, std::true_type{});
-    else if (!idle) stage_loop(Half{}, std::true_type{});
-    else stage_loop(Half{}, std::false_type{});
+    if (!half) stage_loop(Full{}, std::true_type{}, Own{});
+    else if (!idle) stage_loop(Half{}, std::true_type{}, Own{});
+    else stage_loop(Half{}, std::false_type{}, Own{});
   }
 
   // ---- epilogue
@@ -1041,20 +1107,31 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
 
 static bool is_tile_bm(int BM) { return BM == TileBig::TM || BM == TileMed::TM; }
 
-template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
-static hipError_t launch_tile_buf(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
-                                  hipStream_t st) {
+template <class C, bool SWIGLU, bool OUT_BF16, bool BUF, bool LS>
+static hipError_t launch_tile_ls(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
+                                 hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t err = ensure_lds_limit(
-      reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF>),
+      reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF, LS>),
       TileOut<C, SWIGLU, OUT_BF16>::LDS, lds_set);
   if (err != hipSuccess) return err;
   constexpr int cols = SWIGLU ? C::TN / 2 : C::TN;
   const int grid0 = max_tiles * (a.N_out / cols);
   const int grid1 = b ? b_tiles * (b->N_out / cols) : 0;
-  ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF>
+  ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF, LS>
       <<<grid0 + grid1, C::NTHR, TileOut<C, SWIGLU, OUT_BF16>::LDS, st>>>(a, b ? *b : a, grid0);
   return hipGetLastError();
+}
+
+// The two-stage 256-row tiles load through one wave per SIMD (LS): Qwen3
+// shape T = 8192, gate/up GEMM 1.648 -> 1.591 ms and down 0.961 -> 0.945 ms,
+// Mixtral T = 4096 layer 2.89 -> 2.78 ms (same box, alternating runs).  The
+// three-stage 128-row tiles measured the same or 1-2% slower with it.
+template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
+static hipError_t launch_tile_buf(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
+                                  hipStream_t st) {
+  constexpr bool LS = BUF && C::NWAVE == 8 && C::STAGES == 2;
+  return launch_tile_ls<C, SWIGLU, OUT_BF16, BUF, LS>(a, max_tiles, b, b_tiles, st);
 }
 
 // Raw-buffer loads (no vector address arithmetic per load: the gate/up GEMM
