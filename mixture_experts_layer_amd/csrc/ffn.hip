@@ -16,6 +16,23 @@
 
 namespace moe {
 
+// 16 bytes of a weight stream that no other block reads again: a
+// non-temporal load (the nt cache-policy bit).  In the direct-load kernels
+// below, at decode-sized batches where every weight byte is read by exactly
+// one block, it ran the HBM-bound expert GEMMs 8-10% faster than plain
+// loads.  The LDS-tiled prefill GEMMs reuse weight tiles across an expert's
+// row tiles through the L2 and must not use it (nt on their LDS-DMA loads
+// doubled their time); the single-launch decode kernel measured 5-7% slower
+// with it.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t ld_stream16(const void* p) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(static_cast<const u32x4_t*>(p)));
+}
+__device__ __forceinline__ uint4 ld_stream16_u4(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 struct DirectArgs {
   const bf16_t* X;          // activation rows, K contiguous
   const int32_t* src_token; // null: row r reads X row r; else X row src_token[r]
@@ -160,7 +177,7 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
           for (int w = 0; w < NS; ++w)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-              wv[p][nt][w][h] = *reinterpret_cast<const bf16x8_t*>(wq[nt][w] + h * half + ko);
+              wv[p][nt][w][h] = ld_stream16(wq[nt][w] + h * half + ko);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -220,8 +237,8 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
       const int ko = min(s + u, s_end - 1) * 32;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        wa[u][nt] = *reinterpret_cast<const uint4*>(wg[nt] + ko);
-        if (SWIGLU) wb[u][nt] = *reinterpret_cast<const uint4*>(wu[nt] + ko);
+        wa[u][nt] = ld_stream16_u4(wg[nt] + ko);
+        if (SWIGLU) wb[u][nt] = ld_stream16_u4(wu[nt] + ko);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -427,8 +444,8 @@ __global__ __launch_bounds__(DCOLS_WAVES * 64) void ffn_direct_cols_kernel(Direc
 #pragma unroll
       for (int p = 0; p < U / 2; ++p) {
         const int ko = min(s0 + 2 * p + lt, S - 1) * 32;
-        wv[p][0] = *reinterpret_cast<const bf16x8_t*>(wp + ko);
-        wv[p][1] = *reinterpret_cast<const bf16x8_t*>(wp + half + ko);
+        wv[p][0] = ld_stream16(wp + ko);
+        wv[p][1] = ld_stream16(wp + half + ko);
       }
     }
     if (s0 == 0) {
