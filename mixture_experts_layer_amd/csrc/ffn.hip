@@ -570,12 +570,13 @@ struct TileCfg {
 // raw-buffer load of a buffer of nbytes: the address is a scalar base, one
 // 32-bit lane offset and a scalar step, so a load costs no vector
 // instructions; bytes past nbytes read as zero.
+template <int AUX = 0>
 __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t nbytes, void* lds,
                                                   uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, AUX);
 #endif
 }
 
@@ -616,7 +617,10 @@ struct TileOut {
 // BUF: operands reach LDS by raw-buffer loads (X and each expert's weights
 // within 4 GiB); otherwise by global loads from 64-bit per-lane pointers.
 // As in the direct kernel, blocks [0, grid0) take a0 and the rest a1.
-template <class C, bool SWIGLU, bool OUT_BF16, bool BUF, bool LS = false>
+// WNT: weight loads with the non-temporal hint (aux 2 = nt on gfx950), for
+// launches whose experts fill about one row tile each, so that no other
+// block of the launch reads a weight tile again.
+template <class C, bool SWIGLU, bool OUT_BF16, bool BUF, bool LS = false, bool WNT = false>
 __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0, TileArgs a1,
                                                                     int grid0) {
   const bool second = (int)blockIdx.x >= grid0;
@@ -765,9 +769,11 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
       }
 #pragma unroll
       for (int j = 0; j < WL; ++j) {
-        buffer_load_lds16(We, w_nbytes, sw + (wid_u + C::NWAVE * j) * 1024, wo[j], soff);
+        buffer_load_lds16<WNT ? 2 : 0>(We, w_nbytes, sw + (wid_u + C::NWAVE * j) * 1024, wo[j],
+                                       soff);
         if constexpr (ROLE == 1)
-          buffer_load_lds16(We, w_nbytes, sw + (pw_u + C::NWAVE * j) * 1024, wo1[j], soff);
+          buffer_load_lds16<WNT ? 2 : 0>(We, w_nbytes, sw + (pw_u + C::NWAVE * j) * 1024, wo1[j],
+                                         soff);
       }
     } else {
       const int ko = ks * C::TK;
@@ -1124,18 +1130,18 @@ int ffn_row_tile(int dt, int mean_rows, int H, int I_loc, int experts) {
 
 static bool is_tile_bm(int BM) { return BM == TileBig::TM || BM == TileMed::TM; }
 
-template <class C, bool SWIGLU, bool OUT_BF16, bool BUF, bool LS>
+template <class C, bool SWIGLU, bool OUT_BF16, bool BUF, bool LS, bool WNT>
 static hipError_t launch_tile_ls(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
                                  hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t err = ensure_lds_limit(
-      reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF, LS>),
+      reinterpret_cast<const void*>(&ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF, LS, WNT>),
       TileOut<C, SWIGLU, OUT_BF16>::LDS, lds_set);
   if (err != hipSuccess) return err;
   constexpr int cols = SWIGLU ? C::TN / 2 : C::TN;
   const int grid0 = max_tiles * (a.N_out / cols);
   const int grid1 = b ? b_tiles * (b->N_out / cols) : 0;
-  ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF, LS>
+  ffn_tile_kernel<C, SWIGLU, OUT_BF16, BUF, LS, WNT>
       <<<grid0 + grid1, C::NTHR, TileOut<C, SWIGLU, OUT_BF16>::LDS, st>>>(a, b ? *b : a, grid0);
   return hipGetLastError();
 }
@@ -1144,11 +1150,23 @@ static hipError_t launch_tile_ls(const TileArgs& a, int max_tiles, const TileArg
 // shape T = 8192, gate/up GEMM 1.648 -> 1.591 ms and down 0.961 -> 0.945 ms,
 // Mixtral T = 4096 layer 2.89 -> 2.78 ms (same box, alternating runs).  The
 // three-stage 128-row tiles measured the same or 1-2% slower with it.
+// Three-stage tiles (128 rows) of a launch whose experts hold fewer rows than
+// one tile on average (mean_rows < TM) load their weights non-temporally: the
+// Qwen3 EP view at T = 128, 256 and 1024 ran 4-8% faster and Mixtral T = 256
+// about 3% (same box, alternating runs).  With 128 or more rows per expert
+// (DeepSeek-V3 T = 4096) an expert's row tiles share weight tiles through the
+// L2, and the hint measured the same or slower there.
 template <class C, bool SWIGLU, bool OUT_BF16, bool BUF>
 static hipError_t launch_tile_buf(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
-                                  hipStream_t st) {
+                                  int mean_rows, hipStream_t st) {
   constexpr bool LS = BUF && C::NWAVE == 8 && C::STAGES == 2;
-  return launch_tile_ls<C, SWIGLU, OUT_BF16, BUF, LS>(a, max_tiles, b, b_tiles, st);
+  if constexpr (BUF && C::STAGES == 3) {
+    // (not with a second problem riding along: the shared expert's dense
+    // rows reuse its weight tiles)
+    if (mean_rows < C::TM && !b)
+      return launch_tile_ls<C, SWIGLU, OUT_BF16, BUF, LS, true>(a, max_tiles, b, b_tiles, st);
+  }
+  return launch_tile_ls<C, SWIGLU, OUT_BF16, BUF, LS, false>(a, max_tiles, b, b_tiles, st);
 }
 
 // Raw-buffer loads (no vector address arithmetic per load: the gate/up GEMM
@@ -1161,10 +1179,11 @@ static bool tile_buf_ok(const TileArgs& a) {
 
 template <class C, bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_tile_cfg(const TileArgs& a, int max_tiles, const TileArgs* b, int b_tiles,
-                                  hipStream_t st) {
+                                  int mean_rows, hipStream_t st) {
   const bool buf = tile_buf_ok(a) && (!b || tile_buf_ok(*b));
-  if (buf) return launch_tile_buf<C, SWIGLU, OUT_BF16, true>(a, max_tiles, b, b_tiles, st);
-  return launch_tile_buf<C, SWIGLU, OUT_BF16, false>(a, max_tiles, b, b_tiles, st);
+  if (buf)
+    return launch_tile_buf<C, SWIGLU, OUT_BF16, true>(a, max_tiles, b, b_tiles, mean_rows, st);
+  return launch_tile_buf<C, SWIGLU, OUT_BF16, false>(a, max_tiles, b, b_tiles, mean_rows, st);
 }
 
 // N-tiles per group.  One N-tile per group (all M-tiles of an expert that
@@ -1187,12 +1206,14 @@ static hipError_t launch_tile(TileArgs a, int BM, int mean_rows, int max_tiles, 
   const int ntn = a.N_out / (SWIGLU ? TL_N / 2 : TL_N);
   a.group = tile_group(mean_rows, BM, ntn);
   switch (tile_shape(BM, SWIGLU, a.N_out)) {
-    case TILE_BIG: return launch_tile_cfg<TileBig, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    case TILE_BIG:
+      return launch_tile_cfg<TileBig, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, mean_rows, st);
     case TILE_NARROW:
       if constexpr (SWIGLU)
-        return launch_tile_cfg<TileNarrow, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+        return launch_tile_cfg<TileNarrow, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, mean_rows, st);
       [[fallthrough]];
-    default: return launch_tile_cfg<TileMed, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    default:
+      return launch_tile_cfg<TileMed, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, mean_rows, st);
   }
 }
 

@@ -20,7 +20,9 @@
 // consecutive W2 row segments of s elements), all of a batch's loads before
 // its stores.  The layout arithmetic is done once per block (and per thread
 // for W2), not per vector with four integer divisions as in the first
-// version (1-3% faster).
+// version (1-3% faster).  Every byte is read once and written once, so the
+// loads and stores carry the non-temporal hint: 0.65 -> 0.72 of HBM for one
+// Qwen3 rank share (pack 232 -> 205 us, interleave 229 -> 209 us).
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -53,10 +55,10 @@ __global__ __launch_bounds__(RS_THREADS) void reshard_w13_kernel(const v4u* __re
   for (int v0 = threadIdx.x; v0 < hv; v0 += RS_THREADS * RS_BATCH) {
     v4u v[RS_BATCH];
 #pragma unroll
-    for (int u = 0; u < RS_BATCH; ++u) v[u] = sp[min(v0 + u * RS_THREADS, hv - 1)];
+    for (int u = 0; u < RS_BATCH; ++u) v[u] = __builtin_nontemporal_load(&sp[min(v0 + u * RS_THREADS, hv - 1)]);
 #pragma unroll
     for (int u = 0; u < RS_BATCH; ++u)
-      if (v0 + u * RS_THREADS < hv) dp[v0 + u * RS_THREADS] = v[u];
+      if (v0 + u * RS_THREADS < hv) __builtin_nontemporal_store(v[u], &dp[v0 + u * RS_THREADS]);
   }
 }
 
@@ -98,10 +100,10 @@ __global__ __launch_bounds__(RS_THREADS) void reshard_w2_kernel(const v4u* __res
     v4u v[RS_BATCH];
 #pragma unroll
     for (int u = 0; u < RS_BATCH; ++u)
-      if (u < nb) v[u] = src[PACK ? es[u] : cs[u]];
+      if (u < nb) v[u] = __builtin_nontemporal_load(&src[PACK ? es[u] : cs[u]]);
 #pragma unroll
     for (int u = 0; u < RS_BATCH; ++u)
-      if (u < nb) dst[PACK ? cs[u] : es[u]] = v[u];
+      if (u < nb) __builtin_nontemporal_store(v[u], &dst[PACK ? cs[u] : es[u]]);
   }
 }
 
