@@ -398,7 +398,7 @@ int moe_layer_status(void* ws, size_t ws_bytes, void* stream);
 /* The layer share, choosing the single-launch decode path (moe_layer_decode)
  * for shapes it supports while the expert weights the call can touch
  * (min(E_loc, T*k) routed experts plus the shared one, bf16) are at most
- * 512 MB, and the staged path (moe_layer_staged) otherwise.  Both compute the same function; they
+ * 100 MB, and the staged path (moe_layer_staged) otherwise.  Both compute the same function; they
  * differ in rounding only (the staged path rounds each expert's output to
  * dtype dt before the combine, the decode path keeps it in float32). */
 int moe_layer(const moe_layer_desc* d, int T, const void* x, void* y,

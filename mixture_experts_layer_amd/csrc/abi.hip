@@ -158,9 +158,11 @@ bool decode_shape_ok(const moe_layer_desc* d, int T) {
 // moe_layer takes the single-launch path while the expert weights a call can
 // touch -- min(E_loc, T*k) routed experts plus the shared one -- stay under
 // this many bytes: there the launch and dependency chain of the staged path
-// costs more than the single launch's lower streaming rate (measured
-// crossover on MI355X between about 0.3 and 0.6 GB).
-constexpr double DECODE_AUTO_BYTES = 512e6;
+// costs more than the single launch's lower streaming rate.  Measured
+// crossover on MI355X, since the staged path's direct GEMMs stream their
+// weights non-temporally: between 75 MB (Qwen3 TP share T = 2: 35.7 µs
+// staged, 35.1 µs single-launch) and 151 MB (T = 4: 47.8 against 50.3 µs).
+constexpr double DECODE_AUTO_BYTES = 100e6;
 
 bool decode_preferred(const moe_layer_desc* d, int T) {
   const int E_loc = d->e_end - d->e_begin;

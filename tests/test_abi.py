@@ -176,11 +176,13 @@ def test_layer_path_choice():
         base.update(kw)
         return M.MoELayerDesc(**base)
     tp = desc()                                   # tensor-parallel share: 4.7 MB per expert
-    # 13 * 8 experts * 4.72 MB = 491 MB; 14 * 8 * 4.72 MB = 528 MB
-    assert [M.moe_layer_path(tp, T) for T in (1, 8, 13, 14, 64, 65)] == \
-        ["decode", "decode", "decode", "staged", "staged", "staged"]
+    # 2 * 8 experts * 4.72 MB = 75.5 MB; 3 * 8 * 4.72 MB = 113 MB (limit 100 MB)
+    assert [M.moe_layer_path(tp, T) for T in (1, 2, 3, 8, 64, 65)] == \
+        ["decode", "decode", "staged", "staged", "staged", "staged"]
     ep = desc(I_loc=1536)                         # whole experts: 37.7 MB each
-    assert [M.moe_layer_path(ep, T) for T in (1, 2)] == ["decode", "staged"]
+    assert [M.moe_layer_path(ep, T) for T in (1, 2)] == ["staged", "staged"]
+    small = desc(I_loc=1536, H=1024)              # 9.4 MB per expert: 8 experts = 75.5 MB
+    assert [M.moe_layer_path(small, T) for T in (1, 2)] == ["decode", "staged"]
     assert M.moe_layer_path(desc(dt=0), 1) == "staged"        # float32 layers
     assert M.moe_layer_path(tp, 0) == "staged"
     with pytest.raises(M.MoEError):

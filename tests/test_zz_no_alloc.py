@@ -29,7 +29,7 @@ def _static_run(gl, T):
 # (workload, reduced sizes or None, T first, T second): the two calls take the
 # staged path then the single-launch one (Qwen3 TP share), or both the
 # staged path with a shared expert (DeepSeek-V3-shaped, reduced)
-CASES = [("qwen3_tp8_rank0", None, 64, 8),
+CASES = [("qwen3_tp8_rank0", None, 64, 2),
          ("deepseek_v3", dict(H=1024, I=256, E=64), 300, 37)]
 
 
