@@ -404,8 +404,16 @@ __global__ __launch_bounds__(GateWaves<EPR>::value * 64) void gate_tile_kernel(G
 hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, int H, int E,
                                 const float* bias, float* logits, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  // bf16 prefill batches with E a multiple of 4 (16-byte logit stores)
-  const bool mfma_shape = dt == 1 && T > 64 && H % RT_K == 0 && E % 4 == 0;
+  // bf16 prefill batches with E a multiple of 4 (16-byte logit stores).
+  // The MFMA kernel has one block per 64 tokens and 64 experts, so with at
+  // most 128 experts and a few hundred tokens it runs on a handful of CUs;
+  // the per-expert dot products spread over E * T / 2 waves instead.  Up to
+  // 256 tokens with E <= 128 they won (Qwen3 EP view T = 128 routing stage
+  // 44.7 -> 31 us, T = 256 45 -> 40 us, Mixtral T = 256 32 -> 18 us); with
+  // 256 experts (DeepSeek-V3 T = 256, 70 -> 84 us) and at T = 1024 (47 ->
+  // 87 us) the MFMA kernel stays ahead.
+  const int gemv_max_t = E <= 128 ? 256 : 64;
+  const bool mfma_shape = dt == 1 && T > gemv_max_t && H % RT_K == 0 && E % 4 == 0;
   if (!mfma_shape) {
     const long long units = (long long)E * ((T + RT_GEMV_TOK - 1) / RT_GEMV_TOK);
     const int grid = (int)((units + 3) / 4);
