@@ -763,6 +763,7 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
   const int BM_dn = plan.BM_dn;
   FfnArgs fd = f;
   if (BM_dn != l.BM) fd.map_bm = l.BM;
+  if (plan.dn == SHARE_NONE) fd.down_cols = plan.dn_cols;
   FfnArgs g{};
   const int BMs = plan.BMs;
   const bool share_up = plan.up != SHARE_NONE, share_dn = plan.dn != SHARE_NONE;

@@ -105,6 +105,8 @@ struct FfnArgs {
   long long h_rows;         // rows of h
   int map_bm;               // rows per tile-map entry when it differs from the
                             // launch's row tile (direct kernel only); 0: the same
+  int down_cols;            // output columns per block of the LDS-tiled down
+                            // projection with 128-row tiles: 128, or 0 for 256
 };
 // Row tile of the expert GEMMs: 16/32/64 (direct kernel) or 128/256 (LDS-
 // tiled kernel), from the expected rows per expert and the number of experts
@@ -123,6 +125,11 @@ hipError_t launch_ffn_down(const FfnArgs& a, int BM, hipStream_t st, const FfnAr
 // projection's short one streams faster in the direct kernel (16-row tiles
 // walking the gate/up GEMM's map: FfnArgs::map_bm = BM).
 int ffn_down_row_tile(int dt, int mean_rows, int H, int I_loc, int BM);
+// Output columns per block of the routed down projection when it runs 128-row
+// LDS tiles (FfnArgs::down_cols): 128 where 256-column tiles would leave CUs
+// idle (few experts, one row tile each), else 0 (256 columns).  experts: the
+// experts the rows spread over.
+int ffn_down_cols(int dt, int BM_dn, int mean_rows, int experts, int H);
 // Whether b can ride in a's launch of one GEMM (gate_up: the gate/up GEMM,
 // else the down projection): both bf16 with one row tile and the same kernel
 // configuration (tile shape, or waves per block of the direct kernel).
@@ -145,6 +152,7 @@ struct GemmPlan {
   int up, dn;     // SharedLaunch of the shared gate/up and down GEMMs
   int BMs_up;     // row tile the shared gate/up GEMM runs with
   int BMs_dn;     // row tile the shared down GEMM runs with
+  int dn_cols;    // FfnArgs::down_cols of the routed down projection
 };
 GemmPlan plan_layer_gemms(int dt, int T, int k, int E, int E_loc, int H, int I_loc, int I_shared);
 

@@ -316,6 +316,7 @@ TILE = [
     ("qwen3_ep_all128", 256, 128, 16, 1111),
     ("deepseek_v3", 512, 256, 32, 700),
     ("qwen3_ep_all128", 512, 192, 16, 700),     # gate/up width 192: 64-column tiles
+    ("mixtral_8x7b", 512, 256, 8, 200),         # 50 rows per expert: 128-column down tiles
 ]
 
 

@@ -41,13 +41,20 @@ CASES = [
     # Qwen3 EP view: direct at a few rows, 128-row LDS tiles from 64 rows per
     # expert, 256-row tiles at prefill
     (("qwen3_ep", 4096, 1536, 0, 128, 128, 8, 16), dict(gate_up="16", down="16")),
-    (("qwen3_ep", 4096, 1536, 0, 128, 128, 8, 1024), dict(gate_up="128", down="128")),
+    (("qwen3_ep", 4096, 1536, 0, 128, 128, 8, 1024),
+     dict(gate_up="128", down="128", down_cols="256")),
     (("qwen3_ep", 4096, 1536, 0, 128, 128, 8, 8192), dict(gate_up="256", down="256")),
     # Qwen3 TP share (I/P = 192): direct kernel at T <= 64
     (("qwen3_tp", 4096, 192, 0, 128, 128, 8, 64), dict(gate_up="16", down="16")),
-    # Mixtral: direct at T = 16, 256-row tiles at 4096
+    # Mixtral: direct at T = 16, 256-row tiles at 4096; at T = 64-256 (one
+    # 128-row tile per expert) the down projection takes 128-column tiles so
+    # that its blocks fill the CUs, at T = 512 (a second tile for many
+    # experts) no longer
     (("mixtral", 4096, 14336, 0, 8, 8, 2, 16), dict(gate_up="16", down="16")),
-    (("mixtral", 4096, 14336, 0, 8, 8, 2, 4096), dict(gate_up="256", down="256")),
+    (("mixtral", 4096, 14336, 0, 8, 8, 2, 64), dict(gate_up="128", down="128", down_cols="128")),
+    (("mixtral", 4096, 14336, 0, 8, 8, 2, 256), dict(gate_up="128", down="128", down_cols="128")),
+    (("mixtral", 4096, 14336, 0, 8, 8, 2, 512), dict(gate_up="128", down="128", down_cols="256")),
+    (("mixtral", 4096, 14336, 0, 8, 8, 2, 4096), dict(gate_up="256", down="256", down_cols="256")),
     # DeepSeek-V3: direct at T = 1 (shared expert in both routed launches);
     # at T = 8 and 16 the gate/up GEMM on LDS tiles, the down projection
     # direct walking its map, the shared expert riding in both (switched to
