@@ -109,16 +109,29 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int kg = 8 * (lane >> 4);
 
+  // The rows' sources are loaded here but turned into addresses only after
+  // the first batch of weight loads has been issued (set_xp below), so the
+  // weight stream does not wait for the source-token round trip.
   const bf16_t* xp[MT];
   bool xv[MT];
+  int xsrc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int row = r0 + 16 * mt + (lane & 15);
     xv[mt] = row < r1;
-    // a source of -1 (a padding row) reads row 0 instead of memory before X
-    const int src = xv[mt] ? (a.src_token ? max(a.src_token[row], 0) : row) : 0;
-    xp[mt] = a.X + (size_t)src * a.K + kg;
+    xsrc[mt] = xv[mt] ? (a.src_token ? a.src_token[row] : row) : 0;
+    xp[mt] = a.X;
   }
+  auto set_xp = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      // the weight loads above stay ahead of this point; the wait for the
+      // source lands here
+      asm volatile("" : "+v"(xsrc[mt]) :: "memory");
+      // a source of -1 (a padding row) reads row 0 instead of memory before X
+      xp[mt] = a.X + (size_t)max(xsrc[mt], 0) * a.K + kg;
+    }
+  };
   const bf16_t* We = a.W + (size_t)e * a.w_stride;
   const bf16_t* wg[NT];
   const bf16_t* wu[NT];
@@ -179,6 +192,7 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
             for (int h = 0; h < 2; ++h)
               wv[p][nt][w][h] = ld_stream16(wq[nt][w] + h * half + ko);
       }
+      if (s == s_begin) set_xp();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ko = min(s + u, s_end - 1) * 32;
@@ -240,6 +254,11 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
         wa[u][nt] = ld_stream16_u4(wg[nt] + ko);
         if (SWIGLU) wb[u][nt] = ld_stream16_u4(wu[nt] + ko);
       }
+    }
+    if (s == s_begin) set_xp();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ko = min(s + u, s_end - 1) * 32;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         xa[u][mt] = xv[mt] ? *reinterpret_cast<const uint4*>(xp[mt] + ko) : make_uint4(0, 0, 0, 0);
