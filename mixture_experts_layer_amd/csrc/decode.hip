@@ -386,18 +386,17 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int s = sb; s < se; s += DEC_U) {
           uint4 wv[DEC_U], xv[DEC_U];
+          // only the batch's own steps are loaded; the rest multiply zeros
 #pragma unroll
           for (int q = 0; q < DEC_U; ++q) {
-            const int ko = min(s + q, se - 1) * 32;
-            wv[q] = ld16(wp + ko);
-            xv[q] = mv ? ld16(xp + ko) : make_uint4(0, 0, 0, 0);
+            const bool in = s + q < se;
+            wv[q] = in ? ld16(wp + (s + q) * 32) : make_uint4(0, 0, 0, 0);
+            xv[q] = mv && in ? ld16(xp + (s + q) * 32) : make_uint4(0, 0, 0, 0);
           }
 #pragma unroll
-          for (int q = 0; q < DEC_U; ++q) {
-            if (s + q >= se) xv[q] = make_uint4(0, 0, 0, 0);
+          for (int q = 0; q < DEC_U; ++q)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[q]), as_bf16x8(xv[q]), acc,
                                                           0, 0, 0);
-          }
         }
         // accumulator lane l: operand rows 4*(l/16) + i (gate 0..7, up 8..15)
         // of token m0 + l % 16; waves' partial sums meet in LDS in wave order
@@ -470,8 +469,12 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
             const bf16_t* hq = hp + (size_t)(mv ? m0 + r16 : 0) * Ia + kg;
             for (int s = kb; s < ke; s += DEC_U) {
               uint4 wv[DEC_U], hv[DEC_U];
+              // only the batch's own steps are loaded (a share of a few
+              // steps, as at one token per slot, no longer issues DEC_U
+              // loads of W2 and of h); the rest multiply zeros
 #pragma unroll
-              for (int q = 0; q < DEC_U; ++q) wv[q] = ld16(wp + min(s + q, ke - 1) * 32);
+              for (int q = 0; q < DEC_U; ++q)
+                wv[q] = s + q < ke ? ld16(wp + (s + q) * 32) : make_uint4(0, 0, 0, 0);
               if (waiting) {
                 if (lane == 0 && !wait_flag(my_flag, 2u * ep + 2u, false)) set_error(sync, 2);
                 waiting = false;
@@ -479,16 +482,13 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WAVES / 4) void moe_decode_kernel(
                 asm volatile("" ::: "memory");
               }
 #pragma unroll
-              for (int q = 0; q < DEC_U; ++q) {
-                const int ko = min(s + q, ke - 1) * 32;
-                hv[q] = mv ? load_coherent16(hq + ko) : make_uint4(0, 0, 0, 0);
-              }
+              for (int q = 0; q < DEC_U; ++q)
+                hv[q] = mv && s + q < ke ? load_coherent16(hq + (s + q) * 32)
+                                         : make_uint4(0, 0, 0, 0);
 #pragma unroll
-              for (int q = 0; q < DEC_U; ++q) {
-                if (s + q >= ke) hv[q] = make_uint4(0, 0, 0, 0);
+              for (int q = 0; q < DEC_U; ++q)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[q]), as_bf16x8(hv[q]),
                                                               acc, 0, 0, 0);
-              }
             }
           }
           // lane l: H rows hr0 + 4*(l/16) + i of token row m0 + l % 16
