@@ -608,11 +608,16 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t st) {
   a.T = d.T; a.H = d.H; a.E = d.E; a.k = d.k; a.mode = d.mode;
   a.I = d.I_loc; a.Is = d.I_shared; a.e_begin = d.e_begin; a.e_end = d.e_end;
   // down units: KS waves split a slot's K so that the block's waves stay busy
-  // when at most DEC_WAVES / KS slots can be active
+  // when at most DEC_WAVES / KS slots can be active, while each wave keeps at
+  // least one full load batch of the routed contraction (a split below that
+  // costs its cross-wave reduction and barriers for nothing: TP share T = 1,
+  // I = 192, KS 2 -> 1 took the layer from 24.0 to 23.5 us)
   const int E_loc = d.e_end - d.e_begin;
   const int slots = (d.T * d.k < E_loc ? d.T * d.k : E_loc) + (d.I_shared > 0 ? 1 : 0);
   a.ks2 = 1;
-  while (a.ks2 < DEC_WAVES && 2 * a.ks2 * slots <= DEC_WAVES) a.ks2 *= 2;
+  while (a.ks2 < DEC_WAVES && 2 * a.ks2 * slots <= DEC_WAVES &&
+         d.I_loc / 32 / (2 * a.ks2) >= DEC_U)
+    a.ks2 *= 2;
   const int epr = (a.E + 15) / 16;
   if (epr <= 1) return launch_decode_epr<1>(a, st);
   if (epr <= 2) return launch_decode_epr<2>(a, st);
