@@ -620,18 +620,21 @@ __device__ __forceinline__ void wait_stage_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
 }
 
-// The down projection's bf16 output leaves through LDS: the block's finished
-// tile is staged row by row (rows padded by 16 bytes so the column-wise
-// writes spread over the banks) and stored 16 bytes per lane along rows,
-// instead of 8-byte pieces scattered over 32 rows per instruction.  That ran
-// the down GEMM 5-8% faster; the gate/up tile (half as wide) lost more to
-// the two extra barriers than it gained, so it stores directly.
+// A bf16 output tile leaves through LDS: the block's finished tile is staged
+// row by row (rows padded by 16 bytes so the column-wise writes spread over
+// the banks) and stored 16 bytes per lane along rows, instead of 8-byte
+// pieces scattered over 32 rows per instruction, with the non-temporal hint
+// (whole 128-byte lines).  That ran the down GEMM 5-8% faster.  The gate/up
+// tile (half as wide) had lost as much to the two extra barriers as it
+// gained; with the hint on its whole-line stores it measured even at T = 8192
+// and 2% faster per layer at the Qwen3 EP view's T = 1024 (the same hint on
+// its 8-byte direct stores had cost 6-15%).
 template <class C, bool SWIGLU, bool OUT_BF16>
 struct TileOut {
   static constexpr int OC = SWIGLU ? C::TN / 2 : C::TN;   // output columns per block
   static constexpr int PITCH = OC * 2 + 16;                // staged row bytes
   static constexpr int PITCH_W = 2 * OC * 2 + 16;          // wide half tile: TM/2 rows, 2 OC
-  static constexpr bool STAGED = OUT_BF16 && !SWIGLU;
+  static constexpr bool STAGED = OUT_BF16;
   static constexpr int OUT_BYTES =
       C::WIDE && C::TM / 2 * PITCH_W > C::TM * PITCH ? C::TM / 2 * PITCH_W : C::TM * PITCH;
   static constexpr int LDS = (STAGED && OUT_BYTES > C::LDS) ? OUT_BYTES : C::LDS;
@@ -989,12 +992,11 @@ __global__ __launch_bounds__(C::NTHR, C::MINB) void ffn_tile_kernel(TileArgs a0,
     lds_barrier();
     const int nrows = r1 - r0;
     bf16_t* Y = reinterpret_cast<bf16_t*>(a.Y);
-    // Non-temporal stores: the output rows are read next by the combine,
-    // past the L2 in any case, and allocating them in L2 evicted the
-    // operand tiles that other blocks of the launch still read (Qwen3 EP
-    // view: down projection 0.337 -> 0.302 ms at T = 1024, 0.953 -> 0.93 ms
-    // at T = 8192).  The gate/up GEMM's h, which the down projection reads
-    // back, keeps the default policy (the hint there cost 6-15%).
+    // Non-temporal stores: the output rows are read next by another launch
+    // (the down projection or the combine), and allocating them in L2 had
+    // evicted operand tiles that other blocks of this launch still read
+    // (Qwen3 EP view: down projection 0.337 -> 0.302 ms at T = 1024, 0.953
+    // -> 0.93 ms at T = 8192).
     auto store_rows = [&](auto cpr_c, int rows, int pitch_b) {
       constexpr int CPR_OUT = decltype(cpr_c)::value;   // 16-byte chunks per row
       for (int c = threadIdx.x; c < rows * CPR_OUT; c += C::NTHR) {
