@@ -1308,8 +1308,10 @@ static int direct_nw(int BM, int K) {
   // faster).  Measured further: the gate/up GEMM over a long K (>= 192
   // steps, e.g. H = 7168) ran 6% faster with 4 waves; the down projection
   // 10-18% faster with 2 waves (longer per-wave streams, a cheaper
-  // reduction).
-  const int max_nw16 = SWIGLU ? (steps >= 192 ? 4 : 8) : 2;
+  // reduction) -- up to a contraction of 256 steps: over I = 14336 (Mixtral
+  // shape, 448 steps) each of 2 waves chained 28 load batches, and 4 waves
+  // ran the down projection 5-18% faster at T = 1-16 (T = 1: 53.6 -> 44.1 us).
+  const int max_nw16 = SWIGLU ? (steps >= 192 ? 4 : 8) : (steps >= 256 ? 4 : 2);
   // 32- and 64-row tiles (more MFMA work per load): 4 waves for gate/up, 2
   // for the down projection ran the layer 3-15% faster than 8 at 16-32 rows
   // per expert
