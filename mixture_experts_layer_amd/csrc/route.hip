@@ -153,9 +153,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 
 // Each block covers 64 tokens and 32*EW experts; E is split over the grid's
 // second dimension so that a large E gives more blocks (and each block a
-// smaller share of W_r to stream through LDS).  EW = 2 when 64 divides E,
-// else EW = 1 with a partial last block (few experts: the tokens are still
-// read once, where a per-expert GEMV would read them E times).
+// smaller share of W_r to stream through LDS).  EW = 2 when 64 divides E and
+// the grid still has 128 blocks, else EW = 1 (with a partial last block when
+// 32 does not divide E: few experts, the tokens still read once where a
+// per-expert GEMV would read them E times).
 template <int EW>
 static hipError_t launch_router_mfma(const bf16_t* x, const bf16_t* wr, int T, int H, int E,
                                      const float* bias, float* logits, hipStream_t st) {
@@ -427,7 +428,12 @@ hipError_t launch_router_logits(const void* x, const void* wr, int dt, int T, in
   }
   const bf16_t* xb = (const bf16_t*)x;
   const bf16_t* wb = (const bf16_t*)wr;
-  if (E % 64 == 0) return launch_router_mfma<2>(xb, wb, T, H, E, bias, logits, st);
+  // 64 experts per block when that still gives half the CUs a block, else
+  // 32 (twice the blocks, each with a smaller share of W_r to stream):
+  // routing stage 49 -> 42 us at the Qwen3 EP view's T = 512 and 50 -> 43 us
+  // at T = 1024, DeepSeek-V3 T = 1024 72 -> 68 us
+  if (E % 64 == 0 && (long long)((T + RT_TOK - 1) / RT_TOK) * (E / 64) >= 128)
+    return launch_router_mfma<2>(xb, wb, T, H, E, bias, logits, st);
   return launch_router_mfma<1>(xb, wb, T, H, E, bias, logits, st);
 }
 
