@@ -334,6 +334,29 @@ def test_layer_tile_path(name, H, I, E, T):
     check_layer(gl2, gl2.run(T), T)
 
 
+def test_narrow_down_tiles_match_the_grouped_ffn_bit_for_bit():
+    """A few experts of one 128-row tile each: moe_layer runs the down
+    projection on 128-column tiles (plan_layer_gemms), moe_grouped_ffn on the
+    256-column ones.  Each output's sum over K runs in the same order either
+    way, so on the layer's own routing the two give the same bits."""
+    cfg = W.CONFIGS["mixtral_8x7b"]
+    T = 200
+    L = W.make_layer(cfg, device=DEV, seed=11, T_max=T, H=512, I=256, E=8)
+    gl = GpuLayer(L)
+    out = gl.run(T, path="staged")
+    rows = T * gl.k
+    dtc = gl.dt
+    y_perm = torch.empty((rows, gl.H), dtype=L.x.dtype, device=DEV)
+    nb = M.moe_grouped_ffn_workspace_size(rows, gl.E, gl.H, gl.I_loc, dtc)
+    ws = ws_tensor(nb)
+    M.moe_grouped_ffn(None, L.x[:T], out["src_token"], out["offsets"], gl.E, rows, gl.H, gl.I_loc,
+                      gl.w13, gl.w2, dtc, y_perm, dtc, ws, nb)
+    y = torch.empty((T, gl.H), dtype=L.x.dtype, device=DEV)
+    M.moe_combine(y_perm, dtc, out["dst_row"], out["w"], T, gl.k, gl.H, None, y, dtc)
+    torch.cuda.synchronize()
+    assert torch.equal(y, out["y"])
+
+
 # The shared expert's GEMMs ride in the routed GEMMs' launches or run in
 # launches of their own, each GEMM by its own choice (plan_layer_gemms; the
 # host test test_host_tile_choice.py asserts these plans).  Always through
