@@ -780,6 +780,7 @@ static int layer_staged_impl(const moe_layer_desc* d, int T, const void* x, void
     g_dn = g;
     g_dn.max_tiles = cdiv(T, BMs_dn);
   }
+  f.gate_up_pack = plan.up_pack;
   MOE_TRY(launch_ffn_gate_up(f, l.BM, s, share_up ? &g_up : nullptr));
   MOE_TRY(mark(2));
   // the shared expert's h must be complete before a launch that reads it

@@ -87,29 +87,41 @@ __device__ __forceinline__ int xp_slot(int t, int row, int g) {
   return t * 64 + ((row + 2 * t) & 15) * 4 + (g ^ ((row >> 2) & 3));
 }
 
+// Weight operands per 16-column output tile: gate and up apart (SwiGLU), or
+// one (the down projection, or PACK: 8 gate and the matching 8 up rows in one
+// 16-row operand, 8 output columns per tile)
+template <bool SWIGLU, bool PACK>
+constexpr int direct_ns() {
+  return SWIGLU && !PACK ? 2 : 1;
+}
 // K steps per load batch: about 24 16-byte loads in flight per wave
-template <int MT, int NT, bool SWIGLU>
+template <int MT, int NT, bool SWIGLU, bool PACK = false>
 constexpr int direct_u() {
-  constexpr int lps = NT * (SWIGLU ? 2 : 1) + MT;      // loads per K step
+  constexpr int lps = NT * direct_ns<SWIGLU, PACK>() + MT;   // loads per K step
   return 24 / lps < 2 ? 2 : (24 / lps > 8 ? 8 : 24 / lps);
 }
 // 16-byte LDS units of a block's regrouping areas (0: fragment-layout loads)
-template <int MT, int NT, int NW, bool SWIGLU>
+template <int MT, int NT, int NW, bool SWIGLU, bool PACK = false>
 constexpr int direct_xp_units() {
-  return direct_u<MT, NT, SWIGLU>() % 2 == 0 ? NW * NT * (SWIGLU ? 2 : 1) * XP_AREA : 0;
+  return direct_u<MT, NT, SWIGLU, PACK>() % 2 == 0
+             ? NW * NT * direct_ns<SWIGLU, PACK>() * XP_AREA
+             : 0;
 }
 
 // Rows [r0, r1) (at most 16 * MT) of expert e against output columns
-// [n0, n0 + 16 * NT).
-template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
+// [n0, n0 + BN): BN = 16 * NT, or 8 with PACK (SwiGLU, one column tile, the
+// gate rows n0 + [0, 8) and up rows up_off + n0 + [0, 8) as one operand, so
+// the accumulator's lanes 32-63 hold the up sums of lanes 0-31's gate sums).
+template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16, bool PACK = false>
 __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, int r1, int n0,
                                             float* red, uint4* xp_all) {
-  constexpr int NS = SWIGLU ? 2 : 1;
+  static_assert(!PACK || (SWIGLU && NT == 1 && NW > 1), "PACK: SwiGLU, one tile, split K");
+  constexpr int NS = direct_ns<SWIGLU, PACK>();
   constexpr int BM = 16 * MT;
-  constexpr int BN = 16 * NT;
+  constexpr int BN = PACK ? 8 : 16 * NT;
   constexpr int NACC = MT * NT * NS;
   constexpr int PITCH = 65;
-  constexpr int U = direct_u<MT, NT, SWIGLU>();
+  constexpr int U = direct_u<MT, NT, SWIGLU, PACK>();
   constexpr bool PAIRED = U % 2 == 0;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int kg = 8 * (lane >> 4);
@@ -142,7 +154,8 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
   const bf16_t* wu[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int n = n0 + 16 * nt + (lane & 15);
+    const int r = lane & 15;
+    const int n = PACK ? n0 + (r & 7) + (r < 8 ? 0 : a.up_off) : n0 + 16 * nt + r;
     wg[nt] = We + (size_t)n * a.K + kg;
     wu[nt] = We + (size_t)(a.up_off + n) * a.K + kg;
   }
@@ -173,9 +186,10 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
     for (int nt = 0; nt < NT; ++nt) {
       const int n = n0 + 16 * nt + (lane >> 3);
       wq[nt][0] = We + (size_t)n * a.K + 8 * (lane & 3);
-      if (SWIGLU) wq[nt][NS - 1] = We + (size_t)(a.up_off + n) * a.K + 8 * (lane & 3);
+      if (NS == 2) wq[nt][NS - 1] = We + (size_t)(a.up_off + n) * a.K + 8 * (lane & 3);
     }
-    const size_t half = (size_t)8 * a.K;
+    // the operand's upper 8 rows: the next 8 rows, or with PACK the up rows
+    const size_t half = (size_t)(PACK ? a.up_off : 8) * a.K;
     bf16x8_t* area = reinterpret_cast<bf16x8_t*>(xp_all) + wid * (NT * NS * XP_AREA);
     int wi[2], ri[2];
 #pragma unroll
@@ -241,7 +255,7 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
             for (int nt = 0; nt < NT; ++nt) {
               acc[mt][nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   f[nt][0][t], as_bf16x8(xa[2 * p + t][mt]), acc[mt][nt][0], 0, 0, 0);
-              if (SWIGLU)
+              if (NS == 2)
                 acc[mt][nt][NS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     f[nt][NS - 1][t], as_bf16x8(xa[2 * p + t][mt]), acc[mt][nt][NS - 1],
                     0, 0, 0);
@@ -257,7 +271,7 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         wa[u][nt] = ld_stream16_u4(wg[nt] + ko);
-        if (SWIGLU) wb[u][nt] = ld_stream16_u4(wu[nt] + ko);
+        if (NS == 2) wb[u][nt] = ld_stream16_u4(wu[nt] + ko);
       }
     }
     if (s == s_begin) set_xp();
@@ -280,7 +294,7 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
         for (int nt = 0; nt < NT; ++nt) {
           acc[mt][nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               as_bf16x8(wa[u][nt]), as_bf16x8(xa[u][mt]), acc[mt][nt][0], 0, 0, 0);
-          if (SWIGLU)
+          if (NS == 2)
             acc[mt][nt][NS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 as_bf16x8(wb[u][nt]), as_bf16x8(xa[u][mt]), acc[mt][nt][NS - 1], 0, 0, 0);
         }
@@ -325,7 +339,9 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
               acc[mt][nt][w][i];
   __syncthreads();
 
-  // reduce over waves in wave order and write BM x BN outputs, n fastest
+  // reduce over waves in wave order and write BM x BN outputs, n fastest;
+  // the up sum sits in the next accumulator, or with PACK 32 lanes on
+  constexpr int UP = PACK ? 32 : 4 * PITCH;
   for (int o = threadIdx.x; o < BM * BN; o += NW * 64) {
     const int m = o / BN, n = o - m * BN;
     const int row = r0 + m;
@@ -337,7 +353,7 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       g += red[w * NACC * 4 * PITCH + base];
-      if (SWIGLU) u += red[w * NACC * 4 * PITCH + base + 4 * PITCH];
+      if (SWIGLU) u += red[w * NACC * 4 * PITCH + base + UP];
     }
     const float out = SWIGLU ? silu_fast(g) * u : g;
     const size_t yi = (size_t)row * a.N_out + n0 + n;
@@ -353,16 +369,21 @@ __device__ __forceinline__ void direct_rows(const DirectArgs& a, int e, int r0, 
 // projection reading the gate/up GEMM's map), and the block walks them
 // 16 * MT rows at a time (a separate instance: the loop cost the other
 // launches a few percent).
-template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16, bool WALK>
-__global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, DirectArgs a1,
-                                                             int grid0) {
+//
+// The 8-wave gate/up instance is held to four waves per SIMD (128 VGPRs), so
+// that two of its blocks share a CU: left to itself the compiler took 130 and
+// room for one block, and the Qwen3 TP share's gate/up GEMM at T = 8 ran
+// 36.2 us instead of 33.8.
+template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16, bool WALK, bool PACK = false>
+__global__ __launch_bounds__(NW * 64, (NW == 8 && SWIGLU) ? 4 : 1) void ffn_direct_kernel(
+    DirectArgs a0, DirectArgs a1, int grid0) {
   const bool second = (int)blockIdx.x >= grid0;
   const DirectArgs a = second ? a1 : a0;
   const int bid = second ? (int)blockIdx.x - grid0 : (int)blockIdx.x;
   constexpr int BM = 16 * MT;
-  constexpr int BN = 16 * NT;
-  constexpr int NACC = MT * NT * (SWIGLU ? 2 : 1);
-  constexpr int XPU = direct_xp_units<MT, NT, NW, SWIGLU>();
+  constexpr int BN = PACK ? 8 : 16 * NT;
+  constexpr int NACC = MT * NT * direct_ns<SWIGLU, PACK>();
+  constexpr int XPU = direct_xp_units<MT, NT, NW, SWIGLU, PACK>();
   __shared__ float red[NW > 1 ? NW * NACC * 4 * 65 : 1];
   __shared__ uint4 xp_lds[XPU > 0 ? XPU : 1];
 
@@ -385,7 +406,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_direct_kernel(DirectArgs a0, Dire
       if (NW > 1) __syncthreads();    // red is written again by the next rows
     }
   } else {
-    direct_rows<MT, NT, NW, SWIGLU, OUT_BF16>(a, e, r0, r1, ntile * BN, red, xp_lds);
+    direct_rows<MT, NT, NW, SWIGLU, OUT_BF16, PACK>(a, e, r0, r1, ntile * BN, red, xp_lds);
   }
 }
 
@@ -1257,11 +1278,13 @@ static int pick_nw(int steps, int max_nw, int batch) {
   return nw;
 }
 
-template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16>
+template <int MT, int NT, int NW, bool SWIGLU, bool OUT_BF16, bool PACK = false>
 static hipError_t launch_direct_t(const DirectArgs& a, int max_tiles, const DirectArgs* b,
                                   int b_tiles, hipStream_t st) {
-  const int grid0 = max_tiles * (a.N_out / (16 * NT));
-  const int grid1 = b ? b_tiles * (b->N_out / (16 * NT)) : 0;
+  constexpr int BN = PACK ? 8 : 16 * NT;
+  if (a.N_out % BN != 0 || (b && b->N_out % BN != 0)) return hipErrorInvalidValue;
+  const int grid0 = max_tiles * (a.N_out / BN);
+  const int grid1 = b ? b_tiles * (b->N_out / BN) : 0;
   if constexpr (!SWIGLU && MT == 1 && NT == 1) {
     if (a.map_bm > 16 || (b && b->map_bm > 16)) {
       ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16, true><<<grid0 + grid1, NW * 64, 0, st>>>(
@@ -1270,19 +1293,22 @@ static hipError_t launch_direct_t(const DirectArgs& a, int max_tiles, const Dire
     }
   }
   if (a.map_bm > 16 * MT || (b && b->map_bm > 16 * MT)) return hipErrorInvalidValue;
-  ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16, false><<<grid0 + grid1, NW * 64, 0, st>>>(
-      a, b ? *b : a, grid0);
+  ffn_direct_kernel<MT, NT, NW, SWIGLU, OUT_BF16, false, PACK>
+      <<<grid0 + grid1, NW * 64, 0, st>>>(a, b ? *b : a, grid0);
   return hipGetLastError();
 }
 
-template <int MT, int NT, bool SWIGLU, bool OUT_BF16>
+template <int MT, int NT, bool SWIGLU, bool OUT_BF16, bool PACK = false>
 static hipError_t launch_direct_nw(const DirectArgs& a, int nw, int max_tiles, const DirectArgs* b,
                                    int b_tiles, hipStream_t st) {
   switch (nw) {
-    case 1: return launch_direct_t<MT, NT, 1, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
-    case 2: return launch_direct_t<MT, NT, 2, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
-    case 4: return launch_direct_t<MT, NT, 4, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
-    default: return launch_direct_t<MT, NT, 8, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    case 1:
+      if constexpr (PACK) return hipErrorInvalidValue;   // PACK sums over waves
+      else return launch_direct_t<MT, NT, 1, SWIGLU, OUT_BF16>(a, max_tiles, b, b_tiles, st);
+    case 2: return launch_direct_t<MT, NT, 2, SWIGLU, OUT_BF16, PACK>(a, max_tiles, b, b_tiles, st);
+    case 4: return launch_direct_t<MT, NT, 4, SWIGLU, OUT_BF16, PACK>(a, max_tiles, b, b_tiles, st);
+    default:
+      return launch_direct_t<MT, NT, 8, SWIGLU, OUT_BF16, PACK>(a, max_tiles, b, b_tiles, st);
   }
 }
 
@@ -1330,9 +1356,15 @@ static bool direct_cols_ok(const DirectArgs& a, bool swiglu, int BM) {
   return !swiglu && BM == 16 && a.map_bm <= 16 && a.K <= DCOLS_MAX_K && a.N_out % 16 == 0;
 }
 
+// Whether a gate/up launch the plan gave 8-column tiles (PACK) can take
+// them: the partial sums meet over waves, and whole 8-column tiles.
+static bool direct_pack_ok(const DirectArgs& a, int nw, const DirectArgs* b) {
+  return nw >= 2 && a.N_out % 8 == 0 && (!b || b->N_out % 8 == 0);
+}
+
 template <bool SWIGLU, bool OUT_BF16>
 static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, const DirectArgs* b,
-                                int b_tiles, hipStream_t st) {
+                                int b_tiles, hipStream_t st, bool pack = false) {
   if constexpr (!SWIGLU) {
     if (direct_cols_ok(a, false, BM) && (!b || direct_cols_ok(*b, false, BM))) {
       const int cb = (a.N_out / 16 + DCOLS_WAVES - 1) / DCOLS_WAVES;
@@ -1350,6 +1382,10 @@ static hipError_t launch_direct(const DirectArgs& a, int BM, int max_tiles, cons
     }
   }
   const int nw = direct_nw<SWIGLU>(BM, a.K);
+  if constexpr (SWIGLU && DIRECT_NT16 == 1) {
+    if (pack && BM == 16 && direct_pack_ok(a, nw, b))
+      return launch_direct_nw<1, 1, true, OUT_BF16, true>(a, nw, max_tiles, b, b_tiles, st);
+  }
   if (BM == 16)
     return launch_direct_nw<1, DIRECT_NT16, SWIGLU, OUT_BF16>(a, nw, max_tiles, b, b_tiles, st);
   if (BM == 32)
@@ -1419,6 +1455,23 @@ int ffn_down_cols(int dt, int BM_dn, int mean_rows, int experts, int H) {
   return tiles * (H / TileNarrow::TN) <= 256 ? TileNarrow::TN : 0;
 }
 
+// 8-column gate/up tiles.  One 16-row operand carries 8 gate and the matching
+// 8 up rows, so a block streams half the weight bytes of a 16-column one and
+// its blocks spread more evenly over the CUs.  Measured on the Qwen3 TP share
+// (graph-replayed, same box): T = 4 47.3 -> 44.4 us, T = 8 62.7-62.9 -> 61.4-
+// 61.8 us (about 49 touched experts x 12 column tiles = 588 blocks of 16
+// columns for 256 CUs: some CUs streamed three, most two); Qwen3 EP view T = 1
+// (8 experts x 96 tiles, three per CU, narrowed as 7.8 are expected) 1%
+// faster.  At T = 16 and 64, EP T = 16 and Mixtral T = 1 (4-30 blocks per CU)
+// it was within about 1% either way (EP T = 16 1.2% slower): every weight load
+// then comes with its own activation load.  The expected touched experts
+// assume uniform routing.
+int ffn_gate_up_pack(int dt, int BM, int T, int k, int E, int E_loc, int I_loc) {
+  if (dt != 1 || BM != 16 || T <= 0 || k <= 0 || E <= 0 || I_loc % 16 != 0) return 0;
+  const double touched = E_loc * (1.0 - __builtin_pow(1.0 - 1.0 / E, (double)T * k));
+  return touched * (I_loc / 16) < 3.0 * 256 ? 1 : 0;
+}
+
 long long ffn_gate_up_blocks(const FfnArgs& a, int BM) {
   if (a.dt == 0) return (long long)a.max_tiles * (a.I_loc / 16);
   if (is_tile_bm(BM)) {
@@ -1436,7 +1489,8 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st, const Ff
                                      also->max_tiles, st);
     }
     const DirectArgs g2 = gate_up_direct(*also, BM);
-    return launch_direct<true, true>(gate_up_direct(a, BM), BM, a.max_tiles, &g2, also->max_tiles, st);
+    return launch_direct<true, true>(gate_up_direct(a, BM), BM, a.max_tiles, &g2, also->max_tiles, st,
+                                     a.gate_up_pack != 0);
   }
   if (a.max_tiles <= 0) return hipSuccess;
   if (a.dt == 0) {
@@ -1450,7 +1504,8 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int BM, hipStream_t st, const Ff
     if (a.map_bm > 0 && a.map_bm != BM) return hipErrorInvalidValue;
     return launch_tile<true, true>(gate_up_tile(a), BM, a.mean_rows, a.max_tiles, nullptr, 0, st);
   }
-  return launch_direct<true, true>(gate_up_direct(a, BM), BM, a.max_tiles, nullptr, 0, st);
+  return launch_direct<true, true>(gate_up_direct(a, BM), BM, a.max_tiles, nullptr, 0, st,
+                                   a.gate_up_pack != 0);
 }
 
 template <bool OUT_BF16>
@@ -1500,6 +1555,7 @@ GemmPlan plan_layer_gemms(int dt, int T, int k, int E, int E_loc, int H, int I_l
   p.BM = ffn_row_tile(dt, mean, H, I_loc, T * k < E_loc ? T * k : E_loc);
   p.BM_dn = ffn_down_row_tile(dt, mean, H, I_loc, p.BM);
   p.dn_cols = ffn_down_cols(dt, p.BM_dn, mean, T * k < E_loc ? T * k : E_loc, H);
+  p.up_pack = ffn_gate_up_pack(dt, p.BM, T, k, E, E_loc, I_loc);
   if (I_shared <= 0 || T <= 0) return p;
   // the routed problems as the launches see them (any tile count > 0)
   FfnArgs f{};

@@ -107,6 +107,8 @@ struct FfnArgs {
                             // launch's row tile (direct kernel only); 0: the same
   int down_cols;            // output columns per block of the LDS-tiled down
                             // projection with 128-row tiles: 128, or 0 for 256
+  int gate_up_pack;         // 1: a 16-row direct gate/up launch takes 8-column
+                            // tiles (8 gate + 8 up rows in one MFMA operand)
 };
 // Row tile of the expert GEMMs: 16/32/64 (direct kernel) or 128/256 (LDS-
 // tiled kernel), from the expected rows per expert and the number of experts
@@ -130,6 +132,11 @@ int ffn_down_row_tile(int dt, int mean_rows, int H, int I_loc, int BM);
 // idle (few experts, one row tile each), else 0 (256 columns).  experts: the
 // experts the rows spread over.
 int ffn_down_cols(int dt, int BM_dn, int mean_rows, int experts, int H);
+// FfnArgs::gate_up_pack of the routed gate/up GEMM: 1 where its 16-row direct
+// tiles of 16 columns would give the CUs fewer than three blocks each on
+// average, so that whole blocks leave some CUs a third more bytes than
+// others; 8-column tiles halve that step.
+int ffn_gate_up_pack(int dt, int BM, int T, int k, int E, int E_loc, int I_loc);
 // Whether b can ride in a's launch of one GEMM (gate_up: the gate/up GEMM,
 // else the down projection): both bf16 with one row tile and the same kernel
 // configuration (tile shape, or waves per block of the direct kernel).
@@ -153,6 +160,7 @@ struct GemmPlan {
   int BMs_up;     // row tile the shared gate/up GEMM runs with
   int BMs_dn;     // row tile the shared down GEMM runs with
   int dn_cols;    // FfnArgs::down_cols of the routed down projection
+  int up_pack;    // FfnArgs::gate_up_pack of the routed gate/up GEMM
 };
 GemmPlan plan_layer_gemms(int dt, int T, int k, int E, int E_loc, int H, int I_loc, int I_shared);
 

@@ -1,6 +1,6 @@
 // Host-side check of the expert-GEMM kernel choices: prints, for one layer
-// shape and batch, the row tile of each GEMM (and the down projection's
-// output columns per block) and how the shared expert's
+// shape and batch, the row tile of each GEMM (and the output columns per
+// block of the direct gate/up and the tiled down projection) and how the shared expert's
 // GEMMs are launched, as the library's own plan_layer_gemms() decides them
 // (the function the staged layer calls).  Links ffn.hip; launches nothing.
 #include <cstdio>
@@ -19,7 +19,8 @@ int main(int argc, char** argv) {
   const int E = std::atoi(argv[4]), E_loc = std::atoi(argv[5]), k = std::atoi(argv[6]);
   const int T = std::atoi(argv[7]);
   const GemmPlan p = plan_layer_gemms(1, T, k, E, E_loc, H, I, Is);
-  std::printf("gate_up %d down %d down_cols %d", p.BM, p.BM_dn, p.dn_cols ? p.dn_cols : 256);
+  std::printf("gate_up %d down %d down_cols %d gate_up_cols %d", p.BM, p.BM_dn,
+              p.dn_cols ? p.dn_cols : 256, p.up_pack ? 8 : 16);
   if (Is > 0) {
     static const char* how[] = {"own", "shared", "shared_switched"};
     std::printf(" shared_expert %d shared_gate_up %s shared_down %s shared_gate_up_tile %d "

@@ -334,14 +334,19 @@ def test_layer_tile_path(name, H, I, E, T):
     check_layer(gl2, gl2.run(T), T)
 
 
-def test_narrow_down_tiles_match_the_grouped_ffn_bit_for_bit():
-    """A few experts of one 128-row tile each: moe_layer runs the down
-    projection on 128-column tiles (plan_layer_gemms), moe_grouped_ffn on the
-    256-column ones.  Each output's sum over K runs in the same order either
-    way, so on the layer's own routing the two give the same bits."""
-    cfg = W.CONFIGS["mixtral_8x7b"]
-    T = 200
-    L = W.make_layer(cfg, device=DEV, seed=11, T_max=T, H=512, I=256, E=8)
+@pytest.mark.parametrize("name,T,H,I,E", [("mixtral_8x7b", 200, 512, 256, 8),
+                                           ("qwen3_tp8_rank0", 8, 1024, 1536, 128),
+                                           ("qwen3_tp8_rank0", 3, 1024, 1536, 128)])
+def test_narrower_tiles_match_the_grouped_ffn_bit_for_bit(name, T, H, I, E):
+    """Where plan_layer_gemms narrows a GEMM's column tiles, moe_layer and
+    moe_grouped_ffn (which keeps the wide ones) give the same bits on the
+    layer's own routing, since each output's sum over K runs in the same
+    order either way.  Mixtral shape, a few experts of one 128-row tile each:
+    the down projection on 128-column LDS tiles instead of 256.  TP share
+    (I/P = 192) at a few tokens: the direct gate/up GEMM on 8-column tiles,
+    8 gate and 8 up rows in one MFMA operand, instead of 16 columns."""
+    cfg = W.CONFIGS[name]
+    L = W.make_layer(cfg, device=DEV, seed=11, T_max=T, H=H, I=I, E=E)
     gl = GpuLayer(L)
     out = gl.run(T, path="staged")
     rows = T * gl.k
